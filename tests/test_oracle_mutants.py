@@ -1,0 +1,50 @@
+"""Each plausible mistake planted in a copy of the oracle fails at least one pin (CPU only).
+
+The mistakes are planted in the oracle's C source, on the CPU, in a temporary copy; the
+oracle under oracle/ is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "argreduce_oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("ties_to_last_index", "? (a > best) :", "? (a >= best) :"),
+    ("argmin_compares_the_wrong_way", ": (a < best);", ": (a > best);"),
+    ("nan_unsafe_compare", "? (a > best) :", "? !(a <= best) :"),
+    ("signed_zero_ordered", "? (a > best) :", "? (a > best || (a == best && signbit(best) && !signbit(a))) :"),
+    ("identity_seed_instead_of_element0",
+     "double best = element(x, dtype, row0);",
+     "double best = (op == ORACLE_ARGMAX) ? -INFINITY : INFINITY;"),
+    ("row_stride_off_by_one", "const int64_t row0 = r * cols;", "const int64_t row0 = r * (cols - 1);"),
+    ("f16_subnormals_flushed", "mag = ldexp((double)frac, -24);", "mag = 0.0;"),
+    ("f16_exponent_bias", "expo - 25);", "expo - 24);"),
+    ("bf16_wrong_shift", "(uint32_t)b << 16;", "(uint32_t)b << 15;"),
+    ("f64_read_as_f32_stride", "(const char *)x + k * 8, 8);", "(const char *)x + k * 4, 8);"),
+    ("last_column_skipped", "for (int64_t j = 1; j < cols; ++j)", "for (int64_t j = 1; j < cols - 1; ++j)"),
+    ("empty_rows_accepted", "cols < 1 ||", "cols < 0 ||"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.build(str(mutated), str(tmp_path / "libmutant.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin_name, pin in P.all_pins(o, fast=True):
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin_name)
+        except Exception as exc:  # a crash or refusal is a catch too
+            caught.append(f"{pin_name}:{type(exc).__name__}")
+    assert caught, f"mutant {name} passed every pin"

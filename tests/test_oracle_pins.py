@@ -1,0 +1,52 @@
+"""The CPU oracle against what the pages and the mathematics fix (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def test_widen_f16_every_bit_pattern(oracle_lib):
+    P.pin_widen_f16(oracle_lib)
+
+
+def test_widen_bf16_every_bit_pattern(oracle_lib):
+    P.pin_widen_bf16(oracle_lib)
+
+
+def test_widen_f32_f64_sampled_bit_patterns(oracle_lib):
+    P.pin_widen_f32_f64(oracle_lib)
+
+
+@pytest.mark.parametrize("dtype", P.DTYPES)
+@pytest.mark.parametrize("op", P.OPS)
+def test_brute_force_against_closed_form(oracle_lib, dtype, op):
+    P.pin_brute_force(oracle_lib, dtype, op, max_len=5)
+
+
+def test_pages_fixed_cases(oracle_lib):
+    P.pin_fixed_cases(oracle_lib, "cases")
+
+
+def test_readings_of_cases_the_pages_leave_open(oracle_lib):
+    P.pin_fixed_cases(oracle_lib, "readings")
+
+
+@pytest.mark.parametrize("dtype", P.DTYPES)
+@pytest.mark.parametrize("op", P.OPS)
+def test_numpy_first_occurrence_on_nan_free_rows(oracle_lib, dtype, op):
+    P.pin_numpy_first_occurrence(oracle_lib, dtype, op)
+
+
+def test_rejects_empty_rows(oracle_lib):
+    P.pin_rejects_empty_rows(oracle_lib)
+
+
+def test_closed_form_itself_on_hand_rows():
+    """The checker's closed form on rows small enough to verify by eye."""
+    nan, inf = float("nan"), float("inf")
+    rows = np.array([[1, 3, 3, 2], [nan, 5, 6, 7], [-inf, -inf, nan, -inf],
+                     [2, nan, 9, 9], [-0.0, 0.0, -1, 0.0]])
+    assert P.closed_form(rows, "max").tolist() == [1, 0, 0, 2, 0]
+    assert P.closed_form(rows, "min").tolist() == [0, 0, 0, 0, 2]

@@ -1,0 +1,61 @@
+"""The seeded workloads: shapes, formats, determinism, and the oracle on what their
+construction plants (CPU only)."""
+import numpy as np
+import pytest
+
+from argmin_reduction_wide_amd import workloads as W
+
+SHAPES = {
+    "c1": [("f32", (1, 32000))],
+    "c2": [("f32", (1, 202048))],
+    "c3": [("f16", (32, 202048)), ("bf16", (32, 202048))],
+    "c4": [("f32", (4096, 4096)), ("f64", (4096, 4096))],
+    "c5a": [("f32", (65536, 1024))],
+    "c5b": [("f16", (65536, 64))],
+}
+
+
+def test_bf16_rounding_is_nearest_even():
+    # 1 + 2^-8 is halfway between bf16 1.0 and 1 + 2^-7: ties to even -> 1.0 (0x3F80)
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: ties to even -> 0x3F82
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.0, np.inf, np.nan], np.float32)
+    assert W.f32_to_bf16_bits(vals).tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC000, 0x7F80, 0x7FC0]
+
+
+@pytest.mark.parametrize("which", W.CONFIG_NAMES)
+def test_config_shapes_formats_and_determinism(which):
+    a = W.config_workloads(which)
+    assert [(w.dtype, w.data.shape) for w in a] == SHAPES[which]
+    for w in a:
+        assert w.data.dtype == W.STORAGE[w.dtype] and w.data.flags.c_contiguous
+    if which in ("c1", "c5b"):
+        b = W.config_workloads(which)
+        assert all(np.array_equal(x.data.view(np.uint8), y.data.view(np.uint8)) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("which", W.CONFIG_NAMES)
+def test_oracle_returns_planted_indices(oracle_lib, which):
+    for w in W.config_workloads(which):
+        for op in w.ops:
+            got = oracle_lib.argreduce_lastaxis(w.data, w.dtype, op)
+            for row, want in w.planted.get(op, {}).items():
+                assert got[row] == want, (w.name, op, row)
+            assert got.min() >= 0 and got.max() < w.cols
+
+
+@pytest.mark.parametrize("which", ["c1", "c2", "c5a", "c5b"])
+def test_oracle_matches_numpy_on_nan_free_configs(oracle_lib, which):
+    for w in W.config_workloads(which):
+        v = w.data.astype(np.float64)
+        assert not np.isnan(v).any()
+        for op in w.ops:
+            want = np.argmax(v, axis=1) if op == "max" else np.argmin(v, axis=1)
+            assert np.array_equal(oracle_lib.argreduce_lastaxis(w.data, w.dtype, op), want)
+
+
+def test_planted_counts():
+    w = W.c4_square_f32_f64("f32")
+    assert len(w.planted["max"]) >= 41 + 41  # NaN-led and all -inf rows, plus +inf rows
+    c3 = W.c3_rows32_f16_bf16("f16")
+    assert set(c3.planted["max"].values()) >= {0, 202047}
+    assert 202046 in c3.planted["min"].values()
