@@ -1,0 +1,16 @@
+"""MI355X (gfx950) last-axis ArgMax / ArgMin.
+
+The computation runs in the HIP library ``libargreduce.so`` (C ABI: include/argreduce.h);
+``binding`` marshals arguments into it. Importing this package loads nothing; the library
+is loaded on first use and its absence is an error, never a fallback.
+"""
+from .binding import (  # noqa: F401
+    ArgreduceError,
+    argmax,
+    argmin,
+    argreduce_debug_force_path,
+    argreduce_debug_set_capacity,
+    argreduce_lastaxis,
+    argreduce_plan,
+    argreduce_scratch_bytes,
+)

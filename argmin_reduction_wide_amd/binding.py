@@ -1,0 +1,202 @@
+"""ctypes binding of the HIP library ``libargreduce.so`` (argument marshalling only).
+
+The functions carry the names of the C ABI in include/argreduce.h and take the same
+arguments (device pointers as Python ints). ``argmax`` / ``argmin`` are conveniences for
+torch tensors: torch supplies the device memory (output and scratch) and the current
+HIP stream; every step of the reduction runs in the library's kernels. There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libargreduce.so")
+
+# enums of include/argreduce.h
+F32, F16, BF16, F64 = 0, 1, 2, 3
+MAX, MIN = 0, 1
+PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT = -1, 0, 1, 2
+OK = 0
+ERRORS = {
+    -1: "ARGREDUCE_ERR_INVALID_ARG",
+    -2: "ARGREDUCE_ERR_UNSUPPORTED_DTYPE",
+    -3: "ARGREDUCE_ERR_TOO_WIDE",
+    -4: "ARGREDUCE_ERR_SCRATCH_TOO_SMALL",
+    -5: "ARGREDUCE_ERR_HIP",
+    -6: "ARGREDUCE_ERR_NO_DEVICE",
+}
+DTYPE_NAMES = {"f32": F32, "f16": F16, "bf16": BF16, "f64": F64}
+OP_NAMES = {"max": MAX, "min": MIN}
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+# Exported names of include/argreduce.h (checked by the CPU test suite).
+EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
+           "argreduce_debug_set_capacity", "argreduce_debug_force_path",
+           "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events")
+
+
+class ArgreduceError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({code})")
+        self.code = code
+
+
+class argreduce_plan_t(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
+                ("blocks_per_row", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int64), ("grid_rows", ctypes.c_int64),
+                ("unroll", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("device_threads", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m argmin_reduction_wide_amd.build` (no fallback exists)")
+                # torch ships its own HIP runtime; importing it first makes the library
+                # bind to that one (same soname), so torch's streams and allocations
+                # belong to the runtime that launches our kernels.
+                try:
+                    import torch  # noqa: F401
+                except ImportError:
+                    pass
+                h = ctypes.CDLL(LIB_PATH)
+                i64, sz, vp, c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+                h.argreduce_scratch_bytes.argtypes = [i64, i64, c_int]
+                h.argreduce_scratch_bytes.restype = sz
+                h.argreduce_lastaxis.argtypes = [vp, c_int, i64, i64, c_int, vp, vp, sz, vp]
+                h.argreduce_lastaxis.restype = c_int
+                h.argreduce_plan.argtypes = [i64, i64, c_int, ctypes.POINTER(argreduce_plan_t)]
+                h.argreduce_plan.restype = c_int
+                h.argreduce_debug_set_capacity.argtypes = [i64]
+                h.argreduce_debug_set_capacity.restype = c_int
+                h.argreduce_debug_force_path.argtypes = [c_int]
+                h.argreduce_debug_force_path.restype = c_int
+                h.argreduce_debug_launch_empty.argtypes = [vp]
+                h.argreduce_debug_launch_empty.restype = c_int
+                h.argreduce_debug_set_kernel_events.argtypes = [vp, vp]
+                h.argreduce_debug_set_kernel_events.restype = c_int
+                _lib = h
+    return _lib
+
+
+def _dtype_code(dtype) -> int:
+    return DTYPE_NAMES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _op_code(op) -> int:
+    return OP_NAMES[op] if isinstance(op, str) else int(op)
+
+
+# ---------------------------------------------------------------------------------------
+# C ABI, one Python function per exported symbol
+
+
+def argreduce_scratch_bytes(rows: int, cols: int, dtype) -> int:
+    """Scratch bytes for this shape on the current device; SIZE_MAX on invalid input."""
+    return lib().argreduce_scratch_bytes(rows, cols, _dtype_code(dtype))
+
+
+def argreduce_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, out_ptr: int,
+                       scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
+    """Enqueue the reduction; returns the library's status code (0 = success)."""
+    return lib().argreduce_lastaxis(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
+                                    out_ptr, scratch_ptr, scratch_bytes, stream)
+
+
+def argreduce_plan(rows: int, cols: int, dtype) -> dict:
+    p = argreduce_plan_t()
+    rc = lib().argreduce_plan(rows, cols, _dtype_code(dtype), ctypes.byref(p))
+    if rc != OK:
+        raise ArgreduceError(rc, "argreduce_plan")
+    return p.as_dict()
+
+
+def argreduce_debug_set_capacity(threads: int) -> int:
+    return lib().argreduce_debug_set_capacity(threads)
+
+
+def argreduce_debug_force_path(path: int) -> int:
+    return lib().argreduce_debug_force_path(path)
+
+
+def argreduce_debug_launch_empty(stream: int) -> int:
+    return lib().argreduce_debug_launch_empty(stream)
+
+
+def argreduce_debug_set_kernel_events(start: int, stop: int) -> int:
+    return lib().argreduce_debug_set_kernel_events(start, stop)
+
+
+# ---------------------------------------------------------------------------------------
+# torch conveniences
+
+_TORCH_DTYPES = None
+
+
+def _torch_dtype_code(t) -> int:
+    global _TORCH_DTYPES
+    import torch
+
+    if _TORCH_DTYPES is None:
+        _TORCH_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+                         torch.float64: F64}
+    try:
+        return _TORCH_DTYPES[t.dtype]
+    except KeyError:
+        raise ArgreduceError(-2, f"argreduce on {t.dtype}") from None
+
+
+def _reduce(t, op: int, out=None, scratch=None):
+    import torch
+
+    if not t.is_cuda:
+        raise ValueError("argreduce runs on the GPU only; got a CPU tensor")
+    if t.dim() == 0:
+        raise ValueError("argreduce needs at least one dimension")
+    if not t.is_contiguous():
+        raise ValueError("argreduce needs a contiguous tensor (last axis reduced)")
+    dtype = _torch_dtype_code(t)
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols > 0 else 0
+    if out is None:
+        out = torch.empty(t.shape[:-1], dtype=torch.int64, device=t.device)
+    need = argreduce_scratch_bytes(rows, cols, dtype)
+    if need == SIZE_MAX:
+        raise ArgreduceError(-1, f"argreduce_scratch_bytes(rows={rows}, cols={cols})")
+    if need and (scratch is None or scratch.numel() * scratch.element_size() < need):
+        scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
+    sptr = scratch.data_ptr() if (need and scratch is not None) else 0
+    sbytes = scratch.numel() * scratch.element_size() if (need and scratch is not None) else 0
+    stream = torch.cuda.current_stream(t.device).cuda_stream
+    rc = argreduce_lastaxis(t.data_ptr(), dtype, rows, cols, op, out.data_ptr(), sptr, sbytes,
+                            stream)
+    if rc != OK:
+        raise ArgreduceError(rc, f"argreduce_lastaxis(rows={rows}, cols={cols})")
+    return out
+
+
+def argmax(t, out=None, scratch=None):
+    """Index of the maximum along the last axis (first occurrence; leading NaN -> 0)."""
+    return _reduce(t, MAX, out, scratch)
+
+
+def argmin(t, out=None, scratch=None):
+    """Index of the minimum along the last axis (first occurrence; leading NaN -> 0)."""
+    return _reduce(t, MIN, out, scratch)

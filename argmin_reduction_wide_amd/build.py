@@ -1,0 +1,54 @@
+"""Build the gfx950 HIP library ``libargreduce.so`` in-tree with hipcc.
+
+Usage: ``python -m argmin_reduction_wide_amd.build`` (also called by
+``__graft_entry__.build()``). The library lands next to this file, where the Python
+binding loads it from.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libargreduce.so")
+SOURCES = [os.path.join(CSRC, "argreduce_kernels.hip"), os.path.join(CSRC, "argreduce_api.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def flags() -> list[str]:
+    return [
+        "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+        "-fvisibility=hidden", "-mcode-object-version=5",
+        # IEEE comparisons with subnormals: no fast-math, no flush-to-zero.
+        "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+        # no packed-fp32 instructions in device code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+    ]
+
+
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    cmd = [hipcc(), *flags(), *(extra or []), *SOURCES, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-8000:]}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,242 @@
+// C ABI of the last-axis ArgMax / ArgMin library: argument checks, launch planning, scratch
+// sizing, and the test hooks. Declarations and the contract are in include/argreduce.h.
+//
+// Launch planning follows the geometry rule of "[CUDA] Parallelize ArgMax/ArgMin over wide
+// last axes" (Description / Approach): aim at about one wave of resident threads over the
+// device, give every lane a minimum amount of the row, and split a row over several
+// workgroups only when there are too few rows to fill the device, so that the scratch
+// holding the partials stays bounded by the device's thread capacity. The thresholds are
+// re-derived for gfx950: 64-lane wavefronts, 256 CUs of 2048 resident threads, and 16-byte
+// vector loads as the unit of work of a lane.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <limits>
+
+#include "argreduce.h"
+#include "argreduce_internal.hpp"
+
+#define ARGREDUCE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace argreduce {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kBlock = 256;
+// Rows of up to this many 16-byte vectors (32 KiB) are scanned by one wavefront.
+constexpr int64_t kWaveRowMaxVec = 2048;
+// A split row gives each lane at least this many 16-byte vectors.
+constexpr int64_t kSplitMinVecPerLane = 1;
+constexpr int64_t kMaxBlocksPerRow = 1024;
+// Persistent grids hold this many device-fulls of workgroups; further rows are looped.
+constexpr int64_t kOversubscribe = 1;
+
+std::atomic<int64_t> g_device_threads[kMaxDevices];
+std::atomic<int64_t> g_capacity_override{0};
+std::atomic<int> g_force_path{ARGREDUCE_PATH_AUTO};
+
+int64_t elem_size(int dtype) {
+    switch (dtype) {
+        case ARGREDUCE_F32: return 4;
+        case ARGREDUCE_F16: return 2;
+        case ARGREDUCE_BF16: return 2;
+        case ARGREDUCE_F64: return 8;
+        default: return 0;
+    }
+}
+
+int device_threads(int64_t* threads) {
+    const int64_t forced = g_capacity_override.load(std::memory_order_relaxed);
+    if (forced > 0) {
+        *threads = forced;
+        return ARGREDUCE_OK;
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ARGREDUCE_ERR_NO_DEVICE;
+    if (dev < kMaxDevices) {
+        const int64_t cached = g_device_threads[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *threads = cached;
+            return ARGREDUCE_OK;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+        return ARGREDUCE_ERR_NO_DEVICE;
+    const int64_t t = static_cast<int64_t>(cus) * per_cu;
+    if (dev < kMaxDevices) g_device_threads[dev].store(t, std::memory_order_relaxed);
+    *threads = t;
+    return ARGREDUCE_OK;
+}
+
+int64_t next_pow2(int64_t v) {
+    int64_t p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_shape(int64_t rows, int64_t cols, int dtype) {
+    if (elem_size(dtype) == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || cols < 1) return ARGREDUCE_ERR_INVALID_ARG;
+    if (cols > std::numeric_limits<int32_t>::max()) return ARGREDUCE_ERR_TOO_WIDE;
+    if (rows > std::numeric_limits<int64_t>::max() / (cols * elem_size(dtype)))
+        return ARGREDUCE_ERR_INVALID_ARG;
+    return ARGREDUCE_OK;
+}
+
+int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
+    int rc = check_shape(rows, cols, dtype);
+    if (rc != ARGREDUCE_OK) return rc;
+    int64_t cap = 0;
+    rc = device_threads(&cap);
+    if (rc != ARGREDUCE_OK) return rc;
+
+    const int64_t vec_row = ceil_div(cols * elem_size(dtype), 16);  // 16-byte vectors per row
+    const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
+    const int64_t cap_waves = cap / 64 > 0 ? cap / 64 : 1;
+    const int64_t rows1 = rows > 0 ? rows : 1;
+    const int64_t split_b = [&] {
+        const int64_t fill = cap_blocks / rows1;
+        const int64_t work = vec_row / (kBlock * kSplitMinVecPerLane);
+        int64_t b = fill < work ? fill : work;
+        return b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
+    }();
+
+    int path = g_force_path.load(std::memory_order_relaxed);
+    int64_t group = 64, blocks_per_row = 1;
+    if (path == ARGREDUCE_PATH_AUTO) {
+        if (vec_row <= 32) {
+            path = ARGREDUCE_PATH_SUBWAVE;
+            group = next_pow2(vec_row);
+        } else if (vec_row <= kWaveRowMaxVec || rows >= cap_waves) {
+            path = ARGREDUCE_PATH_SUBWAVE;
+            group = 64;
+        } else if (rows >= cap_blocks || split_b <= 1) {
+            path = ARGREDUCE_PATH_BLOCK;
+        } else {
+            path = ARGREDUCE_PATH_SPLIT;
+            blocks_per_row = split_b;
+        }
+    } else if (path == ARGREDUCE_PATH_SUBWAVE) {
+        group = next_pow2(vec_row) < 64 ? next_pow2(vec_row) : 64;
+    } else if (path == ARGREDUCE_PATH_SPLIT) {
+        blocks_per_row = split_b > 2 ? split_b : 2;
+    }
+
+    *p = Plan{};
+    p->path = path;
+    p->block_threads = static_cast<int>(kBlock);
+    p->unroll = 4;
+    p->device_threads = cap;
+    const int64_t max_grid = cap_blocks * kOversubscribe;
+    if (path == ARGREDUCE_PATH_SUBWAVE) {
+        const int64_t rows_per_block = kBlock / group;
+        const int64_t need = ceil_div(rows1, rows_per_block);
+        p->lanes_per_row = static_cast<int>(group);
+        p->blocks_per_row = 1;
+        p->grid_blocks = need < max_grid ? need : max_grid;
+        p->grid_rows = p->grid_blocks * rows_per_block;
+    } else {
+        int64_t grid_rows = max_grid / blocks_per_row;
+        grid_rows = grid_rows > 0 ? grid_rows : 1;
+        grid_rows = rows1 < grid_rows ? rows1 : grid_rows;
+        p->lanes_per_row = static_cast<int>(blocks_per_row * kBlock);
+        p->blocks_per_row = static_cast<int>(blocks_per_row);
+        p->grid_rows = grid_rows;
+        p->grid_blocks = grid_rows * blocks_per_row;
+    }
+    if (blocks_per_row > 1) {
+        p->counters_bytes = static_cast<size_t>(ceil_div(rows1 * 4, 16) * 16);
+        p->entry_bytes = partial_entry_bytes(dtype);
+        p->scratch_bytes = 15 + p->counters_bytes +
+                           static_cast<size_t>(rows1) * static_cast<size_t>(blocks_per_row) *
+                               p->entry_bytes;
+    }
+    return ARGREDUCE_OK;
+}
+
+}  // namespace
+}  // namespace argreduce
+
+using argreduce::Plan;
+
+ARGREDUCE_EXPORT size_t argreduce_scratch_bytes(int64_t rows, int64_t cols,
+                                                argreduce_dtype_t dtype) {
+    Plan p;
+    if (argreduce::make_plan(rows, cols, dtype, &p) != ARGREDUCE_OK)
+        return std::numeric_limits<size_t>::max();
+    return p.scratch_bytes;
+}
+
+ARGREDUCE_EXPORT int argreduce_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype,
+                                    argreduce_plan_t* out) {
+    if (out == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    Plan p;
+    const int rc = argreduce::make_plan(rows, cols, dtype, &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    out->path = p.path;
+    out->lanes_per_row = p.lanes_per_row;
+    out->blocks_per_row = p.blocks_per_row;
+    out->block_threads = p.block_threads;
+    out->grid_blocks = p.grid_blocks;
+    out->grid_rows = p.grid_rows;
+    out->unroll = p.unroll;
+    out->reserved = 0;
+    out->device_threads = p.device_threads;
+    out->scratch_bytes = p.scratch_bytes;
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_lastaxis(const void* x, argreduce_dtype_t dtype, int64_t rows,
+                                        int64_t cols, argreduce_op_t op, int64_t* out_idx,
+                                        void* scratch, size_t scratch_bytes, void* stream) {
+    int rc = argreduce::check_shape(rows, cols, dtype);
+    if (rc != ARGREDUCE_OK) return rc;
+    if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN) return ARGREDUCE_ERR_INVALID_ARG;
+    if (rows == 0) return ARGREDUCE_OK;
+    if (x == nullptr || out_idx == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % argreduce::elem_size(dtype) != 0 ||
+        reinterpret_cast<uintptr_t>(out_idx) % 8 != 0)
+        return ARGREDUCE_ERR_INVALID_ARG;
+    Plan p;
+    rc = argreduce::make_plan(rows, cols, dtype, &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    uint8_t* scratch16 = nullptr;
+    if (p.scratch_bytes > 0) {
+        if (scratch == nullptr || scratch_bytes < p.scratch_bytes)
+            return ARGREDUCE_ERR_SCRATCH_TOO_SMALL;
+        scratch16 = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(scratch) + 15u) &
+                                               ~static_cast<uintptr_t>(15u));
+    }
+    const hipError_t err = argreduce::launch(p, x, dtype, op, rows, cols, out_idx, scratch16,
+                                             static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ARGREDUCE_OK : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_set_capacity(int64_t threads) {
+    if (threads < 0) return ARGREDUCE_ERR_INVALID_ARG;
+    argreduce::g_capacity_override.store(threads, std::memory_order_relaxed);
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_force_path(int path) {
+    if (path < ARGREDUCE_PATH_AUTO || path > ARGREDUCE_PATH_SPLIT) return ARGREDUCE_ERR_INVALID_ARG;
+    argreduce::g_force_path.store(path, std::memory_order_relaxed);
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_launch_empty(void* stream) {
+    return argreduce::launch_empty(static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ARGREDUCE_OK
+               : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_set_kernel_events(void* start, void* stop) {
+    argreduce::set_kernel_events(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+    return ARGREDUCE_OK;
+}

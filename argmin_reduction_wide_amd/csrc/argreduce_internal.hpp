@@ -1,0 +1,41 @@
+// Host-side declarations shared by the C ABI (argreduce_api.cpp) and the kernel
+// launchers (argreduce_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "argreduce.h"
+
+namespace argreduce {
+
+struct Plan {
+    int path;                // argreduce_path_t
+    int lanes_per_row;       // SUBWAVE: group size G (1..64); BLOCK/SPLIT: blocks * 256
+    int blocks_per_row;      // B
+    int block_threads;       // 256
+    int64_t grid_blocks;
+    int64_t grid_rows;
+    int unroll;
+    int64_t device_threads;
+    size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
+    size_t counters_bytes;   // split path: rows * 4 rounded up to 16
+    size_t entry_bytes;      // split path: bytes per (value, index) partial
+};
+
+// Enqueues the kernels of `plan` on `stream`. `scratch16` is the caller's scratch aligned
+// up to 16 bytes (or null when plan.scratch_bytes == 0). Returns a hipError_t.
+hipError_t launch(const Plan& plan, const void* x, int dtype, int op, int64_t rows, int64_t cols,
+                  int64_t* out, uint8_t* scratch16, hipStream_t stream);
+
+// Launches one empty kernel (the launch floor of the measurement hooks).
+hipError_t launch_empty(hipStream_t stream);
+
+// Events recorded around the row-scanning kernel of every launch when both are set.
+void set_kernel_events(hipEvent_t start, hipEvent_t stop);
+
+// Bytes of one (value, index) partial of the split path for this element format.
+size_t partial_entry_bytes(int dtype);
+
+}  // namespace argreduce

@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X last-axis ArgMax: microseconds per call and achieved HBM GB/s.
+
+Headline workload: ArgMax over fp32 [1, 202048] (vocabulary-sized sampler logits,
+iid N(0, 4), seed 2), the shape the "[CUDA] Parallelize ArgMax/ArgMin over wide last axes"
+page profiles; [4096, 4096] fp32 (iid U(-1,1) with planted inf/NaN rows, seed 4) is timed
+as the second shape of the same metric. A step is one call of the library (every kernel it
+enqueues), on inputs already resident in HBM.
+
+Timing: W untimed warm-up calls, then exactly K calls between two HIP events on the stream
+the library launches on, synchronised on both sides; the inputs rotate through copies that
+together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeats one
+buffer and is reported beside it). The dominant kernel's own duration is measured with HIP
+events recorded around that kernel alone (the library's measurement hook), over a second
+pass of K calls; the roofline uses it. The launch floor is an empty kernel launched the
+same way. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this
+host on a bounded sample of calls of the same workload.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+ROTATE_BYTES = 1 << 29  # 512 MiB of rotated inputs, twice the Infinity Cache
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(rows: int, cols: int, itemsize: int) -> int:
+    """Input read once plus one int64 index written per row."""
+    return rows * cols * itemsize + rows * 8
+
+
+class Case:
+    """One workload on the device: rotated input copies, output, scratch."""
+
+    def __init__(self, w, op: str, rotate_bytes: int = ROTATE_BYTES):
+        import numpy as np
+        import torch
+
+        import argmin_reduction_wide_amd.binding as B
+
+        self.w, self.op, self.B = w, op, B
+        self.rows, self.cols = w.rows, w.cols
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "f64": torch.float64}[w.dtype]
+        flat = w.data.reshape(-1)
+        host = (torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
+                if w.dtype == "bf16" else torch.from_numpy(flat.copy()))
+        self.n_rot = max(1, math.ceil(rotate_bytes / w.nbytes))
+        self.x = torch.empty((self.n_rot, self.rows, self.cols), dtype=tdt, device="cuda")
+        one = host.to("cuda").view(self.rows, self.cols)
+        for i in range(self.n_rot):
+            self.x[i].copy_(one)
+        self.ptrs = [self.x[i].data_ptr() for i in range(self.n_rot)]
+        self.out = torch.empty(self.rows, dtype=torch.int64, device="cuda")
+        self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
+        self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.fn = B.lib().argreduce_lastaxis
+        self.dt = B.DTYPE_NAMES[w.dtype]
+        self.opc = B.OP_NAMES[op]
+        self.bytes = algorithmic_bytes(self.rows, self.cols, w.data.itemsize)
+        self.plan = B.argreduce_plan(self.rows, self.cols, w.dtype)
+
+    def call(self, i: int) -> None:
+        rc = self.fn(self.ptrs[i % self.n_rot], self.dt, self.rows, self.cols, self.opc,
+                     self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"argreduce_lastaxis failed with status {rc}")
+
+    def timed(self, steps: int, warmup: int, rotate: bool = True) -> float:
+        """Microseconds per call over exactly `steps` calls."""
+        import torch
+
+        for i in range(warmup):
+            self.call(i if rotate else 0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            self.call(i if rotate else 0)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / steps
+
+    def graph_timed(self, calls: int, replays: int) -> float:
+        """Microseconds per call when `calls` rotated calls are replayed from a HIP graph."""
+        import torch
+
+        calls = max(1, min(calls, self.n_rot * 4))
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        saved = self.stream
+        with torch.cuda.stream(s):
+            self.stream = s.cuda_stream
+            with torch.cuda.graph(g, stream=s):
+                for i in range(calls):
+                    self.call(i)
+        self.stream = saved
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1000.0 / (calls * replays)
+
+    def kernel_timed(self, steps: int) -> float:
+        """Average duration (us) of the row-scanning kernel alone, from HIP events that the
+        library records immediately around it on the launch stream."""
+        import torch
+
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:  # materialise the hipEvent_t handles on this stream
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        try:
+            for i, (a, b) in enumerate(evs):
+                self.B.argreduce_debug_set_kernel_events(a.cuda_event, b.cuda_event)
+                self.call(i)
+        finally:
+            self.B.argreduce_debug_set_kernel_events(0, 0)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) * 1000.0 / steps
+
+    def result(self):
+        import torch
+
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
+
+
+def launch_floor_us(steps: int) -> float:
+    import torch
+
+    import argmin_reduction_wide_amd.binding as B
+
+    stream = torch.cuda.current_stream().cuda_stream
+    f = B.lib().argreduce_debug_launch_empty
+    for _ in range(50):
+        f(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        f(stream)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / steps
+
+
+def roofline(bytes_per_call: int, kernel_us: float) -> dict:
+    achieved = bytes_per_call / (kernel_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+
+
+def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
+    c = Case(w, op)
+    log(f"[bench] {w.name} arg{op}: plan {c.plan}, {c.n_rot} rotated copies")
+    us = c.timed(steps, warmup, rotate=True)
+    hot = c.timed(steps, warmup // 4 + 1, rotate=False)
+    kus = c.kernel_timed(min(steps, 1000))
+    gus = c.graph_timed(min(steps, 200), max(1, steps // 200)) if graph else None
+    rec = {
+        "workload": w.name, "op": op, "dtype": w.dtype, "rows": c.rows, "cols": c.cols,
+        "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
+        "graph_us_per_call": None if gus is None else round(gus, 3),
+        "kernel_us": round(kus, 3),
+        "gbps_per_call": round(c.bytes / (us * 1e-6) / 1e9, 1),
+        "pct_hbm_peak_per_call": round(100 * c.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes": c.bytes, "rotated_copies": c.n_rot, "plan": c.plan,
+        "roofline": roofline(c.bytes, kus),
+    }
+    log(f"[bench]   {json.dumps(rec)}")
+    rec["_case"] = c
+    return rec
+
+
+def cpu_baseline(w, op: str, seconds: float) -> dict:
+    import oracle
+
+    o = oracle.load()
+    o.argreduce_lastaxis(w.data, w.dtype, op)  # warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        res = o.argreduce_lastaxis(w.data, w.dtype, op)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and n >= 3:
+            break
+    return {"value": round(el / n * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{n} calls of arg{op} {w.dtype} [{w.rows},{w.cols}] (the timed workload's "
+                      f"input) by the single-threaded oracle on one host core, {el:.1f} s",
+            "_result": res}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every configured workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the reduction "
+              "has no multi-GPU path in this build (rows or column slices would shard across "
+              "GPUs with one small exchange; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from argmin_reduction_wide_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} "
+        f"CUs={props.multi_processor_count}")
+
+    primary_w = W.c2_row202048_f32()
+    prim = measure(primary_w, "max", args.steps, args.warmup)
+    sec_w = W.c4_square_f32_f64("f32")
+    sec = measure(sec_w, "max", args.steps, args.warmup)
+    floor = launch_floor_us(args.steps)
+    log(f"[bench] launch floor (empty kernel) {floor:.3f} us")
+
+    extra = []
+    if args.all:
+        for name in W.CONFIG_NAMES:
+            for w in W.config_workloads(name):
+                for op in w.ops:
+                    r = measure(w, op, max(200, args.steps // 4), args.warmup // 4 + 1, graph=False)
+                    r.pop("_case")
+                    extra.append(r)
+                    torch.cuda.empty_cache()
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(primary_w, "max", args.cpu_seconds)
+        res = cpu.pop("_result")
+        parity = bool((prim["_case"].result() == res).all())
+
+    prim.pop("_case")
+    sec.pop("_case")
+    rec = {
+        "metric": "ArgMax µs/call and achieved HBM GB/s (% of peak) at [1,202048] and [4096,4096]",
+        "value": prim["us_per_call"],
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["us_per_call"] / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "ArgMax fp32 [1,202048], iid N(0,4) seed 2, inputs rotated over "
+                               f"{prim['rotated_copies']} HBM-resident copies",
+                   "rows": 1, "cols": 202048, "op": "max", "plan": prim["plan"]},
+        "gbps_per_call": prim["gbps_per_call"],
+        "pct_hbm_peak_per_call": prim["pct_hbm_peak_per_call"],
+        "hot_us_per_call": prim["hot_us_per_call"],
+        "graph_us_per_call": prim["graph_us_per_call"],
+        "kernel_us": prim["kernel_us"],
+        "launch_floor_us": round(floor, 3),
+        "roofline": prim["roofline"],
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+        "secondary": sec,
+        "device": props.name,
+    }
+    if extra:
+        rec["all_configs"] = extra
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

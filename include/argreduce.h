@@ -1,0 +1,157 @@
+/*
+ * argreduce.h -- C ABI of the MI355X (gfx950) last-axis ArgMax / ArgMin library.
+ *
+ * One operation: for every row of a contiguous row-major [rows, cols] tensor, the int64
+ * index of its maximum (ArgMax) or minimum (ArgMin). The result is defined by the
+ * sequential one-thread-per-row scan described in "[CUDA] Parallelize ArgMax/ArgMin over
+ * wide last axes" (ONNX Runtime pull request 32092), Description / Semantics:
+ *   - the result equals, for every input, that of a scan that starts with element 0 as the
+ *     running best and moves to a later element only when it compares strictly greater
+ *     (ArgMax) or strictly less (ArgMin);
+ *   - hence ties resolve to the lowest index (select_last_index == 0);
+ *   - a NaN at index 0 yields 0, a NaN elsewhere is never selected (IEEE comparisons with
+ *     NaN are false);
+ *   - rows made only of -inf, +inf or NaN yield 0; -inf / +inf are ordinary values, which
+ *     is why the parallel merge uses them, not the lowest / highest finite value, as the
+ *     identity of an empty partial result.
+ * Element formats are IEEE binary32 (f32), binary16 (f16), bfloat16 (bf16) and binary64
+ * (f64); comparisons are exact (f16 and bf16 are widened exactly to binary32), subnormals
+ * included.
+ *
+ * Threading, memory and streams (same page, Description / Approach and Testing):
+ *   - every pointer argument is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees, synchronises or prints;
+ *   - all work is enqueued on the caller's HIP stream (`stream` is a hipStream_t, NULL for
+ *     the default stream), so a call may be captured into a HIP graph and replayed;
+ *   - functions are safe to call from several host threads; calls that share one scratch
+ *     buffer must be ordered on one stream.
+ *
+ * Status codes: 0 on success, a negative ARGREDUCE_ERR_* value otherwise. On every error
+ * except ARGREDUCE_ERR_HIP nothing has been enqueued and out_idx is untouched.
+ */
+#ifndef ARGREDUCE_H
+#define ARGREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ARGREDUCE_F32 = 0,  /* IEEE binary32, 4-byte aligned */
+    ARGREDUCE_F16 = 1,  /* IEEE binary16, 2-byte aligned */
+    ARGREDUCE_BF16 = 2, /* bfloat16 (upper half of a binary32), 2-byte aligned */
+    ARGREDUCE_F64 = 3   /* IEEE binary64, 8-byte aligned */
+} argreduce_dtype_t;
+
+typedef enum {
+    ARGREDUCE_MAX = 0, /* ArgMax */
+    ARGREDUCE_MIN = 1  /* ArgMin */
+} argreduce_op_t;
+
+enum {
+    ARGREDUCE_OK = 0,
+    ARGREDUCE_ERR_INVALID_ARG = -1,      /* null pointer with rows > 0, rows < 0, cols < 1,
+                                            bad op, misaligned x or out_idx */
+    ARGREDUCE_ERR_UNSUPPORTED_DTYPE = -2,
+    ARGREDUCE_ERR_TOO_WIDE = -3,         /* cols > INT32_MAX (positions are 32-bit) */
+    ARGREDUCE_ERR_SCRATCH_TOO_SMALL = -4,/* scratch_bytes below argreduce_scratch_bytes() */
+    ARGREDUCE_ERR_HIP = -5,              /* a HIP call or kernel launch failed */
+    ARGREDUCE_ERR_NO_DEVICE = -6         /* no current HIP device to plan for */
+};
+
+/*
+ * Bytes of scratch that argreduce_lastaxis needs for this shape on the CURRENT device
+ * ("[CUDA] Parallelize ArgMax/ArgMin over wide last axes", Description / Approach: the
+ * caller allocates the intermediate buffer; its size is bounded by the device's thread
+ * capacity, so it stays in the low kilobytes for any shape).
+ *
+ * Returns 0 when the chosen launch needs no scratch. The figure already includes up to
+ * 15 bytes of slack, so the buffer may start at any byte address. Returns SIZE_MAX on an
+ * invalid argument (rows < 0, cols < 1, cols > INT32_MAX, bad dtype) or when there is no
+ * current device.
+ */
+size_t argreduce_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dtype);
+
+/*
+ * out_idx[r] = ArgMax / ArgMin of row r of x, for r in [0, rows).
+ *
+ *   x             device pointer to rows * cols elements of `dtype`, row-major, rows
+ *                 contiguous (row r starts at element r * cols); aligned to the element
+ *                 size. Read only.
+ *   rows          >= 0; rows == 0 is a no-op that returns ARGREDUCE_OK.
+ *   cols          1 .. INT32_MAX (an empty row has no index). rows * cols may exceed 2^31.
+ *   out_idx       device pointer to `rows` int64 values, 8-byte aligned. Written only on
+ *                 success; each value lies in [0, cols).
+ *   scratch       device pointer to at least argreduce_scratch_bytes(rows, cols, dtype)
+ *                 bytes, at any byte alignment, with any contents on entry (the library
+ *                 clears what it relies on, stream-ordered). May be NULL when that figure
+ *                 is 0. Its contents after the call are unspecified.
+ *   scratch_bytes size of the scratch buffer in bytes.
+ *   stream        hipStream_t on which all work is enqueued (NULL = default stream).
+ *
+ * The call returns after enqueuing; results are ready when the stream reaches that point.
+ */
+int argreduce_lastaxis(const void *x, argreduce_dtype_t dtype, int64_t rows, int64_t cols,
+                       argreduce_op_t op, int64_t *out_idx, void *scratch,
+                       size_t scratch_bytes, void *stream);
+
+/* ----------------------------------------------------------------------------------------
+ * Launch plan and test hooks. The pages' tests force every dispatch path and simulate
+ * devices of several thread capacities ("[CUDA] Parallelize ArgMax/ArgMin over wide last
+ * axes", Description / Testing); these entry points expose the same controls.
+ */
+
+typedef enum {
+    ARGREDUCE_PATH_AUTO = -1,
+    ARGREDUCE_PATH_SUBWAVE = 0, /* a group of 1..64 lanes of one wavefront per row */
+    ARGREDUCE_PATH_BLOCK = 1,   /* one workgroup per row, rows looped over the grid */
+    ARGREDUCE_PATH_SPLIT = 2    /* several workgroups per row; the last one to finish merges */
+} argreduce_path_t;
+
+typedef struct {
+    int32_t path;             /* argreduce_path_t */
+    int32_t lanes_per_row;    /* lanes that scan one row */
+    int32_t blocks_per_row;   /* workgroups per row (1 unless SPLIT) */
+    int32_t block_threads;    /* threads per workgroup */
+    int64_t grid_blocks;      /* workgroups launched */
+    int64_t grid_rows;        /* rows in flight at once (rows beyond are looped over) */
+    int32_t unroll;           /* 16-byte loads each lane keeps in flight per step */
+    int32_t reserved;
+    int64_t device_threads;   /* thread capacity the plan was made for */
+    size_t scratch_bytes;     /* == argreduce_scratch_bytes() for the same arguments */
+} argreduce_plan_t;
+
+/* The plan argreduce_lastaxis would use for these arguments on the current device. */
+int argreduce_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype, argreduce_plan_t *plan);
+
+/* Plan as if the device held `threads` resident threads (0 = the real device). Process-wide.
+ * Lets tests reach the row-loop and split paths of devices of other sizes, and lets
+ * argreduce_plan / argreduce_scratch_bytes run without a GPU. */
+int argreduce_debug_set_capacity(int64_t threads);
+
+/* Force one path (ARGREDUCE_PATH_AUTO restores the automatic choice). Process-wide.
+ * A forced path keeps its own geometry rules; SPLIT always uses at least two workgroups
+ * per row when the row holds at least two 16-byte vectors. */
+int argreduce_debug_force_path(int path);
+
+/* Measurement hook: the launch floor. Enqueues one empty kernel (one workgroup of 64
+ * threads) on `stream`, the same way argreduce_lastaxis enqueues its kernels, so that a
+ * benchmark can time bare launch latency in the same harness ("[CUDA] Parallelize
+ * ArgMax/ArgMin over wide last axes", Description / Results: per-call times include the
+ * launch). Returns ARGREDUCE_OK or ARGREDUCE_ERR_HIP. */
+int argreduce_debug_launch_empty(void *stream);
+
+/* Measurement hook: when both are non-NULL, every later argreduce_lastaxis call launches
+ * its row-scanning kernel (not the counter reset) with `start` recorded just before and
+ * `stop` just after it on the same stream (hipEvent_t values created by the caller with
+ * timing enabled); NULL, NULL turns this off. Process-wide; for benchmarks only. */
+int argreduce_debug_set_kernel_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARGREDUCE_H */

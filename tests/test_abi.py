@@ -1,0 +1,159 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, validates its
+arguments before touching the GPU, and plans launches by the documented rules (CPU only:
+no kernel is launched here; planning runs under a simulated device capacity)."""
+import os
+import re
+
+import pytest
+
+import argmin_reduction_wide_amd.binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "argreduce.h")
+MI355X_THREADS = 256 * 2048
+H200_THREADS = 132 * 2048
+INT32_MAX = 2 ** 31 - 1
+FAKE = 1 << 20  # an aligned, never-dereferenced address
+
+
+@pytest.fixture
+def lib():
+    h = B.lib()
+    yield h
+    B.argreduce_debug_set_capacity(0)
+    B.argreduce_debug_force_path(B.PATH_AUTO)
+
+
+@pytest.fixture
+def mi355x(lib):
+    assert B.argreduce_debug_set_capacity(MI355X_THREADS) == 0
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(argreduce_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_what_the_binding_names():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_has_no_oracle_dependency():
+    # the product library must not link, load or name the CPU oracle
+    blob = open(B.LIB_PATH, "rb").read()
+    assert b"oracle" not in blob
+
+
+@pytest.mark.parametrize("rows,cols,dtype,op,code", [
+    (-1, 10, B.F32, B.MAX, -1),
+    (4, 0, B.F32, B.MAX, -1),
+    (4, -3, B.F32, B.MAX, -1),
+    (4, 10, 7, B.MAX, -2),
+    (4, 10, -1, B.MAX, -2),
+    (4, 10, B.F32, 2, -1),
+    (1, INT32_MAX + 1, B.F16, B.MAX, -3),
+])
+def test_invalid_arguments_rejected_before_any_gpu_call(lib, rows, cols, dtype, op, code):
+    assert B.argreduce_lastaxis(FAKE, dtype, rows, cols, op, FAKE, 0, 0, 0) == code
+
+
+def test_null_and_misaligned_pointers(lib):
+    assert B.argreduce_lastaxis(0, B.F32, 2, 8, B.MAX, FAKE, 0, 0, 0) == -1
+    assert B.argreduce_lastaxis(FAKE, B.F32, 2, 8, B.MAX, 0, 0, 0, 0) == -1
+    assert B.argreduce_lastaxis(FAKE + 2, B.F32, 2, 8, B.MAX, FAKE, 0, 0, 0) == -1
+    assert B.argreduce_lastaxis(FAKE + 4, B.F64, 2, 8, B.MAX, FAKE, 0, 0, 0) == -1
+    assert B.argreduce_lastaxis(FAKE, B.F32, 2, 8, B.MAX, FAKE + 4, 0, 0, 0) == -1
+
+
+def test_zero_rows_is_a_no_op(lib):
+    assert B.argreduce_lastaxis(0, B.F32, 0, 8, B.MAX, 0, 0, 0, 0) == 0
+
+
+def test_scratch_too_small_is_detected_before_launch(mi355x):
+    need = B.argreduce_scratch_bytes(1, 202048, B.F32)
+    assert 0 < need < 64 * 1024
+    assert B.argreduce_lastaxis(FAKE, B.F32, 1, 202048, B.MAX, FAKE, FAKE, need - 1, 0) == -4
+    assert B.argreduce_lastaxis(FAKE, B.F32, 1, 202048, B.MAX, FAKE, 0, need, 0) == -4
+
+
+def test_scratch_bytes_invalid_arguments(lib):
+    assert B.argreduce_scratch_bytes(1, 0, B.F32) == B.SIZE_MAX
+    assert B.argreduce_scratch_bytes(-1, 5, B.F32) == B.SIZE_MAX
+    assert B.argreduce_scratch_bytes(1, INT32_MAX + 1, B.F32) == B.SIZE_MAX
+    assert B.argreduce_scratch_bytes(1, 5, 9) == B.SIZE_MAX
+
+
+@pytest.mark.parametrize("dtype", [B.F32, B.F16, B.BF16, B.F64])
+@pytest.mark.parametrize("cap", [MI355X_THREADS, H200_THREADS, 4096])
+def test_scratch_is_bounded_by_device_capacity(lib, dtype, cap):
+    """Scratch stays in the low kilobytes for any shape, INT_MAX widths included."""
+    B.argreduce_debug_set_capacity(cap)
+    entry = 16 if dtype == B.F64 else 8
+    bound = 15 + 16 * ((cap // 256) * 4 // 16 + 1) + (cap // 256) * entry
+    for rows in (1, 2, 7, 32, 1000, cap // 256 - 1, cap // 256, 65536):
+        for cols in (1, 63, 64, 4096, 202048, 2 ** 24, INT32_MAX):
+            s = B.argreduce_scratch_bytes(rows, cols, dtype)
+            assert s != B.SIZE_MAX and s <= bound, (rows, cols, s, bound)
+
+
+def test_plan_paths_for_the_measured_shapes(mi355x):
+    p = B.argreduce_plan(1, 202048, B.F32)
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] > 1
+    assert p["scratch_bytes"] == B.argreduce_scratch_bytes(1, 202048, B.F32)
+    assert B.argreduce_plan(32, 202048, B.F16)["path"] == B.PATH_SPLIT
+    assert B.argreduce_plan(1, 32000, B.F32)["path"] == B.PATH_SPLIT
+    p = B.argreduce_plan(65536, 64, B.F16)
+    assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 8
+    assert B.argreduce_plan(65536, 1024, B.F32)["lanes_per_row"] == 64
+    assert B.argreduce_plan(4096, 4096, B.F32)["path"] == B.PATH_SUBWAVE
+    assert B.argreduce_plan(4096, 8, B.F32)["lanes_per_row"] == 2
+
+
+def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
+    """Split rows give each lane at least one 16-byte vector and fill at most one wave."""
+    for rows, cols, dtype in [(1, 32000, B.F32), (1, 202048, B.F32), (8, 202048, B.F32),
+                              (32, 202048, B.F16), (1, 2 ** 24, B.F64), (100, 50000, B.BF16)]:
+        p = B.argreduce_plan(rows, cols, dtype)
+        if p["path"] != B.PATH_SPLIT:
+            continue
+        esize = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}[dtype]
+        vec = -(-cols * esize // 16)
+        assert p["blocks_per_row"] * 256 <= vec
+        assert p["grid_blocks"] <= MI355X_THREADS // 256
+        assert p["grid_rows"] == rows
+
+
+def test_pages_geometry_reading_at_h200_capacity(lib):
+    """At an H200-sized capacity the split rule gives the pages' 197 blocks for
+    [1, 202048] fp32 (4 elements = one 16-byte vector per thread, 256 threads)."""
+    B.argreduce_debug_set_capacity(H200_THREADS)
+    p = B.argreduce_plan(1, 202048, B.F32)
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 197
+
+
+def test_small_capacity_forces_row_loops(lib):
+    B.argreduce_debug_set_capacity(1024)  # four workgroups
+    p = B.argreduce_plan(100, 100000, B.F32)
+    assert p["grid_rows"] < 100 and p["grid_blocks"] <= 4
+    p = B.argreduce_plan(100000, 64, B.F32)
+    assert p["grid_blocks"] <= 4
+
+
+def test_forced_paths(mi355x):
+    assert B.argreduce_debug_force_path(B.PATH_SPLIT) == 0
+    p = B.argreduce_plan(3, 7, B.F32)
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] >= 2 and p["scratch_bytes"] > 0
+    assert B.argreduce_debug_force_path(B.PATH_BLOCK) == 0
+    p = B.argreduce_plan(1, 202048, B.F32)
+    assert p["path"] == B.PATH_BLOCK and p["blocks_per_row"] == 1 and p["scratch_bytes"] == 0
+    assert B.argreduce_debug_force_path(B.PATH_SUBWAVE) == 0
+    p = B.argreduce_plan(1, 202048, B.F32)
+    assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 64
+    assert B.argreduce_debug_force_path(5) == -1
+    assert B.argreduce_debug_set_capacity(-5) == -1

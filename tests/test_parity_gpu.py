@@ -1,0 +1,251 @@
+"""GPU parity: the HIP library against the CPU oracle, bit for bit (int64 indices).
+
+Covers the six measured workloads at full size, the pages' axis-length sweep and our own
+dispatch thresholds, every launch path forced on ragged and misaligned rows under several
+simulated device capacities, a special-value fuzz, widths straddling the widest scan step,
+scratch handling (offsets, dirty contents, undersized buffers), HIP graph capture and
+replay, and INT32_MAX-wide rows. Each case is printed before it runs.
+"""
+import numpy as np
+import pytest
+
+import argmin_reduction_wide_amd.binding as B
+from argmin_reduction_wide_amd import workloads as W
+from gpu_helpers import announce, check, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "f16", "bf16", "f64")
+OPS = ("max", "min")
+VW = {"f32": 4, "f16": 8, "bf16": 8, "f64": 2}
+H200_THREADS = 132 * 2048
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU; none is visible"
+    B.argreduce_debug_set_capacity(0)
+    B.argreduce_debug_force_path(B.PATH_AUTO)
+    yield
+    B.argreduce_debug_set_capacity(0)
+    B.argreduce_debug_force_path(B.PATH_AUTO)
+
+
+@pytest.fixture
+def hooks():
+    yield
+    B.argreduce_debug_set_capacity(0)
+    B.argreduce_debug_force_path(B.PATH_AUTO)
+
+
+def test_device_plan_is_sane():
+    p = B.argreduce_plan(1, 202048, "f32")
+    announce(f"plan [1,202048] f32 on this device: {p}")
+    assert p["device_threads"] >= 256 * 64
+    assert p["path"] == B.PATH_SPLIT
+
+
+@pytest.mark.parametrize("which", W.CONFIG_NAMES)
+def test_config_full_size(oracle_lib, which):
+    for w in W.config_workloads(which):
+        for op in w.ops:
+            got = check(oracle_lib, w.data, w.dtype, op, f"config {which} {w.name} plan="
+                        f"{B.argreduce_plan(w.rows, w.cols, w.dtype)}")
+            for row, want in w.planted.get(op, {}).items():
+                assert got[row] == want, (w.name, op, row)
+
+
+def sweep_cols(dtype):
+    v = VW[dtype]
+    base = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+            300, 1000, 1023, 1025, 4095, 4097, 129280]
+    # our thresholds: 32 vectors (group -> wavefront) and 2048 vectors (wavefront -> split)
+    for nvec in (32, 2048):
+        base += [nvec * v - 1, nvec * v, nvec * v + 1]
+    return sorted(set(base))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("op", OPS)
+def test_axis_length_sweep(oracle_lib, dtype, op):
+    """Axis lengths of both sides of every threshold x rows 1 / 3 / 300 x value kinds."""
+    rng = np.random.default_rng(100 + DTYPES.index(dtype) * 2 + OPS.index(op))
+    for cols in sweep_cols(dtype):
+        for rows in (1, 3, 300):
+            if rows * cols > 8_000_000:
+                continue
+            for kind in ("normal", "ties", "constant", "mixed"):
+                arr = W.random_rows(rng, rows, cols, dtype, kind)
+                check(oracle_lib, arr, dtype, op, f"sweep cols={cols} rows={rows} kind={kind}")
+
+
+FORCED_SHAPES = [(1, 1), (1, 5), (2, 17), (5, 300), (33, 1000), (3, 40000), (700, 129), (4, 70001)]
+
+
+@pytest.mark.parametrize("path", [B.PATH_SUBWAVE, B.PATH_BLOCK, B.PATH_SPLIT])
+@pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
+def test_forced_paths_ragged_misaligned(oracle_lib, hooks, path, cap):
+    rng = np.random.default_rng(7 + path * 10 + cap % 97)
+    B.argreduce_debug_set_capacity(cap)
+    B.argreduce_debug_force_path(path)
+    for dtype in DTYPES:
+        for rows, cols in FORCED_SHAPES:
+            for offset in (0, 1, 3):
+                arr = W.random_rows(rng, rows, cols, dtype, "mixed" if offset else "ties")
+                for op in OPS:
+                    check(oracle_lib, arr, dtype, op,
+                          f"forced path={path} cap={cap} offset={offset} "
+                          f"plan={B.argreduce_plan(rows, cols, dtype)}", offset_elems=offset)
+
+
+@pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
+def test_special_value_fuzz(oracle_lib, hooks, cap):
+    """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal} under several capacities."""
+    rng = np.random.default_rng(1000 + cap % 1013)
+    B.argreduce_debug_set_capacity(cap)
+    for trial in range(40):
+        dtype = DTYPES[trial % 4]
+        rows = int(rng.integers(1, 200))
+        cols = int(rng.choice([1, 2, 5, 31, 64, 100, 257, 1000, 5000, 33333]))
+        kind = "special" if trial % 2 == 0 else "mixed"
+        arr = W.random_rows(rng, rows, cols, dtype, kind)
+        for op in OPS:
+            check(oracle_lib, arr, dtype, op, f"fuzz trial={trial} cap={cap} kind={kind}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_widths_straddling_widest_scan_step(oracle_lib, hooks, dtype):
+    """cols = S-1, S, S+1 where S is the elements one scan step of a row covers."""
+    rng = np.random.default_rng(55)
+    for cap in (1024, 0):
+        B.argreduce_debug_set_capacity(cap)
+        p = B.argreduce_plan(1, 1 << 22, dtype)
+        step = p["lanes_per_row"] * p["unroll"] * VW[dtype]
+        for cols in (step - 1, step, step + 1, 2 * step + 1):
+            if cols > (1 << 24):
+                continue
+            arr = W.random_rows(rng, 1, cols, dtype, "ties")
+            for op in OPS:
+                check(oracle_lib, arr, dtype, op, f"straddle cap={cap} step={step} cols={cols}")
+
+
+def test_scratch_offsets_dirty_and_reuse(oracle_lib):
+    import torch
+
+    rng = np.random.default_rng(77)
+    w = W.c2_row202048_f32()
+    t = to_device(w.data, "f32")
+    want = {op: oracle_lib.argreduce_lastaxis(w.data, "f32", op) for op in OPS}
+    need = B.argreduce_scratch_bytes(1, 202048, "f32")
+    big = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    for off in range(16):
+        for op in OPS:
+            big.copy_(torch.from_numpy(rng.integers(0, 256, need + 64, dtype=np.uint8)))
+            announce(f"scratch offset={off} dirty op={op}")
+            rc, got = run(t, "f32", op, scratch=big, scratch_offset=off)
+            assert rc == 0 and np.array_equal(got, want[op]), (off, op)
+    # the same scratch serves shapes of other sizes in turn
+    for rows, cols, dtype in [(32, 202048, "f16"), (1, 32000, "f32"), (8, 202048, "f64")]:
+        arr = W.random_rows(rng, rows, cols, dtype, "ties")
+        need = B.argreduce_scratch_bytes(rows, cols, dtype)
+        if need > big.numel():
+            big = torch.empty(need, dtype=torch.uint8, device="cuda")
+        for op in OPS:
+            check(oracle_lib, arr, dtype, op, "scratch reuse", scratch=big)
+
+
+def test_undersized_scratch_leaves_output_untouched():
+    import torch
+
+    t = to_device(W.c2_row202048_f32().data, "f32")
+    need = B.argreduce_scratch_bytes(1, 202048, "f32")
+    small = torch.zeros(need - 1, dtype=torch.uint8, device="cuda")
+    announce("undersized scratch")
+    rc, got = run(t, "f32", "max", scratch=small)
+    assert rc == -4
+    assert got.tolist() == [-7]
+
+
+def test_graph_capture_and_replay(oracle_lib):
+    """Capture one call per path into a HIP graph; replay with new inputs; every replay
+    must match the oracle (the counter reset is a kernel, so it replays correctly)."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    for rows, cols, dtype in [(1, 202048, "f32"), (32, 20000, "bf16"), (300, 4096, "f32"),
+                              (4096, 64, "f16")]:
+        x = torch.empty((rows, cols), dtype={"f32": torch.float32, "f16": torch.float16,
+                                            "bf16": torch.bfloat16}[dtype], device="cuda")
+        out = torch.empty(rows, dtype=torch.int64, device="cuda")
+        need = B.argreduce_scratch_bytes(rows, cols, dtype)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        sptr, sbytes = (scratch.data_ptr(), need) if need else (0, 0)
+        announce(f"graph warm-up rows={rows} cols={cols} dtype={dtype} need={need}")
+        assert B.argreduce_lastaxis(x.data_ptr(), dtype, rows, cols, "max", out.data_ptr(),
+                                    sptr, sbytes, torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+        announce(f"graph capture rows={rows} cols={cols} dtype={dtype}")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                rc = B.argreduce_lastaxis(x.data_ptr(), dtype, rows, cols, "max", out.data_ptr(),
+                                          sptr, sbytes, s.cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        for rep in range(10):
+            arr = W.random_rows(rng, rows, cols, dtype, "ties" if rep % 2 else "mixed")
+            x.copy_(to_device(arr, dtype))
+            torch.cuda.synchronize()
+            announce(f"graph replay {rep}")
+            g.replay()
+            torch.cuda.synchronize()
+            want = oracle_lib.argreduce_lastaxis(arr, dtype, "max")
+            assert np.array_equal(out.cpu().numpy(), want), (rows, cols, dtype, rep)
+        del g
+
+
+def test_torch_wrapper_shapes(oracle_lib):
+    import torch
+    import argmin_reduction_wide_amd as ar
+
+    rng = np.random.default_rng(5)
+    arr = W.random_rows(rng, 6, 5000, "f32", "mixed")
+    t = to_device(arr, "f32").view(2, 3, 5000)
+    announce("torch wrapper 3-D")
+    got = ar.argmax(t)
+    assert got.shape == (2, 3) and got.dtype == torch.int64
+    assert np.array_equal(got.reshape(-1).cpu().numpy(), oracle_lib.argreduce_lastaxis(arr, "f32", "max"))
+    got = ar.argmin(t)
+    assert np.array_equal(got.reshape(-1).cpu().numpy(), oracle_lib.argreduce_lastaxis(arr, "f32", "min"))
+    with pytest.raises(ValueError):
+        ar.argmax(torch.zeros(4, 4))  # CPU tensors are refused, never computed on the host
+
+
+def test_int32_max_wide_rows():
+    """[1, INT32_MAX] and [2, 2^30 + 3] f16 (4 GiB each): zeros with planted +1 / -1 values.
+    The expected indices are fixed by the construction (first +1 for ArgMax, first -1 for
+    ArgMin); rows * cols exceeds 2^31 in the second shape."""
+    import torch
+
+    for rows, cols in [(1, 2 ** 31 - 1), (2, 2 ** 30 + 3)]:
+        announce(f"wide rows={rows} cols={cols} f16 alloc")
+        x = torch.zeros((rows, cols), dtype=torch.float16, device="cuda")
+        want_max, want_min = [], []
+        for r in range(rows):
+            k1, k2 = cols - 5 - r, cols - 1
+            x[r, k1] = 1.0
+            x[r, k2] = 1.0
+            x[r, cols - 3] = -1.0
+            x[r, cols - 2] = -1.0
+            want_max.append(k1)
+            want_min.append(cols - 3)
+        for op, want in (("max", want_max), ("min", want_min)):
+            announce(f"wide rows={rows} cols={cols} op={op} plan={B.argreduce_plan(rows, cols, 'f16')}")
+            rc, got = run(x, "f16", op)
+            assert rc == 0 and got.tolist() == want, (rows, cols, op, got)
+        del x
+        torch.cuda.empty_cache()
