@@ -25,11 +25,22 @@ constexpr int kMaxDevices = 64;
 constexpr int64_t kBlock = 256;
 // Rows of up to this many 16-byte vectors (32 KiB) are scanned by one wavefront.
 constexpr int64_t kWaveRowMaxVec = 2048;
-// A split row gives each lane at least this many 16-byte vectors.
-constexpr int64_t kSplitMinVecPerLane = 1;
+// A split row gives each lane about this many 16-byte vectors (all in flight at once).
+constexpr int64_t kSplitVecPerLane = 2;
+// Split rows use at most 1/kSplitFillDiv of one device wave of workgroups: with several
+// rows, fewer workgroups per row (more vectors per lane, fewer partials to merge) measured
+// faster than filling the device.
+constexpr int64_t kSplitFillDiv = 4;
 constexpr int64_t kMaxBlocksPerRow = 1024;
-// Persistent grids hold this many device-fulls of workgroups; further rows are looped.
-constexpr int64_t kOversubscribe = 1;
+// Grids hold at most this many device-fulls of workgroups; further rows are looped over.
+// Many-row shapes run fastest with every row's team launched at once (the dispatcher keeps
+// the CUs fed), so the cap only bounds pathological row counts.
+constexpr int64_t kOversubscribe = 64;
+// 16-byte loads in flight per lane: more costs registers (and with them occupancy);
+// 8-byte elements need twice the registers per loaded vector.
+constexpr int64_t kMaxUnrollWave = 8;
+constexpr int64_t kMaxUnrollWaveF64 = 4;
+constexpr int64_t kMaxUnrollBlocks = 8;
 
 std::atomic<int64_t> g_device_threads[kMaxDevices];
 std::atomic<int64_t> g_capacity_override{0};
@@ -98,14 +109,11 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
 
     const int64_t vec_row = ceil_div(cols * elem_size(dtype), 16);  // 16-byte vectors per row
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
-    const int64_t cap_waves = cap / 64 > 0 ? cap / 64 : 1;
     const int64_t rows1 = rows > 0 ? rows : 1;
-    const int64_t split_b = [&] {
-        const int64_t fill = cap_blocks / rows1;
-        const int64_t work = vec_row / (kBlock * kSplitMinVecPerLane);
-        int64_t b = fill < work ? fill : work;
-        return b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
-    }();
+    const int64_t fill_b = cap_blocks / kSplitFillDiv / rows1;  // workgroups per row allowed
+    const int64_t want_b = ceil_div(vec_row, kBlock * kSplitVecPerLane);
+    int64_t split_b = fill_b < want_b ? fill_b : want_b;
+    split_b = split_b < kMaxBlocksPerRow ? split_b : kMaxBlocksPerRow;
 
     int path = g_force_path.load(std::memory_order_relaxed);
     int64_t group = 64, blocks_per_row = 1;
@@ -113,14 +121,14 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         if (vec_row <= 32) {
             path = ARGREDUCE_PATH_SUBWAVE;
             group = next_pow2(vec_row);
-        } else if (vec_row <= kWaveRowMaxVec || rows >= cap_waves) {
+        } else if (vec_row <= kWaveRowMaxVec) {
             path = ARGREDUCE_PATH_SUBWAVE;
             group = 64;
-        } else if (rows >= cap_blocks || split_b <= 1) {
-            path = ARGREDUCE_PATH_BLOCK;
-        } else {
+        } else if (split_b >= 2) {
             path = ARGREDUCE_PATH_SPLIT;
             blocks_per_row = split_b;
+        } else {
+            path = ARGREDUCE_PATH_BLOCK;
         }
     } else if (path == ARGREDUCE_PATH_SUBWAVE) {
         group = next_pow2(vec_row) < 64 ? next_pow2(vec_row) : 64;
@@ -131,31 +139,41 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     *p = Plan{};
     p->path = path;
     p->block_threads = static_cast<int>(kBlock);
-    p->unroll = 4;
     p->device_threads = cap;
     const int64_t max_grid = cap_blocks * kOversubscribe;
     if (path == ARGREDUCE_PATH_SUBWAVE) {
+        // enough 16-byte loads in flight per lane to cover the row in one step (narrow
+        // groups already hold at most one vector per lane)
+        int64_t unroll = 1;
+        if (group == 64) {
+            const int64_t cap_u = dtype == ARGREDUCE_F64 ? kMaxUnrollWaveF64 : kMaxUnrollWave;
+            unroll = next_pow2(ceil_div(vec_row, 64));
+            unroll = unroll < cap_u ? unroll : cap_u;
+        }
         const int64_t rows_per_block = kBlock / group;
         const int64_t need = ceil_div(rows1, rows_per_block);
         p->lanes_per_row = static_cast<int>(group);
         p->blocks_per_row = 1;
+        p->unroll = static_cast<int>(unroll);
         p->grid_blocks = need < max_grid ? need : max_grid;
         p->grid_rows = p->grid_blocks * rows_per_block;
     } else {
+        int64_t unroll = next_pow2(ceil_div(vec_row, blocks_per_row * kBlock));
+        unroll = unroll < kMaxUnrollBlocks ? unroll : kMaxUnrollBlocks;
         int64_t grid_rows = max_grid / blocks_per_row;
         grid_rows = grid_rows > 0 ? grid_rows : 1;
         grid_rows = rows1 < grid_rows ? rows1 : grid_rows;
         p->lanes_per_row = static_cast<int>(blocks_per_row * kBlock);
         p->blocks_per_row = static_cast<int>(blocks_per_row);
+        p->unroll = static_cast<int>(unroll);
         p->grid_rows = grid_rows;
         p->grid_blocks = grid_rows * blocks_per_row;
     }
     if (blocks_per_row > 1) {
-        p->counters_bytes = static_cast<size_t>(ceil_div(rows1 * 4, 16) * 16);
+        // the published words of every (row, workgroup), plus slack to align the pointer
         p->entry_bytes = partial_entry_bytes(dtype);
-        p->scratch_bytes = 15 + p->counters_bytes +
-                           static_cast<size_t>(rows1) * static_cast<size_t>(blocks_per_row) *
-                               p->entry_bytes;
+        p->scratch_bytes = 15 + static_cast<size_t>(rows1) * static_cast<size_t>(blocks_per_row) *
+                                    p->entry_bytes;
     }
     return ARGREDUCE_OK;
 }

@@ -11,11 +11,12 @@
 //     for ArgMin, index SENTINEL > any position): the identity the page prescribes;
 //   * candidates of different lanes, waves and workgroups are merged with a commutative,
 //     associative rule: the better value wins, equal values go to the lower index;
-//   * the lane that owns the row's first element is seeded with (fix(x[0]), 0), where
-//     fix(NaN) is the op's absorbing value (+inf for ArgMax, -inf for ArgMin) and
-//     fix(v) = v otherwise. A NaN at position 0 then beats every other candidate, which
-//     gives the page's "leading NaN yields index 0"; a -inf (ArgMax) at position 0 is kept
-//     as a real candidate, which gives "a row of -inf returns 0".
+//   * position 0 is taken unconditionally by the lane that visits it (always that lane's
+//     first visit), as the candidate (fix(x[0]), 0), where fix(NaN) is the op's absorbing
+//     value (+inf for ArgMax, -inf for ArgMin) and fix(v) = v otherwise. A NaN at
+//     position 0 then beats every other candidate, which gives the page's "leading NaN
+//     yields index 0"; a -inf (ArgMax) at position 0 is kept as a real candidate, which
+//     gives "a row of -inf returns 0".
 //
 // NaN elsewhere never enters a candidate (every comparison with NaN is false). -0 and +0
 // compare equal, so the index decides. No fast-math, no flush-to-zero: subnormals compare
@@ -122,10 +123,17 @@ struct Cand {
         v = identity();
         i = kSentinel;
     }
-    // Position 0 of the row: taken unconditionally, with NaN replaced by the absorbing value.
-    __device__ void seed(C x0) {
-        v = (x0 != x0) ? absorbing() : x0;
-        i = 0;
+    // Value under which position 0 enters: NaN becomes the absorbing value.
+    __device__ static C fix(C x0) { return (x0 != x0) ? absorbing() : x0; }
+    // Visit of one element by a lane: position 0 (always the lane's first visit) is taken
+    // unconditionally as (fix(e), 0); any other position by the strict update.
+    __device__ void visit(C e, uint32_t pos) {
+        if (pos == 0) {
+            v = fix(e);
+            i = 0;
+        } else {
+            update(e, pos);
+        }
     }
     // Strict update, for positions visited in increasing order by one lane.
     __device__ void update(C e, uint32_t pos) {
@@ -142,23 +150,47 @@ struct Cand {
 };
 
 // ---------------------------------------------------------------------------------------
-// Cross-lane merges.
+// Cross-lane merges, on the DPP crossbar (no LDS round trip).
+//
+// update_dpp keeps a lane's own value where the pattern gives it no source (row_mask),
+// and merging a candidate with itself changes nothing, so every step is safe in all lanes.
 
-template <typename C>
-__device__ inline C shfl_xor(C v, int mask, int width) {
-    return __shfl_xor(v, mask, width);
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(v), static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_val(float v) {
+    return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ inline double dpp_val(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(b));
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(b >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+template <int CTRL, int ROW_MASK, typename C, int OP>
+__device__ inline void dpp_merge(Cand<C, OP>& c) {
+    const C ov = dpp_val<CTRL, ROW_MASK>(c.v);
+    const uint32_t oi = dpp_u32<CTRL, ROW_MASK>(c.i);
+    c.merge(ov, oi);
 }
 
-// Butterfly over aligned groups of G lanes (G a power of two <= 64): every lane of the
-// group ends with the group's merged candidate.
+// Merge over aligned groups of G lanes (G a power of two <= 64). Afterwards the group's
+// last lane (lane % G == G - 1) holds the group's merged candidate; for G <= 16 every lane
+// of the group does. Steps: swap neighbours, swap pairs (quad permutes), mirror within 8,
+// mirror within 16, broadcast lane 15 of each 16-lane row into the next row (rows 1, 3),
+// broadcast lane 31 into rows 2 and 3.
 template <int G, typename C, int OP>
 __device__ inline void group_merge(Cand<C, OP>& c) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) {
-        const C ov = shfl_xor(c.v, m, G);
-        const uint32_t oi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(c.i), m, G));
-        c.merge(ov, oi);
-    }
+    if constexpr (G >= 2) dpp_merge<0xB1, 0xf>(c);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) dpp_merge<0x4E, 0xf>(c);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) dpp_merge<0x141, 0xf>(c);  // row_half_mirror
+    if constexpr (G >= 16) dpp_merge<0x140, 0xf>(c); // row_mirror
+    if constexpr (G >= 32) dpp_merge<0x142, 0xa>(c); // row_bcast:15
+    if constexpr (G >= 64) dpp_merge<0x143, 0xc>(c); // row_bcast:31
 }
 
 // Merge over the whole workgroup; the result is valid in thread 0. Uses LDS and two
@@ -171,19 +203,16 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
     group_merge<kWave>(c);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    if (lane == 0) {
+    if (lane == kWave - 1) {
         s_v[wave] = c.v;
         s_i[wave] = c.i;
     }
     __syncthreads();
-    if (wave == 0) {
-        if (lane < kWaves) {
-            c.v = s_v[lane];
-            c.i = s_i[lane];
-        } else {
-            c.init();
-        }
-        group_merge<kWaves>(c);
+    if (threadIdx.x == 0) {
+        c.v = s_v[0];
+        c.i = s_i[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) c.merge(s_v[w], s_i[w]);
     }
     __syncthreads();  // s_v / s_i may be reused by the caller's next call
 }
@@ -194,31 +223,51 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
 // A team of `team` lanes scans row `row` (cols elements, starting at any address aligned
 // to the element size). The row is cut into a head of up to VW-1 elements before the first
 // 16-byte boundary, a body of nvec 16-byte vectors, and a tail of up to VW-1 elements.
-// Lane `lane` takes head/tail elements lane, lane+team, ... and body vectors lane,
-// lane+team, ... in increasing order, U vectors in flight per step. Positions are 32-bit
-// and formed only after the bounds check: the remaining count (nvec - base) is compared,
-// never a sum that could pass INT32_MAX. Byte offsets are 64-bit.
+// Lane `lane` takes head elements lane, lane+team, ..., then body vectors lane,
+// lane+team, ... (U vectors in flight per step, loaded nontemporally: each byte is read
+// once), then tail elements; its positions therefore increase, and position 0 is the
+// first position of whichever lane visits it.
+//
+// Body vectors feed VW candidates per lane, one per element slot k of a vector, each
+// holding the position of its vector (element k is that position + k): a strict update
+// costs one compare and two selects per element. The slots and the head/tail candidate are
+// merged with the tie rule at the end. Positions are 32-bit and formed only after the
+// bounds check: the remaining count (nvec - base) is compared, never a sum that could pass
+// INT32_MAX. Byte offsets are 64-bit.
 
 template <typename Fmt, int OP, int U, bool kGuard>
 __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base, uint32_t rem,
                                  uint32_t lane, uint32_t team, uint32_t head,
-                                 Cand<typename Fmt::C, OP>& c) {
+                                 Cand<typename Fmt::C, OP> (&s)[Fmt::VW]) {
+    using C = typename Fmt::C;
     u32x4 q[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;
         if (!kGuard || d < rem)
-            q[u] = *reinterpret_cast<const u32x4*>(body + static_cast<size_t>(base + d) * 16u);
+            q[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(body + static_cast<size_t>(base + d) * 16u));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;
         if (!kGuard || d < rem) {
-            typename Fmt::C e[Fmt::VW];
+            C e[Fmt::VW];
             Fmt::unpack(q[u], e);
             const uint32_t pos = head + (base + d) * Fmt::VW;
+            if (u == 0) {
+                // Only the first vector of lane 0 can start at position 0 (head == 0); it is
+                // slot 0's first visit, so position 0 is taken unconditionally.
+                const bool first = (pos == 0);
+                const C e0 = first ? Cand<C, OP>::fix(e[0]) : e[0];
+                const bool t = first || Cand<C, OP>::better(e0, s[0].v);
+                s[0].v = t ? e0 : s[0].v;
+                s[0].i = t ? pos : s[0].i;
+            } else {
+                s[0].update(e[0], pos);
+            }
 #pragma unroll
-            for (int k = 0; k < Fmt::VW; ++k) c.update(e[k], pos + k);
+            for (int k = 1; k < Fmt::VW; ++k) s[k].update(e[k], pos);
         }
     }
 }
@@ -226,32 +275,39 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
 template <typename Fmt, int OP, int U>
 __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, uint32_t lane,
                                 uint32_t team, Cand<typename Fmt::C, OP>& c) {
+    using C = typename Fmt::C;
     c.init();
+    Cand<C, OP> s[Fmt::VW];
+#pragma unroll
+    for (int k = 0; k < Fmt::VW; ++k) s[k].init();
     const uint32_t misalign = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
     uint32_t head = ((16u - misalign) & 15u) / Fmt::kSize;
     head = head < cols ? head : cols;
     const uint32_t nvec = (cols - head) / Fmt::VW;
     const uint32_t tail0 = head + nvec * Fmt::VW;
 
-    if (lane == 0) c.seed(Fmt::load1(row));
     for (uint32_t k = lane; k < head; k += team)
-        c.update(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
 
     const uint8_t* body = row + static_cast<size_t>(head) * Fmt::kSize;  // 16-byte aligned
     const uint32_t step = team * U;
     for (uint32_t base = 0; base < nvec; base += step) {
         const uint32_t rem = nvec - base;
         if (rem >= step) {
-            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, c);
+            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, s);
         } else {
-            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, c);
+            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, s);
             break;
         }
         if (rem == step) break;
     }
 
     for (uint32_t k = tail0 + lane; k < cols; k += team)
-        c.update(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+
+#pragma unroll
+    for (int k = 0; k < Fmt::VW; ++k)
+        if (s[k].i != kSentinel) c.merge(s[k].v, s[k].i + k);
 }
 
 }  // namespace argreduce

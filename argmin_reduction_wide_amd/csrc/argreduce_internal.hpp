@@ -20,8 +20,7 @@ struct Plan {
     int unroll;
     int64_t device_threads;
     size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
-    size_t counters_bytes;   // split path: rows * 4 rounded up to 16
-    size_t entry_bytes;      // split path: bytes per (value, index) partial
+    size_t entry_bytes;      // split path: bytes per published (nonce, index) slot
 };
 
 // Enqueues the kernels of `plan` on `stream`. `scratch16` is the caller's scratch aligned
@@ -35,7 +34,7 @@ hipError_t launch_empty(hipStream_t stream);
 // Events recorded around the row-scanning kernel of every launch when both are set.
 void set_kernel_events(hipEvent_t start, hipEvent_t stop);
 
-// Bytes of one (value, index) partial of the split path for this element format.
+// Bytes of one published slot of the split path.
 size_t partial_entry_bytes(int dtype);
 
 }  // namespace argreduce

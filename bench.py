@@ -10,11 +10,16 @@ enqueues), on inputs already resident in HBM.
 Timing: W untimed warm-up calls, then exactly K calls between two HIP events on the stream
 the library launches on, synchronised on both sides; the inputs rotate through copies that
 together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeats one
-buffer and is reported beside it). The dominant kernel's own duration is measured with HIP
-events recorded around that kernel alone (the library's measurement hook), over a second
-pass of K calls; the roofline uses it. The launch floor is an empty kernel launched the
-same way. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this
-host on a bounded sample of calls of the same workload.
+buffer and is reported beside it). Every call is exactly one launch of one kernel, so the
+timed region divided by K is that kernel's average launch duration; the roofline uses it.
+HIP events recorded around the kernel alone (the library's measurement hook) give a second
+view, reported as kernel_event_us. The launch floor is an empty kernel launched the same
+way. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this host
+on a bounded sample of calls of the same workload.
+
+`--pmc-pass` runs a fixed sequence for hardware-counter collection instead (a 256 MiB
+device copy, whose known bytes calibrate FETCH_SIZE / WRITE_SIZE, then 100 calls of each
+timed workload) and prints nothing on stdout.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -32,6 +37,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = ("argmin_reduction_wide_amd/csrc/argreduce_kernels.hip",
+                  "argmin_reduction_wide_amd/csrc/argreduce_device.hpp",
+                  "argmin_reduction_wide_amd/csrc/argreduce_api.cpp",
+                  "argmin_reduction_wide_amd/csrc/argreduce_internal.hpp",
+                  "include/argreduce.h")
 ROTATE_BYTES = 1 << 29  # 512 MiB of rotated inputs, twice the Infinity Cache
 
 
@@ -170,10 +181,36 @@ def launch_floor_us(steps: int) -> float:
     return e0.elapsed_time(e1) * 1000.0 / steps
 
 
-def roofline(bytes_per_call: int, kernel_us: float) -> dict:
+def kernel_source_hash() -> str:
+    """sha256 over the library sources: counter figures are valid only for this build."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary (scaled by the
+    copy-kernel calibration), or None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(workload)
+    return None if k is None else int(round(k["traffic_bytes"]))
+
+
+def roofline(bytes_per_call: int, kernel_us: float, workload: str = "") -> dict:
     achieved = bytes_per_call / (kernel_us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(workload)}
 
 
 def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
@@ -187,15 +224,45 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
         "workload": w.name, "op": op, "dtype": w.dtype, "rows": c.rows, "cols": c.cols,
         "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
         "graph_us_per_call": None if gus is None else round(gus, 3),
-        "kernel_us": round(kus, 3),
+        "kernel_event_us": round(kus, 3),
         "gbps_per_call": round(c.bytes / (us * 1e-6) / 1e9, 1),
         "pct_hbm_peak_per_call": round(100 * c.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes": c.bytes, "rotated_copies": c.n_rot, "plan": c.plan,
-        "roofline": roofline(c.bytes, kus),
+        "roofline": roofline(c.bytes, us, w.name if op == "max" else ""),
     }
     log(f"[bench]   {json.dumps(rec)}")
     rec["_case"] = c
     return rec
+
+
+COPY_BYTES = 256 << 20
+
+
+def pmc_pass() -> int:
+    """Fixed kernel sequence for counter collection: a device-to-device copy of COPY_BYTES
+    (the calibration: it reads and writes exactly that many bytes), then 100 calls of the
+    [1,202048] and [4096,4096] fp32 ArgMax workloads on rotated inputs."""
+    import torch
+
+    from argmin_reduction_wide_amd import workloads as W
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    for w in (W.c2_row202048_f32(), W.c4_square_f32_f64("f32")):
+        c = Case(w, "max")
+        for i in range(100):
+            c.call(i)
+        torch.cuda.synchronize()
+        log(f"[pmc] {w.name}: 100 calls, {c.bytes} algorithmic bytes per call, plan {c.plan}")
+        del c
+        torch.cuda.empty_cache()
+    return 0
 
 
 def cpu_baseline(w, op: str, seconds: float) -> dict:
@@ -224,6 +291,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every configured workload")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run the counter-collection sequence (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the reduction "
@@ -240,6 +309,9 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} "
         f"CUs={props.multi_processor_count}")
+
+    if args.pmc_pass:
+        return pmc_pass()
 
     primary_w = W.c2_row202048_f32()
     prim = measure(primary_w, "max", args.steps, args.warmup)
@@ -287,7 +359,7 @@ def main() -> int:
         "pct_hbm_peak_per_call": prim["pct_hbm_peak_per_call"],
         "hot_us_per_call": prim["hot_us_per_call"],
         "graph_us_per_call": prim["graph_us_per_call"],
-        "kernel_us": prim["kernel_us"],
+        "kernel_event_us": prim["kernel_event_us"],
         "launch_floor_us": round(floor, 3),
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,

@@ -27,7 +27,10 @@
  *     buffer must be ordered on one stream.
  *
  * Status codes: 0 on success, a negative ARGREDUCE_ERR_* value otherwise. On every error
- * except ARGREDUCE_ERR_HIP nothing has been enqueued and out_idx is untouched.
+ * except ARGREDUCE_ERR_HIP nothing has been enqueued and out_idx is untouched. One
+ * device-side condition cannot be returned by the call: should a workgroup of a split row
+ * never publish its result (not expected: those workgroups wait on nothing), the row's
+ * finalizing workgroup gives up after a bounded wait and stores -1 in out_idx[r].
  */
 #ifndef ARGREDUCE_H
 #define ARGREDUCE_H
@@ -68,8 +71,8 @@ enum {
  * caller allocates the intermediate buffer; its size is bounded by the device's thread
  * capacity, so it stays in the low kilobytes for any shape).
  *
- * Returns 0 when the chosen launch needs no scratch. The figure already includes up to
- * 15 bytes of slack, so the buffer may start at any byte address. Returns SIZE_MAX on an
+ * Returns 0 when the chosen launch needs no scratch, else 8 bytes per (row, workgroup)
+ * of a split row plus 15 bytes of slack, so the buffer may start at any byte address. Returns SIZE_MAX on an
  * invalid argument (rows < 0, cols < 1, cols > INT32_MAX, bad dtype) or when there is no
  * current device.
  */
@@ -86,9 +89,12 @@ size_t argreduce_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dty
  *   out_idx       device pointer to `rows` int64 values, 8-byte aligned. Written only on
  *                 success; each value lies in [0, cols).
  *   scratch       device pointer to at least argreduce_scratch_bytes(rows, cols, dtype)
- *                 bytes, at any byte alignment, with any contents on entry (the library
- *                 clears what it relies on, stream-ordered). May be NULL when that figure
- *                 is 0. Its contents after the call are unspecified.
+ *                 bytes, at any byte alignment, with any contents on entry: a row split
+ *                 over several workgroups publishes one 8-byte word per workgroup, tagged
+ *                 with a per-call nonce, and the call ignores words that do not carry its
+ *                 own nonce and an in-range index (arbitrary contents pass that filter with
+ *                 probability below 2^-32 per word). May be NULL when that figure is 0.
+ *                 The call leaves the words it used zeroed.
  *   scratch_bytes size of the scratch buffer in bytes.
  *   stream        hipStream_t on which all work is enqueued (NULL = default stream).
  *
@@ -133,8 +139,8 @@ int argreduce_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype, argreduc
 int argreduce_debug_set_capacity(int64_t threads);
 
 /* Force one path (ARGREDUCE_PATH_AUTO restores the automatic choice). Process-wide.
- * A forced path keeps its own geometry rules; SPLIT always uses at least two workgroups
- * per row when the row holds at least two 16-byte vectors. */
+ * A forced path keeps its own geometry rules; a forced SPLIT uses at least two workgroups
+ * per row, however short the row. */
 int argreduce_debug_force_path(int path);
 
 /* Measurement hook: the launch floor. Enqueues one empty kernel (one workgroup of 64

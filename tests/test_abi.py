@@ -94,8 +94,10 @@ def test_scratch_bytes_invalid_arguments(lib):
 def test_scratch_is_bounded_by_device_capacity(lib, dtype, cap):
     """Scratch stays in the low kilobytes for any shape, INT_MAX widths included."""
     B.argreduce_debug_set_capacity(cap)
-    entry = 16 if dtype == B.F64 else 8
-    bound = 15 + 16 * ((cap // 256) * 4 // 16 + 1) + (cap // 256) * entry
+    # a split row's workgroups publish 2 (f64: 4) 8-byte words each, and one device wave
+    # of workgroups bounds how many there are
+    entry = 32 if dtype == B.F64 else 16
+    bound = 15 + entry * (cap // 256)
     for rows in (1, 2, 7, 32, 1000, cap // 256 - 1, cap // 256, 65536):
         for cols in (1, 63, 64, 4096, 202048, 2 ** 24, INT32_MAX):
             s = B.argreduce_scratch_bytes(rows, cols, dtype)
@@ -116,7 +118,8 @@ def test_plan_paths_for_the_measured_shapes(mi355x):
 
 
 def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
-    """Split rows give each lane at least one 16-byte vector and fill at most one wave."""
+    """Split rows give each lane at least one 16-byte vector, cover the row in one step of
+    in-flight loads, and fill at most one wave of the device."""
     for rows, cols, dtype in [(1, 32000, B.F32), (1, 202048, B.F32), (8, 202048, B.F32),
                               (32, 202048, B.F16), (1, 2 ** 24, B.F64), (100, 50000, B.BF16)]:
         p = B.argreduce_plan(rows, cols, dtype)
@@ -125,24 +128,32 @@ def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
         esize = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}[dtype]
         vec = -(-cols * esize // 16)
         assert p["blocks_per_row"] * 256 <= vec
+        if p["blocks_per_row"] * 256 * 8 >= vec:
+            assert p["blocks_per_row"] * 256 * p["unroll"] >= vec  # one step of loads
+        else:
+            assert p["unroll"] == 8  # very wide rows loop over steps of 8 vectors per lane
         assert p["grid_blocks"] <= MI355X_THREADS // 256
         assert p["grid_rows"] == rows
 
 
-def test_pages_geometry_reading_at_h200_capacity(lib):
-    """At an H200-sized capacity the split rule gives the pages' 197 blocks for
-    [1, 202048] fp32 (4 elements = one 16-byte vector per thread, 256 threads)."""
+def test_split_is_bounded_by_capacity(lib):
+    """About two 16-byte vectors per lane, and never more workgroups than a quarter of one
+    device wave: at an H200-sized capacity (1056 workgroups of 256 threads) [1, 202048] fp32
+    uses 99 workgroups, and [32, 202048] fp32 is limited to 1056 // 4 // 32 = 8 per row."""
     B.argreduce_debug_set_capacity(H200_THREADS)
     p = B.argreduce_plan(1, 202048, B.F32)
-    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 197
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 99 and p["unroll"] == 2
+    p = B.argreduce_plan(32, 202048, B.F32)
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 8 and p["unroll"] == 8
+    assert p["grid_blocks"] <= H200_THREADS // 256 // 4
 
 
 def test_small_capacity_forces_row_loops(lib):
-    B.argreduce_debug_set_capacity(1024)  # four workgroups
-    p = B.argreduce_plan(100, 100000, B.F32)
-    assert p["grid_rows"] < 100 and p["grid_blocks"] <= 4
+    B.argreduce_debug_set_capacity(1024)  # four workgroups; grids hold 64 device-fulls
+    p = B.argreduce_plan(1000, 100000, B.F32)
+    assert p["path"] == B.PATH_BLOCK and p["grid_rows"] < 1000 and p["grid_blocks"] <= 4 * 64
     p = B.argreduce_plan(100000, 64, B.F32)
-    assert p["grid_blocks"] <= 4
+    assert p["grid_rows"] < 100000 and p["grid_blocks"] <= 4 * 64
 
 
 def test_forced_paths(mi355x):
