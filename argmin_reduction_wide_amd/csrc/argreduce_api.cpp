@@ -23,8 +23,10 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kBlock = 256;
-// Rows of up to this many 16-byte vectors (32 KiB) are scanned by one wavefront.
-constexpr int64_t kWaveRowMaxVec = 2048;
+// Rows of up to this many 16-byte vectors (4 KiB) are scanned by one wavefront; rows of up
+// to kBlockRowMaxVec (32 KiB) by one workgroup with all of a lane's loads in one step.
+constexpr int64_t kWaveRowMaxVec = 256;
+constexpr int64_t kBlockRowMaxVec = 2048;
 // A split row gives each lane about this many 16-byte vectors (all in flight at once).
 constexpr int64_t kSplitVecPerLane = 2;
 // Split rows use at most 1/kSplitFillDiv of one device wave of workgroups: with several
@@ -124,6 +126,10 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         } else if (vec_row <= kWaveRowMaxVec) {
             path = ARGREDUCE_PATH_SUBWAVE;
             group = 64;
+        } else if (vec_row <= kBlockRowMaxVec) {
+            // one workgroup per row, every load of a lane issued at once: measured faster
+            // than a wavefront per row from 4 KiB rows up, and than splitting up to 32 KiB
+            path = ARGREDUCE_PATH_BLOCK;
         } else if (split_b >= 2) {
             path = ARGREDUCE_PATH_SPLIT;
             blocks_per_row = split_b;

@@ -38,44 +38,45 @@ enum Op { kMax = 0, kMin = 1 };
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------------------
-// Element formats. VW = elements per 16-byte vector; C = the (exact) comparison type.
+// Element formats. VW = elements per 16-byte vector; C = the (exact) comparison type;
+// Vec = the 16-byte vector type the body is loaded as. Loading each format as its own
+// vector type keeps the compiler from re-reading parts of a vector through narrower loads.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct F32 {
     using C = float;
+    using Vec = f32x4;
     static constexpr int kSize = 4;
     static constexpr int VW = 4;
     __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
-    __device__ static void unpack(const u32x4 q, C (&e)[VW]) {
-        e[0] = __uint_as_float(q.x);
-        e[1] = __uint_as_float(q.y);
-        e[2] = __uint_as_float(q.z);
-        e[3] = __uint_as_float(q.w);
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
+        e[0] = q.x;
+        e[1] = q.y;
+        e[2] = q.z;
+        e[3] = q.w;
     }
 };
 
 struct F16 {
     using C = float;
+    using Vec = f16x8;
     static constexpr int kSize = 2;
     static constexpr int VW = 8;
-    __device__ static C lo(uint32_t w) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
-    }
-    __device__ static C hi(uint32_t w) {
-        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-    }
     __device__ static C load1(const uint8_t* p) {
         return static_cast<float>(*reinterpret_cast<const _Float16*>(p));
     }
-    __device__ static void unpack(const u32x4 q, C (&e)[VW]) {
-        e[0] = lo(q.x); e[1] = hi(q.x);
-        e[2] = lo(q.y); e[3] = hi(q.y);
-        e[4] = lo(q.z); e[5] = hi(q.z);
-        e[6] = lo(q.w); e[7] = hi(q.w);
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
+#pragma unroll
+        for (int k = 0; k < VW; ++k) e[k] = static_cast<float>(q[k]);
     }
 };
 
 struct BF16 {
     using C = float;
+    using Vec = u32x4;
     static constexpr int kSize = 2;
     static constexpr int VW = 8;
     // bfloat16 is the upper half of a binary32: widening is a shift (exact).
@@ -84,7 +85,7 @@ struct BF16 {
     __device__ static C load1(const uint8_t* p) {
         return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
     }
-    __device__ static void unpack(const u32x4 q, C (&e)[VW]) {
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
         e[0] = lo(q.x); e[1] = hi(q.x);
         e[2] = lo(q.y); e[3] = hi(q.y);
         e[4] = lo(q.z); e[5] = hi(q.z);
@@ -94,12 +95,13 @@ struct BF16 {
 
 struct F64 {
     using C = double;
+    using Vec = f64x2;
     static constexpr int kSize = 8;
     static constexpr int VW = 2;
     __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const double*>(p); }
-    __device__ static void unpack(const u32x4 q, C (&e)[VW]) {
-        e[0] = __hiloint2double(static_cast<int>(q.y), static_cast<int>(q.x));
-        e[1] = __hiloint2double(static_cast<int>(q.w), static_cast<int>(q.z));
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
+        e[0] = q.x;
+        e[1] = q.y;
     }
 };
 
@@ -240,14 +242,18 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
                                  uint32_t lane, uint32_t team, uint32_t head,
                                  Cand<typename Fmt::C, OP> (&s)[Fmt::VW]) {
     using C = typename Fmt::C;
-    u32x4 q[U];
+    using Vec = typename Fmt::Vec;
+    Vec q[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;
         if (!kGuard || d < rem)
             q[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(body + static_cast<size_t>(base + d) * 16u));
+                reinterpret_cast<const Vec*>(body + static_cast<size_t>(base + d) * 16u));
     }
+    // Issue every load of the step before any arithmetic: the scheduler would otherwise
+    // interleave (and, under register pressure, wait on) loads one by one.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;

@@ -113,7 +113,10 @@ def test_plan_paths_for_the_measured_shapes(mi355x):
     p = B.argreduce_plan(65536, 64, B.F16)
     assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 8
     assert B.argreduce_plan(65536, 1024, B.F32)["lanes_per_row"] == 64
-    assert B.argreduce_plan(4096, 4096, B.F32)["path"] == B.PATH_SUBWAVE
+    p = B.argreduce_plan(4096, 4096, B.F32)  # 16 KiB rows: a workgroup each, one step
+    assert p["path"] == B.PATH_BLOCK and p["unroll"] == 4 and p["grid_blocks"] == 4096
+    p = B.argreduce_plan(4096, 4096, B.F64)
+    assert p["path"] == B.PATH_BLOCK and p["unroll"] == 8
     assert B.argreduce_plan(4096, 8, B.F32)["lanes_per_row"] == 2
 
 

@@ -61,8 +61,9 @@ def sweep_cols(dtype):
     v = VW[dtype]
     base = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
             300, 1000, 1023, 1025, 4095, 4097, 129280]
-    # our thresholds: 32 vectors (group -> wavefront) and 2048 vectors (wavefront -> split)
-    for nvec in (32, 2048):
+    # our thresholds: 32 vectors (group -> wavefront), 256 (wavefront -> workgroup) and
+    # 2048 (workgroup -> split)
+    for nvec in (32, 256, 2048):
         base += [nvec * v - 1, nvec * v, nvec * v + 1]
     return sorted(set(base))
 
