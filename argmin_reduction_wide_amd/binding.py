@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libargreduce.so")
 
 # enums of include/argreduce.h
 F32, F16, BF16, F64 = 0, 1, 2, 3
-MAX, MIN = 0, 1
+MAX, MIN, MAX_LAST, MIN_LAST = 0, 1, 2, 3
 PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT = -1, 0, 1, 2
 OK = 0
 ERRORS = {
@@ -29,7 +29,7 @@ ERRORS = {
     -6: "ARGREDUCE_ERR_NO_DEVICE",
 }
 DTYPE_NAMES = {"f32": F32, "f16": F16, "bf16": BF16, "f64": F64}
-OP_NAMES = {"max": MAX, "min": MIN}
+OP_NAMES = {"max": MAX, "min": MIN, "max_last": MAX_LAST, "min_last": MIN_LAST}
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 # Exported names of include/argreduce.h (checked by the CPU test suite).
@@ -192,11 +192,13 @@ def _reduce(t, op: int, out=None, scratch=None):
     return out
 
 
-def argmax(t, out=None, scratch=None):
-    """Index of the maximum along the last axis (first occurrence; leading NaN -> 0)."""
-    return _reduce(t, MAX, out, scratch)
+def argmax(t, out=None, scratch=None, select_last_index: bool = False):
+    """Index of the maximum along the last axis (first occurrence, or the last with
+    select_last_index; NaN is never selected, a leading NaN gives 0)."""
+    return _reduce(t, MAX_LAST if select_last_index else MAX, out, scratch)
 
 
-def argmin(t, out=None, scratch=None):
-    """Index of the minimum along the last axis (first occurrence; leading NaN -> 0)."""
-    return _reduce(t, MIN, out, scratch)
+def argmin(t, out=None, scratch=None, select_last_index: bool = False):
+    """Index of the minimum along the last axis (first occurrence, or the last with
+    select_last_index; NaN is never selected, a leading NaN gives 0)."""
+    return _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch)

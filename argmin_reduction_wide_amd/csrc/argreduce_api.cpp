@@ -221,7 +221,9 @@ ARGREDUCE_EXPORT int argreduce_lastaxis(const void* x, argreduce_dtype_t dtype, 
                                         void* scratch, size_t scratch_bytes, void* stream) {
     int rc = argreduce::check_shape(rows, cols, dtype);
     if (rc != ARGREDUCE_OK) return rc;
-    if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN) return ARGREDUCE_ERR_INVALID_ARG;
+    if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN && op != ARGREDUCE_MAX_LAST &&
+        op != ARGREDUCE_MIN_LAST)
+        return ARGREDUCE_ERR_INVALID_ARG;
     if (rows == 0) return ARGREDUCE_OK;
     if (x == nullptr || out_idx == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(x) % argreduce::elem_size(dtype) != 0 ||

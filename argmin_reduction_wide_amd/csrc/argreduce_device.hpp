@@ -18,6 +18,12 @@
 //     yields index 0"; a -inf (ArgMax) at position 0 is kept as a real candidate, which
 //     gives "a row of -inf returns 0".
 //
+// The last-index ops (ONNX's select_last_index = 1: the same scan with a non-strict
+// comparison) mirror the tie rule: a lane moves to equal later elements, equal values go
+// to the HIGHER index, and the empty candidate's index is -1. A NaN at position 0 enters
+// as (NaN, INT32_MAX): no comparison can displace a NaN value inside a lane, merges give
+// that index priority explicitly, and the result maps it back to 0.
+//
 // NaN elsewhere never enters a candidate (every comparison with NaN is false). -0 and +0
 // compare equal, so the index decides. No fast-math, no flush-to-zero: subnormals compare
 // exactly. Values travel only through compare-and-select, never through min/max
@@ -32,8 +38,13 @@ namespace argreduce {
 constexpr int kBlockThreads = 256;  // threads per workgroup of every kernel
 constexpr int kWave = 64;           // gfx950 wavefront
 constexpr uint32_t kSentinel = 0x7fffffffu;  // > every position (cols <= INT32_MAX)
+constexpr uint32_t kNoneLast = 0xffffffffu;  // -1 as int32: < every position
+constexpr uint32_t kNaN0Last = 0x7fffffffu;  // leading NaN under the last-index ops
 
-enum Op { kMax = 0, kMin = 1 };
+// Values match argreduce_op_t.
+enum Op { kMax = 0, kMin = 1, kMaxLast = 2, kMinLast = 3 };
+__host__ __device__ constexpr bool op_is_max(int op) { return op == kMax || op == kMaxLast; }
+__host__ __device__ constexpr bool op_is_last(int op) { return op == kMaxLast || op == kMinLast; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -113,39 +124,69 @@ struct Cand {
     C v;
     uint32_t i;
 
+    static constexpr bool kMaxOp = op_is_max(OP);
+    static constexpr bool kLast = op_is_last(OP);
+    static constexpr uint32_t kNone = kLast ? kNoneLast : kSentinel;  // empty candidate
+
     __device__ static constexpr C identity() {
-        return OP == kMax ? -__builtin_huge_val() : __builtin_huge_val();
+        return kMaxOp ? -__builtin_huge_val() : __builtin_huge_val();
     }
     __device__ static constexpr C absorbing() {
-        return OP == kMax ? __builtin_huge_val() : -__builtin_huge_val();
+        return kMaxOp ? __builtin_huge_val() : -__builtin_huge_val();
     }
-    __device__ static bool better(C a, C b) { return OP == kMax ? (a > b) : (a < b); }
+    __device__ static bool better(C a, C b) { return kMaxOp ? (a > b) : (a < b); }
+    // Tie preference between two indices: lower wins, or higher for the last-index ops
+    // (compared as signed, so the empty candidate's -1 loses).
+    __device__ static bool tie_wins(uint32_t a, uint32_t b) {
+        return kLast ? static_cast<int32_t>(a) > static_cast<int32_t>(b) : a < b;
+    }
+    // Whether an index can come out of a lane's scan of a row of `cols` elements.
+    __device__ static bool valid_index(uint32_t a, uint32_t cols) {
+        return a < cols || a == kNone || (kLast && a == kNaN0Last);
+    }
+    // The row's result from the merged candidate's index.
+    __device__ static int64_t result(uint32_t a) {
+        return (kLast && a == kNaN0Last) ? int64_t{0} : static_cast<int64_t>(a);
+    }
 
     __device__ void init() {
         v = identity();
-        i = kSentinel;
+        i = kNone;
     }
     // Value under which position 0 enters: NaN becomes the absorbing value.
     __device__ static C fix(C x0) { return (x0 != x0) ? absorbing() : x0; }
-    // Visit of one element by a lane: position 0 (always the lane's first visit) is taken
-    // unconditionally as (fix(e), 0); any other position by the strict update.
+    // Position 0, always the first element its lane visits: taken unconditionally, as
+    // (fix(e), 0); under the last-index ops a NaN there enters as (NaN, INT32_MAX), which
+    // no later element can replace (every comparison with NaN is false).
+    __device__ void take_first(C e) {
+        const bool nan = (e != e);
+        if constexpr (kLast) {
+            v = e;
+            i = nan ? kNaN0Last : 0u;
+        } else {
+            v = nan ? absorbing() : e;
+            i = 0u;
+        }
+    }
+    // Visit of one element by a lane, positions increasing.
     __device__ void visit(C e, uint32_t pos) {
         if (pos == 0) {
-            v = fix(e);
-            i = 0;
+            take_first(e);
         } else {
             update(e, pos);
         }
     }
-    // Strict update, for positions visited in increasing order by one lane.
+    // Update for positions visited in increasing order by one lane: strict comparison, or
+    // non-strict for the last-index ops (false for NaN either way).
     __device__ void update(C e, uint32_t pos) {
-        const bool t = better(e, v);
+        const bool t = kLast ? (better(e, v) || e == v) : better(e, v);
         v = t ? e : v;
         i = t ? pos : i;
     }
-    // Merge with another lane's candidate: better value wins, equal values -> lower index.
+    // Merge with another lane's candidate: better value wins, equal values -> tie rule;
+    // under the last-index ops a leading NaN (index INT32_MAX) wins outright.
     __device__ void merge(C ov, uint32_t oi) {
-        const bool t = better(ov, v) || (ov == v && oi < i);
+        const bool t = (kLast && oi == kNaN0Last) || better(ov, v) || (ov == v && tie_wins(oi, i));
         v = t ? ov : v;
         i = t ? oi : i;
     }
@@ -264,11 +305,13 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
             if (u == 0) {
                 // Only the first vector of lane 0 can start at position 0 (head == 0); it is
                 // slot 0's first visit, so position 0 is taken unconditionally.
+                Cand<C, OP> t0 = s[0];
+                t0.update(e[0], pos);
+                Cand<C, OP> f0;
+                f0.take_first(e[0]);
                 const bool first = (pos == 0);
-                const C e0 = first ? Cand<C, OP>::fix(e[0]) : e[0];
-                const bool t = first || Cand<C, OP>::better(e0, s[0].v);
-                s[0].v = t ? e0 : s[0].v;
-                s[0].i = t ? pos : s[0].i;
+                s[0].v = first ? f0.v : t0.v;
+                s[0].i = first ? f0.i : t0.i;
             } else {
                 s[0].update(e[0], pos);
             }
@@ -313,7 +356,7 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
 
 #pragma unroll
     for (int k = 0; k < Fmt::VW; ++k)
-        if (s[k].i != kSentinel) c.merge(s[k].v, s[k].i + k);
+        if (s[k].i != Cand<C, OP>::kNone) c.merge(s[k].v, s[k].i + k);
 }
 
 }  // namespace argreduce

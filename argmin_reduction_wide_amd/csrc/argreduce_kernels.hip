@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
         Cand<typename Fmt::C, OP> c;
         scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
         group_merge<G>(c);
-        if (lane == G - 1) out[r] = static_cast<int64_t>(c.i);
+        if (lane == G - 1) out[r] = Cand<typename Fmt::C, OP>::result(c.i);
     }
 }
 
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
         scan_row<Fmt, OP, U>(row, cols, lane, team, c);
         block_merge(c);
         if (B == 1) {
-            if (threadIdx.x == 0) out[r] = static_cast<int64_t>(c.i);
+            if (threadIdx.x == 0) out[r] = Cand<C, OP>::result(c.i);
             continue;
         }
         uint64_t* rs = slots + static_cast<size_t>(r) * B * Words<C>::kStride;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
                     ok = ok && (w[j] & 0xffffffff00000000ull) == tag;
                     pay[j] = static_cast<uint32_t>(w[j]);
                 }
-                ok = ok && (pay[0] < cols || pay[0] == kSentinel);
+                ok = ok && Cand<C, OP>::valid_index(pay[0], cols);
                 if (!ok) {
                     if (++spins > kSpinLimit) {
                         s_timeout = 1;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
                 __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         block_merge(m);
-        if (threadIdx.x == 0) out[r] = s_timeout ? int64_t{-1} : static_cast<int64_t>(m.i);
+        if (threadIdx.x == 0) out[r] = s_timeout ? int64_t{-1} : Cand<C, OP>::result(m.i);
     }
 }
 
@@ -259,8 +259,13 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
 template <typename Fmt>
 hipError_t launch_op(const Plan& p, const void* x, int op, int64_t rows, int64_t cols, int64_t* out,
                      uint8_t* scratch16, hipStream_t s) {
-    return op == ARGREDUCE_MAX ? launch_fmt<Fmt, kMax>(p, x, rows, cols, out, scratch16, s)
-                               : launch_fmt<Fmt, kMin>(p, x, rows, cols, out, scratch16, s);
+    switch (op) {
+        case ARGREDUCE_MAX: return launch_fmt<Fmt, kMax>(p, x, rows, cols, out, scratch16, s);
+        case ARGREDUCE_MIN: return launch_fmt<Fmt, kMin>(p, x, rows, cols, out, scratch16, s);
+        case ARGREDUCE_MAX_LAST: return launch_fmt<Fmt, kMaxLast>(p, x, rows, cols, out, scratch16, s);
+        case ARGREDUCE_MIN_LAST: return launch_fmt<Fmt, kMinLast>(p, x, rows, cols, out, scratch16, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace

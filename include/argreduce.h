@@ -50,8 +50,15 @@ typedef enum {
 } argreduce_dtype_t;
 
 typedef enum {
-    ARGREDUCE_MAX = 0, /* ArgMax */
-    ARGREDUCE_MIN = 1  /* ArgMin */
+    ARGREDUCE_MAX = 0,      /* ArgMax, ties to the lowest index */
+    ARGREDUCE_MIN = 1,      /* ArgMin, ties to the lowest index */
+    /* Ties to the HIGHEST index: ONNX's select_last_index = 1, which the first page's
+     * Semantics section names and leaves to the CPU. Defined here as the same sequential
+     * scan with the non-strict comparison (>= / <=): a later equal element replaces the
+     * running best, NaN is still never selected, a NaN at index 0 still yields 0, and a row
+     * of all -inf (ArgMax) yields its last index. */
+    ARGREDUCE_MAX_LAST = 2,
+    ARGREDUCE_MIN_LAST = 3
 } argreduce_op_t;
 
 enum {

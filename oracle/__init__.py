@@ -13,7 +13,9 @@ compiles it with gcc and marshals numpy arrays into it.
 
 Element formats are given as strings: ``"f32"`` (numpy float32), ``"f16"`` (numpy
 float16), ``"bf16"`` (numpy uint16 holding bfloat16 bit patterns) and ``"f64"`` (numpy
-float64). Ops are ``"max"`` (ArgMax) and ``"min"`` (ArgMin).
+float64). Ops are ``"max"`` (ArgMax), ``"min"`` (ArgMin), and ``"max_last"`` /
+``"min_last"`` (ties to the last index, ONNX's select_last_index = 1: the same scan with
+a non-strict comparison).
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ _SRC = os.path.join(_HERE, "argreduce_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_argreduce.so")
 
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
-OP_CODE = {"max": 0, "min": 1}
+OP_CODE = {"max": 0, "min": 1, "max_last": 2, "min_last": 3}
 NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64}
 
 # -O2, IEEE semantics: no -ffast-math, no -ffinite-math-only, no flush-to-zero.

@@ -22,6 +22,11 @@
  *   comparison, which is false whenever either operand is NaN. The index of the final
  *   running best is the result, stored as int64.
  *
+ *   Last-index variants (ONNX's select_last_index = 1, which the first page names in its
+ *   Semantics section and leaves to the CPU): the same scan with the non-strict comparison
+ *   (greater-or-equal / less-or-equal), so that a later equal element replaces the
+ *   running best. The pages define no more than that; this is the plain reading.
+ *
  *   Elements are widened to double before they are compared. For f16, bf16 and f32 the
  *   widening is exact and order-preserving, NaN stays NaN and -0 / +0 keep comparing
  *   equal, so a comparison of two widened elements has the same outcome as the same
@@ -42,6 +47,8 @@
 
 #define ORACLE_ARGMAX 0
 #define ORACLE_ARGMIN 1
+#define ORACLE_ARGMAX_LAST 2
+#define ORACLE_ARGMIN_LAST 3
 
 /* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 static double decode_f16(uint16_t h)
@@ -107,7 +114,7 @@ int oracle_argreduce_lastaxis(const void *x, int dtype, int64_t rows, int64_t co
                               int op, int64_t *out)
 {
     if (rows < 0 || cols < 1 || dtype < ORACLE_F32 || dtype > ORACLE_F64 ||
-        (op != ORACLE_ARGMAX && op != ORACLE_ARGMIN))
+        op < ORACLE_ARGMAX || op > ORACLE_ARGMIN_LAST)
         return -1;
     for (int64_t r = 0; r < rows; ++r) {
         const int64_t row0 = r * cols;
@@ -115,7 +122,13 @@ int oracle_argreduce_lastaxis(const void *x, int dtype, int64_t rows, int64_t co
         int64_t idx = 0;
         for (int64_t j = 1; j < cols; ++j) {
             const double a = element(x, dtype, row0 + j);
-            const int better = (op == ORACLE_ARGMAX) ? (a > best) : (a < best);
+            int better;
+            switch (op) {
+            case ORACLE_ARGMAX: better = a > best; break;
+            case ORACLE_ARGMIN: better = a < best; break;
+            case ORACLE_ARGMAX_LAST: better = a >= best; break;
+            default: better = a <= best; break;
+            }
             if (better) {
                 best = a;
                 idx = j;

@@ -10,14 +10,17 @@ disagrees with something fixed from outside it:
   of length 1..5 drawn from a 9-symbol alphabet of special values;
 * the scan against the fixed cases the ONNX Runtime pages state (tests/golden);
 * the scan against numpy.argmax / numpy.argmin, which return the first occurrence of the
-  extremum and agree with the definition on NaN-free rows.
+  extremum and agree with the definition on NaN-free rows (on reversed rows for the
+  last-index ops).
 
 The closed form is derived as follows. If element 0 is NaN the scan never moves (every
 comparison with NaN is false), so the result is 0. Otherwise the running best is never
 NaN, a NaN element is never taken, and the strict comparison moves only to a strictly
 better element; so the scan ends at the first position holding the extremum of the
 non-NaN elements (which include element 0). -0 and +0 compare equal; -inf and +inf are
-ordinary extremes.
+ordinary extremes. With the non-strict comparison of the last-index ops the scan also
+moves to equal elements, so it ends at the LAST position holding that extremum (and still
+at 0 when element 0 is NaN, since every comparison with the NaN running best is false).
 
 These functions are shared by tests/test_oracle_pins.py (run on the real oracle) and by
 tests/test_oracle_mutants.py (run on deliberately broken copies of it, each of which must
@@ -35,7 +38,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "pages_fixed_cases.json")
 DTYPES = ("f32", "f16", "bf16", "f64")
-OPS = ("max", "min")
+OPS = ("max", "min", "max_last", "min_last")
 
 MIN_SUBNORMAL = {"f32": 2.0 ** -149, "f16": 2.0 ** -24, "bf16": 2.0 ** -133, "f64": 2.0 ** -1074}
 MAX_FINITE = {"f32": float(np.finfo(np.float32).max), "f16": 65504.0,
@@ -62,15 +65,20 @@ def exact_storage(values, dtype: str) -> np.ndarray:
 
 
 def closed_form(values: np.ndarray, op: str) -> np.ndarray:
-    """First position of the extremum of the non-NaN elements; 0 when element 0 is NaN."""
+    """First (last, for the *_last ops) position of the extremum of the non-NaN elements;
+    0 when element 0 is NaN."""
     v = np.asarray(values, dtype=np.float64)
     nan = np.isnan(v)
-    if op == "max":
+    if op in ("max", "max_last"):
         ext = np.where(nan, -np.inf, v).max(axis=1)
     else:
         ext = np.where(nan, np.inf, v).min(axis=1)
-    first = (v == ext[:, None]).argmax(axis=1)
-    return np.where(nan[:, 0], 0, first).astype(np.int64)
+    hit = v == ext[:, None]
+    if op.endswith("_last"):
+        pos = v.shape[1] - 1 - hit[:, ::-1].argmax(axis=1)
+    else:
+        pos = hit.argmax(axis=1)
+    return np.where(nan[:, 0], 0, pos).astype(np.int64)
 
 
 def symbol(s, dtype: str) -> float:
@@ -176,7 +184,11 @@ def pin_numpy_first_occurrence(o, dtype: str, op: str) -> None:
                 v = ((v.view(np.uint32) >> np.uint32(16)) << np.uint32(16)).view(np.float32)
             v = v.astype({"f32": np.float32, "f16": np.float16, "bf16": np.float32,
                           "f64": np.float64}[dtype]).astype(np.float64)
-            want = np.argmax(v, axis=1) if op == "max" else np.argmin(v, axis=1)
+            f = np.argmax if op.startswith("max") else np.argmin
+            if op.endswith("_last"):
+                want = cols - 1 - f(v[:, ::-1], axis=1)
+            else:
+                want = f(v, axis=1)
             got = o.argreduce_lastaxis(exact_storage(v, dtype), dtype, op)
             assert np.array_equal(got, want), f"{dtype} {op} {rows}x{cols} {kind} vs numpy"
 

@@ -56,7 +56,8 @@ def test_library_has_no_oracle_dependency():
     (4, -3, B.F32, B.MAX, -1),
     (4, 10, 7, B.MAX, -2),
     (4, 10, -1, B.MAX, -2),
-    (4, 10, B.F32, 2, -1),
+    (4, 10, B.F32, 4, -1),
+    (4, 10, B.F32, -1, -1),
     (1, INT32_MAX + 1, B.F16, B.MAX, -3),
 ])
 def test_invalid_arguments_rejected_before_any_gpu_call(lib, rows, cols, dtype, op, code):

@@ -13,11 +13,19 @@ import oracle_pins as P
 SRC = os.path.join(os.path.dirname(oracle.__file__), "argreduce_oracle.c")
 
 # (name, original text, planted mistake)
+MAX_CASE = "case ORACLE_ARGMAX: better = a > best;"
 MUTANTS = [
-    ("ties_to_last_index", "? (a > best) :", "? (a >= best) :"),
-    ("argmin_compares_the_wrong_way", ": (a < best);", ": (a > best);"),
-    ("nan_unsafe_compare", "? (a > best) :", "? !(a <= best) :"),
-    ("signed_zero_ordered", "? (a > best) :", "? (a > best || (a == best && signbit(best) && !signbit(a))) :"),
+    ("ties_to_last_index", MAX_CASE, "case ORACLE_ARGMAX: better = a >= best;"),
+    ("argmin_compares_the_wrong_way", "case ORACLE_ARGMIN: better = a < best;",
+     "case ORACLE_ARGMIN: better = a > best;"),
+    ("nan_unsafe_compare", MAX_CASE, "case ORACLE_ARGMAX: better = !(a <= best);"),
+    ("signed_zero_ordered", MAX_CASE,
+     "case ORACLE_ARGMAX: better = a > best || (a == best && signbit(best) && !signbit(a));"),
+    ("last_index_ties_to_first", "case ORACLE_ARGMAX_LAST: better = a >= best;",
+     "case ORACLE_ARGMAX_LAST: better = a > best;"),
+    ("min_last_strict", "default: better = a <= best;", "default: better = a < best;"),
+    ("last_index_nan_unsafe", "case ORACLE_ARGMAX_LAST: better = a >= best;",
+     "case ORACLE_ARGMAX_LAST: better = !(a < best);"),
     ("identity_seed_instead_of_element0",
      "double best = element(x, dtype, row0);",
      "double best = (op == ORACLE_ARGMAX) ? -INFINITY : INFINITY;"),

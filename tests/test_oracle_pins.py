@@ -50,3 +50,5 @@ def test_closed_form_itself_on_hand_rows():
                      [2, nan, 9, 9], [-0.0, 0.0, -1, 0.0]])
     assert P.closed_form(rows, "max").tolist() == [1, 0, 0, 2, 0]
     assert P.closed_form(rows, "min").tolist() == [0, 0, 0, 0, 2]
+    assert P.closed_form(rows, "max_last").tolist() == [2, 0, 3, 3, 3]
+    assert P.closed_form(rows, "min_last").tolist() == [0, 0, 3, 0, 2]

@@ -16,7 +16,7 @@ from gpu_helpers import announce, check, run, to_device
 pytestmark = pytest.mark.gpu
 
 DTYPES = ("f32", "f16", "bf16", "f64")
-OPS = ("max", "min")
+OPS = ("max", "min", "max_last", "min_last")
 VW = {"f32": 4, "f16": 8, "bf16": 8, "f64": 2}
 H200_THREADS = 132 * 2048
 
@@ -55,6 +55,14 @@ def test_config_full_size(oracle_lib, which):
                         f"{B.argreduce_plan(w.rows, w.cols, w.dtype)}")
             for row, want in w.planted.get(op, {}).items():
                 assert got[row] == want, (w.name, op, row)
+
+
+@pytest.mark.parametrize("which", W.CONFIG_NAMES)
+def test_config_full_size_last_index(oracle_lib, which):
+    """The same workloads under the last-index ops (ties to the highest index)."""
+    for w in W.config_workloads(which):
+        for op in w.ops:
+            check(oracle_lib, w.data, w.dtype, op + "_last", f"config {which} {w.name} last")
 
 
 def sweep_cols(dtype):
