@@ -54,6 +54,11 @@ class Oracle:
         f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_void_p]
         f.restype = ctypes.c_int
+        a = lib.oracle_argreduce_axis
+        a.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                      ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+        a.restype = ctypes.c_int
+        self._a = a
         d = lib.oracle_widen
         d.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
         d.restype = ctypes.c_int
@@ -67,6 +72,21 @@ class Oracle:
         rc = self._f(x.ctypes.data, DTYPE_CODE[dtype], rows, cols, OP_CODE[op], out.ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle rejected rows={rows} cols={cols} dtype={dtype} op={op}")
+        return out
+
+    def argreduce_axis(self, x: np.ndarray, dtype: str, op: str) -> np.ndarray:
+        """int64 index over the middle axis of the 3-D array ``x`` (outer, len, inner);
+        result shape (outer, inner)."""
+        want = NUMPY_STORAGE[dtype]
+        if x.dtype != want or x.ndim != 3:
+            raise TypeError(f"{dtype} data must be a 3-D {np.dtype(want)} array")
+        x = np.ascontiguousarray(x)
+        outer, length, inner = x.shape
+        out = np.empty((outer, inner), dtype=np.int64)
+        rc = self._a(x.ctypes.data, DTYPE_CODE[dtype], outer, length, inner, OP_CODE[op],
+                     out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected shape {x.shape} dtype={dtype} op={op}")
         return out
 
     def widen(self, x: np.ndarray, dtype: str) -> np.ndarray:

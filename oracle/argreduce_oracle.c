@@ -105,6 +105,20 @@ static double element(const void *x, int dtype, int64_t k)
     }
 }
 
+/* Whether the scan moves from the running best to element a (IEEE comparisons: false
+ * whenever either operand is NaN). */
+static int moves(int op, double a, double best)
+{
+    int better;
+    switch (op) {
+    case ORACLE_ARGMAX: better = a > best; break;
+    case ORACLE_ARGMIN: better = a < best; break;
+    case ORACLE_ARGMAX_LAST: better = a >= best; break;
+    default: better = a <= best; break;
+    }
+    return better;
+}
+
 /*
  * out[r] = index chosen by the sequential strict-compare scan of row r.
  * Returns 0 on success, -1 on an argument the definition does not cover
@@ -122,19 +136,43 @@ int oracle_argreduce_lastaxis(const void *x, int dtype, int64_t rows, int64_t co
         int64_t idx = 0;
         for (int64_t j = 1; j < cols; ++j) {
             const double a = element(x, dtype, row0 + j);
-            int better;
-            switch (op) {
-            case ORACLE_ARGMAX: better = a > best; break;
-            case ORACLE_ARGMIN: better = a < best; break;
-            case ORACLE_ARGMAX_LAST: better = a >= best; break;
-            default: better = a <= best; break;
-            }
-            if (better) {
+            if (moves(op, a, best)) {
                 best = a;
                 idx = j;
             }
         }
         out[r] = idx;
+    }
+    return 0;
+}
+
+/*
+ * Reduction over the middle axis of a contiguous [outer, len, inner] tensor:
+ * out[o * inner + i] = index chosen by the same sequential scan over r = 0 .. len-1 of
+ * the elements x[o][r][i] (flat position (o * len + r) * inner + i). With inner == 1 this
+ * is the last-axis reduction above. ONNX Runtime's CUDA provider leaves this case to its
+ * fallback ("[CUDA] Parallelize ArgMax/ArgMin over wide last axes", Semantics).
+ */
+int oracle_argreduce_axis(const void *x, int dtype, int64_t outer, int64_t len, int64_t inner,
+                          int op, int64_t *out)
+{
+    if (outer < 0 || len < 1 || inner < 1 || dtype < ORACLE_F32 || dtype > ORACLE_F64 ||
+        op < ORACLE_ARGMAX || op > ORACLE_ARGMIN_LAST)
+        return -1;
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t i = 0; i < inner; ++i) {
+            const int64_t base = o * len * inner + i;
+            double best = element(x, dtype, base);
+            int64_t idx = 0;
+            for (int64_t r = 1; r < len; ++r) {
+                const double a = element(x, dtype, base + r * inner);
+                if (moves(op, a, best)) {
+                    best = a;
+                    idx = r;
+                }
+            }
+            out[o * inner + i] = idx;
+        }
     }
     return 0;
 }

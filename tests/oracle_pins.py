@@ -193,6 +193,35 @@ def pin_numpy_first_occurrence(o, dtype: str, op: str) -> None:
             assert np.array_equal(got, want), f"{dtype} {op} {rows}x{cols} {kind} vs numpy"
 
 
+def pin_axis(o, dtype: str, op: str) -> None:
+    """The middle-axis scan against the closed form applied to the transposed data, and
+    against the last-axis scan when inner == 1."""
+    rng = np.random.default_rng(31 + DTYPES.index(dtype) * 4 + OPS.index(op))
+    alpha = alphabet9(dtype)
+    for outer, length, inner in ((1, 1, 1), (2, 5, 3), (3, 17, 1), (1, 64, 33), (4, 9, 70),
+                                 (2, 300, 5)):
+        vals = alpha[rng.integers(0, alpha.size, size=(outer, length, inner))]
+        if length > 5:  # mostly ordinary values, with ties, so rows have a real extremum
+            q = np.clip(np.rint(4 * rng.standard_normal((outer, length, inner))), -8, 7) / 4
+            keep = rng.random((outer, length, inner)) < 0.9
+            vals = np.where(keep, q, vals)
+        got = o.argreduce_axis(exact_storage(vals, dtype), dtype, op)
+        rows = np.moveaxis(vals, 1, 2).reshape(outer * inner, length)
+        want = closed_form(rows, op).reshape(outer, inner)
+        assert np.array_equal(got, want), f"axis {dtype} {op} {vals.shape}"
+        if inner == 1:
+            last = o.argreduce_lastaxis(exact_storage(vals[:, :, 0], dtype), dtype, op)
+            assert np.array_equal(got[:, 0], last), f"axis vs last axis {dtype} {op}"
+    v = rng.standard_normal((3, 40, 7))
+    if dtype == "bf16":
+        v = ((v.astype(np.float32).view(np.uint32) >> np.uint32(16)) << np.uint32(16)).view(np.float32)
+    v = v.astype({"f32": np.float32, "f16": np.float16, "bf16": np.float32,
+                  "f64": np.float64}[dtype]).astype(np.float64)
+    f = np.argmax if op.startswith("max") else np.argmin
+    want = (v.shape[1] - 1 - f(v[:, ::-1, :], axis=1)) if op.endswith("_last") else f(v, axis=1)
+    assert np.array_equal(o.argreduce_axis(exact_storage(v, dtype), dtype, op), want), "axis vs numpy"
+
+
 def pin_rejects_empty_rows(o) -> None:
     try:
         o.argreduce_lastaxis(np.zeros((3, 0), dtype=np.float32), "f32", "max")
@@ -216,4 +245,5 @@ def all_pins(o, fast: bool = False):
                          lambda d=dtype, p=op: pin_brute_force(o, d, p, max_len)))
             pins.append((f"numpy_{dtype}_{op}",
                          lambda d=dtype, p=op: pin_numpy_first_occurrence(o, d, p)))
+            pins.append((f"axis_{dtype}_{op}", lambda d=dtype, p=op: pin_axis(o, d, p)))
     return pins

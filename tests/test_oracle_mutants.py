@@ -36,6 +36,8 @@ MUTANTS = [
     ("f64_read_as_f32_stride", "(const char *)x + k * 8, 8);", "(const char *)x + k * 4, 8);"),
     ("last_column_skipped", "for (int64_t j = 1; j < cols; ++j)", "for (int64_t j = 1; j < cols - 1; ++j)"),
     ("empty_rows_accepted", "cols < 1 ||", "cols < 0 ||"),
+    ("axis_stride_wrong", "element(x, dtype, base + r * inner)", "element(x, dtype, base + r * len)"),
+    ("axis_output_transposed", "out[o * inner + i] = idx;", "out[i * outer + o] = idx;"),
 ]
 
 

@@ -39,6 +39,12 @@ def test_numpy_first_occurrence_on_nan_free_rows(oracle_lib, dtype, op):
     P.pin_numpy_first_occurrence(oracle_lib, dtype, op)
 
 
+@pytest.mark.parametrize("dtype", P.DTYPES)
+@pytest.mark.parametrize("op", P.OPS)
+def test_middle_axis_against_closed_form(oracle_lib, dtype, op):
+    P.pin_axis(oracle_lib, dtype, op)
+
+
 def test_rejects_empty_rows(oracle_lib):
     P.pin_rejects_empty_rows(oracle_lib)
 
