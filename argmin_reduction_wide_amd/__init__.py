@@ -8,6 +8,9 @@ from .binding import (  # noqa: F401
     ArgreduceError,
     argmax,
     argmin,
+    argreduce_axis,
+    argreduce_axis_plan,
+    argreduce_axis_scratch_bytes,
     argreduce_debug_force_path,
     argreduce_debug_set_capacity,
     argreduce_lastaxis,

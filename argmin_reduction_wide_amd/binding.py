@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libargreduce.so")
 # enums of include/argreduce.h
 F32, F16, BF16, F64 = 0, 1, 2, 3
 MAX, MIN, MAX_LAST, MIN_LAST = 0, 1, 2, 3
-PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT = -1, 0, 1, 2
+PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS = -1, 0, 1, 2, 3
 OK = 0
 ERRORS = {
     -1: "ARGREDUCE_ERR_INVALID_ARG",
@@ -35,7 +35,8 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 # Exported names of include/argreduce.h (checked by the CPU test suite).
 EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_debug_set_capacity", "argreduce_debug_force_path",
-           "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events")
+           "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events",
+           "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan")
 
 
 class ArgreduceError(RuntimeError):
@@ -48,11 +49,12 @@ class argreduce_plan_t(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
                 ("blocks_per_row", ctypes.c_int32), ("block_threads", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int64), ("grid_rows", ctypes.c_int64),
-                ("unroll", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("device_threads", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t)]
+                ("unroll", ctypes.c_int32), ("outputs_per_block", ctypes.c_int32),
+                ("device_threads", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t),
+                ("load_bytes", ctypes.c_int32), ("dispatches", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib = None
@@ -88,6 +90,13 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_debug_set_capacity.restype = c_int
                 h.argreduce_debug_force_path.argtypes = [c_int]
                 h.argreduce_debug_force_path.restype = c_int
+                h.argreduce_axis_scratch_bytes.argtypes = [i64, i64, i64, c_int]
+                h.argreduce_axis_scratch_bytes.restype = sz
+                h.argreduce_axis.argtypes = [vp, c_int, i64, i64, i64, c_int, vp, vp, sz, vp]
+                h.argreduce_axis.restype = c_int
+                h.argreduce_axis_plan.argtypes = [i64, i64, i64, c_int,
+                                                  ctypes.POINTER(argreduce_plan_t)]
+                h.argreduce_axis_plan.restype = c_int
                 h.argreduce_debug_launch_empty.argtypes = [vp]
                 h.argreduce_debug_launch_empty.restype = c_int
                 h.argreduce_debug_set_kernel_events.argtypes = [vp, vp]
@@ -128,6 +137,24 @@ def argreduce_plan(rows: int, cols: int, dtype) -> dict:
     return p.as_dict()
 
 
+def argreduce_axis_scratch_bytes(outer: int, length: int, inner: int, dtype) -> int:
+    return lib().argreduce_axis_scratch_bytes(outer, length, inner, _dtype_code(dtype))
+
+
+def argreduce_axis(x_ptr: int, dtype, outer: int, length: int, inner: int, op, out_ptr: int,
+                   scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
+    return lib().argreduce_axis(x_ptr, _dtype_code(dtype), outer, length, inner, _op_code(op),
+                                out_ptr, scratch_ptr, scratch_bytes, stream)
+
+
+def argreduce_axis_plan(outer: int, length: int, inner: int, dtype) -> dict:
+    p = argreduce_plan_t()
+    rc = lib().argreduce_axis_plan(outer, length, inner, _dtype_code(dtype), ctypes.byref(p))
+    if rc != OK:
+        raise ArgreduceError(rc, "argreduce_axis_plan")
+    return p.as_dict()
+
+
 def argreduce_debug_set_capacity(threads: int) -> int:
     return lib().argreduce_debug_set_capacity(threads)
 
@@ -163,7 +190,9 @@ def _torch_dtype_code(t) -> int:
         raise ArgreduceError(-2, f"argreduce on {t.dtype}") from None
 
 
-def _reduce(t, op: int, out=None, scratch=None):
+def _reduce(t, op: int, out=None, scratch=None, dim: int = -1):
+    import math
+
     import torch
 
     if not t.is_cuda:
@@ -171,34 +200,36 @@ def _reduce(t, op: int, out=None, scratch=None):
     if t.dim() == 0:
         raise ValueError("argreduce needs at least one dimension")
     if not t.is_contiguous():
-        raise ValueError("argreduce needs a contiguous tensor (last axis reduced)")
+        raise ValueError("argreduce needs a contiguous tensor")
+    dim = dim % t.dim()
     dtype = _torch_dtype_code(t)
-    cols = t.shape[-1]
-    rows = t.numel() // cols if cols > 0 else 0
+    outer = math.prod(t.shape[:dim])
+    length = t.shape[dim]
+    inner = math.prod(t.shape[dim + 1:])
     if out is None:
-        out = torch.empty(t.shape[:-1], dtype=torch.int64, device=t.device)
-    need = argreduce_scratch_bytes(rows, cols, dtype)
+        out = torch.empty(t.shape[:dim] + t.shape[dim + 1:], dtype=torch.int64, device=t.device)
+    need = argreduce_axis_scratch_bytes(outer, length, inner, dtype)
     if need == SIZE_MAX:
-        raise ArgreduceError(-1, f"argreduce_scratch_bytes(rows={rows}, cols={cols})")
+        raise ArgreduceError(-1, f"argreduce_axis_scratch_bytes({outer}, {length}, {inner})")
     if need and (scratch is None or scratch.numel() * scratch.element_size() < need):
         scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
     sptr = scratch.data_ptr() if (need and scratch is not None) else 0
     sbytes = scratch.numel() * scratch.element_size() if (need and scratch is not None) else 0
     stream = torch.cuda.current_stream(t.device).cuda_stream
-    rc = argreduce_lastaxis(t.data_ptr(), dtype, rows, cols, op, out.data_ptr(), sptr, sbytes,
-                            stream)
+    rc = argreduce_axis(t.data_ptr(), dtype, outer, length, inner, op, out.data_ptr(), sptr,
+                        sbytes, stream)
     if rc != OK:
-        raise ArgreduceError(rc, f"argreduce_lastaxis(rows={rows}, cols={cols})")
+        raise ArgreduceError(rc, f"argreduce_axis(outer={outer}, len={length}, inner={inner})")
     return out
 
 
-def argmax(t, out=None, scratch=None, select_last_index: bool = False):
-    """Index of the maximum along the last axis (first occurrence, or the last with
+def argmax(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False):
+    """Index of the maximum along `dim` (first occurrence, or the last with
     select_last_index; NaN is never selected, a leading NaN gives 0)."""
-    return _reduce(t, MAX_LAST if select_last_index else MAX, out, scratch)
+    return _reduce(t, MAX_LAST if select_last_index else MAX, out, scratch, dim)
 
 
-def argmin(t, out=None, scratch=None, select_last_index: bool = False):
-    """Index of the minimum along the last axis (first occurrence, or the last with
+def argmin(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False):
+    """Index of the minimum along `dim` (first occurrence, or the last with
     select_last_index; NaN is never selected, a leading NaN gives 0)."""
-    return _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch)
+    return _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch, dim)

@@ -26,6 +26,8 @@ constexpr int64_t kBlock = 256;
 // Rows of up to this many 16-byte vectors (4 KiB) are scanned by one wavefront; rows of up
 // to kBlockRowMaxVec (32 KiB) by one workgroup with all of a lane's loads in one step.
 constexpr int64_t kWaveRowMaxVec = 256;
+// Middle axis: at most one wavefront of lanes along `inner` per tile.
+constexpr int64_t kAxisMaxLanes = 64;
 constexpr int64_t kBlockRowMaxVec = 2048;
 // A split row gives each lane about this many 16-byte vectors (all in flight at once).
 constexpr int64_t kSplitVecPerLane = 2;
@@ -184,9 +186,87 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     return ARGREDUCE_OK;
 }
 
+int check_axis_shape(int64_t outer, int64_t len, int64_t inner, int dtype) {
+    if (elem_size(dtype) == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
+    if (outer < 0 || len < 1 || inner < 1) return ARGREDUCE_ERR_INVALID_ARG;
+    if (len > std::numeric_limits<int32_t>::max()) return ARGREDUCE_ERR_TOO_WIDE;
+    const int64_t lim = std::numeric_limits<int64_t>::max() / elem_size(dtype);
+    if (inner > lim / len || (outer > 0 && outer > lim / (len * inner)))
+        return ARGREDUCE_ERR_INVALID_ARG;
+    return ARGREDUCE_OK;
+}
+
+// Plan of a middle-axis reduction with inner > 1.
+int make_axis_plan(int64_t outer, int64_t len, int64_t inner, int dtype, uintptr_t x_addr,
+                   AxisPlan* p) {
+    int rc = check_axis_shape(outer, len, inner, dtype);
+    if (rc != ARGREDUCE_OK) return rc;
+    int64_t cap = 0;
+    rc = device_threads(&cap);
+    if (rc != ARGREDUCE_OK) return rc;
+    const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
+    const int64_t esize = elem_size(dtype);
+    const int64_t vw = 16 / esize;
+    *p = AxisPlan{};
+    p->outer = outer;
+    p->len = len;
+    p->inner = inner;
+    // 16-byte vectors when every (o, r) row of the tensor starts 16-byte aligned
+    p->vec = (inner % vw == 0 && x_addr % 16 == 0) ? 1 : 0;
+    // lanes along `inner`: the next power of two of the vectors (or elements) per row, <= 64
+    const int64_t units = p->vec ? inner / vw : inner;
+    const int64_t lanes = units < kAxisMaxLanes ? next_pow2(units) : kAxisMaxLanes;
+    p->lanes = static_cast<int>(lanes);
+    const int64_t tile = p->vec ? lanes * vw : lanes;
+    const int64_t rows_per_tile = kBlock / lanes;  // thread rows along the axis (TR)
+    p->tile = static_cast<int>(tile);
+    p->tiles_per_o = ceil_div(inner, tile);
+    p->tiles = outer * p->tiles_per_o;
+    const int64_t tiles1 = p->tiles > 0 ? p->tiles : 1;
+    p->unroll = (p->vec && vw == 2) ? 4 : 8;
+    // Split the axis over workgroups while the tiles leave the device's resident workgroups
+    // unfilled, but not beyond one step (unroll positions) per thread.
+    const int64_t fill = cap_blocks / tiles1;
+    const int64_t want = ceil_div(len, rows_per_tile * p->unroll);
+    int64_t b = fill < want ? fill : want;
+    b = b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
+    b = b > 1 ? b : 1;
+    const int forced = g_force_path.load(std::memory_order_relaxed);
+    if (forced == ARGREDUCE_PATH_SPLIT) b = b > 2 ? b : 2;
+    if (forced == ARGREDUCE_PATH_BLOCK) b = 1;
+    p->blocks_per_tile = static_cast<int>(b);
+    const int64_t max_grid = cap_blocks * kOversubscribe;
+    int64_t grid_tiles = max_grid / b;
+    grid_tiles = grid_tiles > 0 ? grid_tiles : 1;
+    grid_tiles = tiles1 < grid_tiles ? tiles1 : grid_tiles;
+    p->grid_tiles = grid_tiles;
+    p->grid_blocks = grid_tiles * b;
+    p->device_threads = cap;
+    p->scratch_bytes = b > 1 ? 15 + static_cast<size_t>(tiles1) * static_cast<size_t>(b) *
+                                        static_cast<size_t>(tile) * axis_partial_bytes(dtype)
+                             : 0;
+    return ARGREDUCE_OK;
+}
+
+void fill_plan(const Plan& p, argreduce_plan_t* out) {
+    out->path = p.path;
+    out->lanes_per_row = p.lanes_per_row;
+    out->blocks_per_row = p.blocks_per_row;
+    out->block_threads = p.block_threads;
+    out->grid_blocks = p.grid_blocks;
+    out->grid_rows = p.grid_rows;
+    out->unroll = p.unroll;
+    out->outputs_per_block = p.path == ARGREDUCE_PATH_SUBWAVE ? p.block_threads / p.lanes_per_row : 1;
+    out->device_threads = p.device_threads;
+    out->scratch_bytes = p.scratch_bytes;
+    out->load_bytes = 16;
+    out->dispatches = 1;
+}
+
 }  // namespace
 }  // namespace argreduce
 
+using argreduce::AxisPlan;
 using argreduce::Plan;
 
 ARGREDUCE_EXPORT size_t argreduce_scratch_bytes(int64_t rows, int64_t cols,
@@ -203,16 +283,7 @@ ARGREDUCE_EXPORT int argreduce_plan(int64_t rows, int64_t cols, argreduce_dtype_
     Plan p;
     const int rc = argreduce::make_plan(rows, cols, dtype, &p);
     if (rc != ARGREDUCE_OK) return rc;
-    out->path = p.path;
-    out->lanes_per_row = p.lanes_per_row;
-    out->blocks_per_row = p.blocks_per_row;
-    out->block_threads = p.block_threads;
-    out->grid_blocks = p.grid_blocks;
-    out->grid_rows = p.grid_rows;
-    out->unroll = p.unroll;
-    out->reserved = 0;
-    out->device_threads = p.device_threads;
-    out->scratch_bytes = p.scratch_bytes;
+    argreduce::fill_plan(p, out);
     return ARGREDUCE_OK;
 }
 
@@ -265,4 +336,70 @@ ARGREDUCE_EXPORT int argreduce_debug_launch_empty(void* stream) {
 ARGREDUCE_EXPORT int argreduce_debug_set_kernel_events(void* start, void* stop) {
     argreduce::set_kernel_events(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
     return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT size_t argreduce_axis_scratch_bytes(int64_t outer, int64_t len, int64_t inner,
+                                                     argreduce_dtype_t dtype) {
+    if (inner == 1) return argreduce_scratch_bytes(outer, len, dtype);
+    // The plan (and scratch) differ between 16-byte aligned tensors and others; size for
+    // the larger of the two.
+    AxisPlan p, q;
+    if (argreduce::make_axis_plan(outer, len, inner, dtype, 0, &p) != ARGREDUCE_OK ||
+        argreduce::make_axis_plan(outer, len, inner, dtype, 1, &q) != ARGREDUCE_OK)
+        return std::numeric_limits<size_t>::max();
+    return p.scratch_bytes > q.scratch_bytes ? p.scratch_bytes : q.scratch_bytes;
+}
+
+ARGREDUCE_EXPORT int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inner,
+                                         argreduce_dtype_t dtype, argreduce_plan_t* out) {
+    if (out == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    if (inner == 1) return argreduce_plan(outer, len, dtype, out);
+    AxisPlan p;
+    const int rc = argreduce::make_axis_plan(outer, len, inner, dtype, 0, &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    out->path = ARGREDUCE_PATH_AXIS;
+    out->lanes_per_row = static_cast<int32_t>(p.blocks_per_tile * (argreduce::kBlock / p.lanes));
+    out->blocks_per_row = p.blocks_per_tile;
+    out->block_threads = static_cast<int32_t>(argreduce::kBlock);
+    out->grid_blocks = p.grid_blocks;
+    out->grid_rows = p.grid_tiles;
+    out->unroll = p.unroll;
+    out->outputs_per_block = p.tile;
+    out->device_threads = p.device_threads;
+    out->scratch_bytes = p.scratch_bytes;
+    out->load_bytes = p.vec ? 16 : static_cast<int32_t>(argreduce::elem_size(dtype));
+    out->dispatches = p.blocks_per_tile > 1 ? 2 : 1;
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_axis(const void* x, argreduce_dtype_t dtype, int64_t outer,
+                                    int64_t len, int64_t inner, argreduce_op_t op,
+                                    int64_t* out_idx, void* scratch, size_t scratch_bytes,
+                                    void* stream) {
+    if (inner == 1)
+        return argreduce_lastaxis(x, dtype, outer, len, op, out_idx, scratch, scratch_bytes,
+                                  stream);
+    int rc = argreduce::check_axis_shape(outer, len, inner, dtype);
+    if (rc != ARGREDUCE_OK) return rc;
+    if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN && op != ARGREDUCE_MAX_LAST &&
+        op != ARGREDUCE_MIN_LAST)
+        return ARGREDUCE_ERR_INVALID_ARG;
+    if (outer == 0) return ARGREDUCE_OK;
+    if (x == nullptr || out_idx == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(x) % argreduce::elem_size(dtype) != 0 ||
+        reinterpret_cast<uintptr_t>(out_idx) % 8 != 0)
+        return ARGREDUCE_ERR_INVALID_ARG;
+    AxisPlan p;
+    rc = argreduce::make_axis_plan(outer, len, inner, dtype, reinterpret_cast<uintptr_t>(x), &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    uint8_t* scratch16 = nullptr;
+    if (p.scratch_bytes > 0) {
+        if (scratch == nullptr || scratch_bytes < p.scratch_bytes)
+            return ARGREDUCE_ERR_SCRATCH_TOO_SMALL;
+        scratch16 = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(scratch) + 15u) &
+                                               ~static_cast<uintptr_t>(15u));
+    }
+    const hipError_t err = argreduce::launch_axis(p, x, dtype, op, out_idx, scratch16,
+                                                  static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ARGREDUCE_OK : ARGREDUCE_ERR_HIP;
 }

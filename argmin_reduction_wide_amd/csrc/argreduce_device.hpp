@@ -284,21 +284,28 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
                                  Cand<typename Fmt::C, OP> (&s)[Fmt::VW]) {
     using C = typename Fmt::C;
     using Vec = typename Fmt::Vec;
-    Vec q[U];
+    // In the last, partial step (kGuard) a lane past the end re-reads the last vector
+    // instead of skipping its load: a load under a lane condition becomes a branch, and the
+    // loads of a step then wait on each other. Visiting a real element again, with its own
+    // position and after every smaller position of the lane, changes no result.
+    uint32_t dd[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;
-        if (!kGuard || d < rem)
-            q[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const Vec*>(body + static_cast<size_t>(base + d) * 16u));
+        dd[u] = (!kGuard || d < rem) ? d : rem - 1;
     }
+    Vec q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        q[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const Vec*>(body + static_cast<size_t>(base + dd[u]) * 16u));
     // Issue every load of the step before any arithmetic: the scheduler would otherwise
     // interleave (and, under register pressure, wait on) loads one by one.
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t d = lane + static_cast<uint32_t>(u) * team;
-        if (!kGuard || d < rem) {
+        const uint32_t d = dd[u];
+        {
             C e[Fmt::VW];
             Fmt::unpack(q[u], e);
             const uint32_t pos = head + (base + d) * Fmt::VW;

@@ -23,6 +23,26 @@ struct Plan {
     size_t entry_bytes;      // split path: bytes per published (nonce, index) slot
 };
 
+// Launch plan of a reduction over the middle axis of [outer, len, inner], inner > 1.
+struct AxisPlan {
+    int64_t outer, len, inner;
+    int vec;                 // 1: each lane owns VW outputs loaded as one 16-byte vector
+    int lanes;               // lanes along `inner` per workgroup (TL)
+    int tile;                // outputs per workgroup tile (TL, times VW with vec)
+    int64_t tiles_per_o;     // tiles per outer index
+    int64_t tiles;           // outer * tiles_per_o
+    int blocks_per_tile;     // B (> 1: partials, merged by a second dispatch)
+    int64_t grid_blocks;
+    int64_t grid_tiles;      // tiles in flight at once (further tiles are looped over)
+    int unroll;              // loads in flight per thread along the axis
+    int64_t device_threads;
+    size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
+};
+
+// Enqueues the middle-axis kernel of `plan` on `stream`.
+hipError_t launch_axis(const AxisPlan& plan, const void* x, int dtype, int op, int64_t* out,
+                       uint8_t* scratch16, hipStream_t stream);
+
 // Enqueues the kernels of `plan` on `stream`. `scratch16` is the caller's scratch aligned
 // up to 16 bytes (or null when plan.scratch_bytes == 0). Returns a hipError_t.
 hipError_t launch(const Plan& plan, const void* x, int dtype, int op, int64_t rows, int64_t cols,
@@ -33,6 +53,9 @@ hipError_t launch_empty(hipStream_t stream);
 
 // Events recorded around the row-scanning kernel of every launch when both are set.
 void set_kernel_events(hipEvent_t start, hipEvent_t stop);
+
+// Bytes of one (value, index) partial of a two-dispatch middle-axis reduction.
+size_t axis_partial_bytes(int dtype);
 
 // Bytes of one published slot of the split path.
 size_t partial_entry_bytes(int dtype);

@@ -11,6 +11,10 @@
 //              xor-shuffle tree within the group).
 //   k_blocks   B workgroups of 256 threads per row; B == 1 is a workgroup per row.
 //
+// and, for a reduction over a middle axis, k_axis (a tile of outputs per workgroup, the
+// axis split over B workgroups when tiles are few) with k_axis_merge as its second
+// dispatch when B > 1.
+//
 // Merging a row split over B > 1 workgroups. The page merges partials through a small
 // global buffer reduced by the last block to arrive, ordered as partial write, device-wide
 // fence, per-row atomic completion counter that the caller's memset clears every call.
@@ -35,6 +39,7 @@
 #include <hip/hip_ext.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "argreduce_device.hpp"
 #include "argreduce_internal.hpp"
@@ -177,6 +182,226 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
     }
 }
 
+
+// Tree merge of the TR = 256 / TL thread rows of a workgroup (TL lanes each, EPL candidates
+// per lane) through LDS: the result lands in thread row 0. Ends with a barrier, so the
+// arrays may be rewritten right after.
+template <int TL, int EPL, typename Cand, typename C>
+__device__ void merge_rows(Cand (&c)[EPL], C (*s_v)[kBlockThreads], uint32_t (*s_i)[kBlockThreads]) {
+    constexpr int TR = kBlockThreads / TL;
+    const uint32_t tl = threadIdx.x % TL;
+    const uint32_t tr = threadIdx.x / TL;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+        s_v[k][threadIdx.x] = c[k].v;
+        s_i[k][threadIdx.x] = c[k].i;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = TR / 2; h > 0; h >>= 1) {
+        // rows [0, h) take rows [h, 2h): no row is read and written in the same round
+        if (tr < static_cast<uint32_t>(h)) {
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                c[k].merge(s_v[k][(tr + h) * TL + tl], s_i[k][(tr + h) * TL + tl]);
+                s_v[k][threadIdx.x] = c[k].v;
+                s_i[k][threadIdx.x] = c[k].i;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Workgroup id with the 8 XCDs in mind: workgroups are handed to the XCDs round-robin
+// (XCD = blockIdx % 8); this maps the ones XCD k receives onto one contiguous range of ids,
+// so that each XCD streams its own contiguous part of the tensor.
+__device__ inline uint32_t xcd_contiguous_id() {
+    const uint32_t g = gridDim.x, q = g / 8, r = g % 8, k = blockIdx.x % 8;
+    return k * q + (k < r ? k : r) + blockIdx.x / 8;
+}
+
+template <typename C>
+struct Partial {
+    C v;
+    uint32_t i;
+};
+
+// Reduction over the middle axis of a contiguous [outer, len, inner] tensor (inner > 1),
+// laid out like the column kernel of AcceleratedKernels.jl's pull request on reductions of
+// wide matrices along dims (Wide matrices: a column kernel): a workgroup takes a tile of
+// consecutive outputs of one outer index, TL lanes along `inner`, so that every load of a
+// wavefront reads consecutive memory. With VEC each lane owns VW consecutive outputs and
+// loads them as one 16-byte vector (inner * sizeof(T) a multiple of 16, x 16-byte aligned);
+// otherwise one output and one element. The TR = 256 / TL thread rows split the reduced axis
+// (thread row tr takes positions tr, tr + TR, ..., U loads in flight) and tree-merge in LDS.
+//
+// With B > 1 the axis is also split over B workgroups per tile (few outputs, long axis):
+// each stores a plain (value, index) partial per output and k_axis_merge, the second
+// dispatch, merges them; the kernel boundary orders the two, so nothing waits.
+template <typename Fmt, int OP, int TL, bool VEC, int U>
+__global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restrict__ x,
+                                                        uint32_t len, int64_t inner,
+                                                        int64_t tiles_per_o, int64_t tiles,
+                                                        uint32_t B, int64_t grid_tiles,
+                                                        int64_t* __restrict__ out,
+                                                        Partial<typename Fmt::C>* __restrict__ part) {
+    using C = typename Fmt::C;
+    using L = typename std::conditional<VEC, typename Fmt::Vec, C>::type;
+    constexpr int TR = kBlockThreads / TL;
+    constexpr int EPL = VEC ? Fmt::VW : 1;  // outputs per lane
+    constexpr int TO = TL * EPL;            // outputs per tile
+    __shared__ C s_v[EPL][kBlockThreads];
+    __shared__ uint32_t s_i[EPL][kBlockThreads];
+    const uint32_t tl = threadIdx.x % TL;
+    const uint32_t tr = threadIdx.x / TL;
+    const uint32_t id = xcd_contiguous_id();
+    const uint32_t b = id % B;
+    const int64_t slot = id / B;
+    const uint32_t rteam = B * TR;  // thread rows sharing one tile
+    const uint32_t rlane = b * TR + tr;
+    const uint32_t step = rteam * U;
+    const size_t rstride = static_cast<size_t>(inner) * Fmt::kSize;
+    for (int64_t t = slot; t < tiles; t += grid_tiles) {
+        const int64_t o = t / tiles_per_o;
+        const int64_t i0 = (t - o * tiles_per_o) * TO + static_cast<int64_t>(tl) * EPL;
+        const bool active = i0 < inner;  // with VEC all EPL outputs of a lane exist together
+        Cand<C, OP> c[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) c[k].init();
+        if (active) {
+            const uint8_t* col =
+                x + (static_cast<size_t>(o) * len * static_cast<size_t>(inner) + i0) * Fmt::kSize;
+            // One step: U loads per lane (positions base + rlane + u * rteam), issued back to
+            // back, then the compares. No load sits under a lane condition (that would make
+            // it a branch, and the loads of the step would wait on each other): in the last,
+            // partial step a lane past the end re-reads the last position, and visiting a
+            // real element again, with its own position and after every smaller position of
+            // the lane, changes no result.
+            auto scan = [&](uint32_t base, auto guard) {
+                constexpr bool kGuard = decltype(guard)::value;
+                const uint32_t rem = len - base;
+                uint32_t dd[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t d = rlane + static_cast<uint32_t>(u) * rteam;
+                    dd[u] = (!kGuard || d < rem) ? d : rem - 1;
+                }
+                L q[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint8_t* a = col + static_cast<size_t>(base + dd[u]) * rstride;
+                    if constexpr (VEC)
+                        q[u] = __builtin_nontemporal_load(reinterpret_cast<const L*>(a));
+                    else
+                        q[u] = Fmt::load1(a);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if constexpr (VEC) {
+                        C e[Fmt::VW];
+                        Fmt::unpack(q[u], e);
+#pragma unroll
+                        for (int k = 0; k < EPL; ++k) c[k].update(e[k], base + dd[u]);
+                    } else {
+                        c[0].update(q[u], base + dd[u]);
+                    }
+                }
+            };
+            // Position 0 enters as its own candidate (fix(x0), 0), merged into the scan's
+            // result at the end: the merge is commutative, so this equals taking it first.
+            // The scan's plain visit of position 0 is then harmless (a NaN moves nothing;
+            // any other value makes the same candidate). Its load is issued here and only
+            // waited for after the scan.
+            L seed;
+            if (rlane == 0) {
+                if constexpr (VEC)
+                    seed = *reinterpret_cast<const L*>(col);
+                else
+                    seed = Fmt::load1(col);
+            }
+            // step <= 1024 * 256 * 8, so base + step cannot wrap below len <= INT32_MAX
+            const uint32_t full = len - len % step;
+            for (uint32_t base = 0; base < full; base += step) scan(base, std::false_type{});
+            if (full < len) scan(full, std::true_type{});
+            if (rlane == 0) {
+                C e[EPL];
+                if constexpr (VEC) {
+                    Fmt::unpack(seed, e);
+                } else {
+                    e[0] = seed;
+                }
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) {
+                    Cand<C, OP> f;
+                    f.take_first(e[k]);
+                    c[k].merge(f.v, f.i);
+                }
+            }
+        }
+        merge_rows<TL>(c, s_v, s_i);  // the tile's candidates, in thread row 0
+        if (tr == 0 && active) {
+            if (B == 1) {
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) out[o * inner + i0 + k] = Cand<C, OP>::result(c[k].i);
+            } else {
+                // part[(t * B + b) * TO + output]: one workgroup's partials are contiguous
+                Partial<C>* pp = part + (static_cast<size_t>(t) * B + b) * TO + tl * EPL;
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) {
+                    pp[k].v = c[k].v;
+                    pp[k].i = c[k].i;
+                }
+            }
+        }
+    }
+}
+
+// Second dispatch of a split middle-axis reduction. Workgroup g takes ML consecutive
+// outputs of one tile (g = tile * groups + group): lane ml owns an output, the 256 / ML
+// thread rows share out its B partials (coalesced: the partials of one first-dispatch
+// workgroup are contiguous), then the thread rows tree-merge through LDS.
+template <typename Fmt, int OP, int ML>
+__global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
+    const Partial<typename Fmt::C>* __restrict__ part, uint32_t B, int64_t inner,
+    int64_t tiles_per_o, int to, int64_t tiles, int64_t* __restrict__ out) {
+    using C = typename Fmt::C;
+    constexpr int MR = kBlockThreads / ML;
+    constexpr int kBatch = 8;
+    __shared__ C s_v[1][kBlockThreads];
+    __shared__ uint32_t s_i[1][kBlockThreads];
+    const uint32_t ml = threadIdx.x % ML;
+    const uint32_t mr = threadIdx.x / ML;
+    const int64_t groups = (to + ML - 1) / ML;
+    for (int64_t g = blockIdx.x; g < tiles * groups; g += gridDim.x) {
+        const int64_t t = g / groups;
+        const int64_t j = (g - t * groups) * ML + ml;  // output within the tile
+        const int64_t o = t / tiles_per_o;
+        const int64_t i = (t - o * tiles_per_o) * to + j;
+        const bool active = j < to && i < inner;
+        Cand<C, OP> m[1];
+        m[0].init();
+        if (active) {
+            const Partial<C>* col = part + static_cast<size_t>(t) * B * to + j;
+            uint32_t b = mr;
+            // batches of kBatch independent loads, then the remainder one by one
+            for (; b + (kBatch - 1) * MR < B; b += kBatch * MR) {
+                Partial<C> e[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) e[u] = col[static_cast<size_t>(b + u * MR) * to];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) m[0].merge(e[u].v, e[u].i);
+            }
+            for (; b < B; b += MR) {
+                const Partial<C> e = col[static_cast<size_t>(b) * to];
+                m[0].merge(e.v, e.i);
+            }
+        }
+        merge_rows<ML>(m, s_v, s_i);
+        if (mr == 0 && active) out[o * inner + i] = Cand<C, OP>::result(m[0].i);
+    }
+}
+
 __global__ void k_empty() {}
 
 namespace {
@@ -256,6 +481,72 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
     return hipGetLastError();
 }
 
+template <typename Fmt, int OP, int TL, bool VEC, int U>
+void launch_axis_tl(const AxisPlan& p, const uint8_t* x, int64_t* out, uint8_t* scratch16,
+                    hipStream_t s) {
+    using P = Partial<typename Fmt::C>;
+    P* part = reinterpret_cast<P*>(scratch16);
+    const uint32_t B = static_cast<uint32_t>(p.blocks_per_tile);
+    launch_scan(k_axis<Fmt, OP, TL, VEC, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
+                static_cast<uint32_t>(p.len), p.inner, p.tiles_per_o, p.tiles, B, p.grid_tiles,
+                out, B > 1 ? part : nullptr);
+    if (B == 1) return;
+    // lanes per output group: fewer (more thread rows) as B grows, so that every thread
+    // loads at most 8 partials
+    const int ml = B <= 32 ? 64 : (B <= 256 ? 8 : 1);
+    const int64_t groups = (p.tile + ml - 1) / ml;
+    const int64_t work = p.tiles * groups;
+    const dim3 grid(static_cast<uint32_t>(work < (int64_t{1} << 20) ? work : (int64_t{1} << 20)));
+    const P* cpart = part;
+    if (ml == 64)
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 64>), grid, dim3(kBlockThreads), 0, s, cpart, B,
+                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+    else if (ml == 8)
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 8>), grid, dim3(kBlockThreads), 0, s, cpart, B,
+                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+    else
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 1>), grid, dim3(kBlockThreads), 0, s, cpart, B,
+                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+}
+
+template <typename Fmt, int OP>
+hipError_t launch_axis_fmt(const AxisPlan& p, const void* xv, int64_t* out, uint8_t* scratch16,
+                           hipStream_t s) {
+    const uint8_t* x = static_cast<const uint8_t*>(xv);
+    // 16-byte loads: U = 8 (4 for 8-byte elements, whose vectors need twice the registers
+    // per output); element loads: U = 8. Element loads have inner >= 2, so at least 2 lanes.
+    constexpr int UV = Fmt::VW == 2 ? 4 : 8;
+    switch (p.vec * 1000 + p.lanes) {
+        case 2: launch_axis_tl<Fmt, OP, 2, false, 8>(p, x, out, scratch16, s); break;
+        case 4: launch_axis_tl<Fmt, OP, 4, false, 8>(p, x, out, scratch16, s); break;
+        case 8: launch_axis_tl<Fmt, OP, 8, false, 8>(p, x, out, scratch16, s); break;
+        case 16: launch_axis_tl<Fmt, OP, 16, false, 8>(p, x, out, scratch16, s); break;
+        case 32: launch_axis_tl<Fmt, OP, 32, false, 8>(p, x, out, scratch16, s); break;
+        case 64: launch_axis_tl<Fmt, OP, 64, false, 8>(p, x, out, scratch16, s); break;
+        case 1001: launch_axis_tl<Fmt, OP, 1, true, UV>(p, x, out, scratch16, s); break;
+        case 1002: launch_axis_tl<Fmt, OP, 2, true, UV>(p, x, out, scratch16, s); break;
+        case 1004: launch_axis_tl<Fmt, OP, 4, true, UV>(p, x, out, scratch16, s); break;
+        case 1008: launch_axis_tl<Fmt, OP, 8, true, UV>(p, x, out, scratch16, s); break;
+        case 1016: launch_axis_tl<Fmt, OP, 16, true, UV>(p, x, out, scratch16, s); break;
+        case 1032: launch_axis_tl<Fmt, OP, 32, true, UV>(p, x, out, scratch16, s); break;
+        case 1064: launch_axis_tl<Fmt, OP, 64, true, UV>(p, x, out, scratch16, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename Fmt>
+hipError_t launch_axis_op(const AxisPlan& p, const void* x, int op, int64_t* out,
+                          uint8_t* scratch16, hipStream_t s) {
+    switch (op) {
+        case ARGREDUCE_MAX: return launch_axis_fmt<Fmt, kMax>(p, x, out, scratch16, s);
+        case ARGREDUCE_MIN: return launch_axis_fmt<Fmt, kMin>(p, x, out, scratch16, s);
+        case ARGREDUCE_MAX_LAST: return launch_axis_fmt<Fmt, kMaxLast>(p, x, out, scratch16, s);
+        case ARGREDUCE_MIN_LAST: return launch_axis_fmt<Fmt, kMinLast>(p, x, out, scratch16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename Fmt>
 hipError_t launch_op(const Plan& p, const void* x, int op, int64_t rows, int64_t cols, int64_t* out,
                      uint8_t* scratch16, hipStream_t s) {
@@ -281,6 +572,17 @@ hipError_t launch(const Plan& p, const void* x, int dtype, int op, int64_t rows,
     }
 }
 
+hipError_t launch_axis(const AxisPlan& p, const void* x, int dtype, int op, int64_t* out,
+                       uint8_t* scratch16, hipStream_t s) {
+    switch (dtype) {
+        case ARGREDUCE_F32: return launch_axis_op<F32>(p, x, op, out, scratch16, s);
+        case ARGREDUCE_F16: return launch_axis_op<F16>(p, x, op, out, scratch16, s);
+        case ARGREDUCE_BF16: return launch_axis_op<BF16>(p, x, op, out, scratch16, s);
+        case ARGREDUCE_F64: return launch_axis_op<F64>(p, x, op, out, scratch16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_empty(hipStream_t s) {
     hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
     return hipGetLastError();
@@ -289,6 +591,10 @@ hipError_t launch_empty(hipStream_t s) {
 void set_kernel_events(hipEvent_t start, hipEvent_t stop) {
     g_ev_start.store(start, std::memory_order_relaxed);
     g_ev_stop.store(stop, std::memory_order_relaxed);
+}
+
+size_t axis_partial_bytes(int dtype) {
+    return dtype == ARGREDUCE_F64 ? sizeof(Partial<double>) : sizeof(Partial<float>);
 }
 
 size_t partial_entry_bytes(int dtype) {

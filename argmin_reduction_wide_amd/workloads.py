@@ -75,6 +75,9 @@ class Workload:
     seed: int
     recipe: str
     planted: dict = field(default_factory=dict)  # op -> {row: expected index}
+    # For a reduction over a middle axis: (outer, len, inner); data is then stored as
+    # (outer, len * inner) and the reduced axis is `len`.
+    axis_shape: tuple | None = None
 
     @property
     def rows(self) -> int:
@@ -219,6 +222,32 @@ def c5b_narrow_rows_f16(seed: int = 6, rows: int = 65536, cols: int = 64) -> Wor
     )
 
 
+def axis_many_outputs_f32(seed: int = 7, outer: int = 64, length: int = 4096,
+                          inner: int = 256) -> Workload:
+    """ArgMax f32 over the middle axis of [64, 4096, 256]: 16384 outputs, each over 4096
+    elements 1 KiB apart; N(0,1) quantised to 16 levels (frequent ties)."""
+    rng = np.random.default_rng(seed)
+    v = quantised_normal(rng, (outer, length * inner))
+    return Workload(
+        name=f"argmax_f32_axis1_{outer}x{length}x{inner}", dtype="f32", ops=("max",),
+        data=to_storage(v, "f32"), seed=seed, axis_shape=(outer, length, inner),
+        recipe="N(0,1) quantised to 16 levels, f32, reduced over the middle axis",
+    )
+
+
+def axis_few_outputs_f32(seed: int = 8, outer: int = 1, length: int = 1 << 20,
+                         inner: int = 32) -> Workload:
+    """ArgMax f32 over the middle axis of [1, 1048576, 32]: 32 outputs over a long axis
+    (a column reduction of a tall, narrow matrix); N(0,1) quantised to 16 levels."""
+    rng = np.random.default_rng(seed)
+    v = quantised_normal(rng, (outer, length * inner))
+    return Workload(
+        name=f"argmax_f32_axis1_{outer}x{length}x{inner}", dtype="f32", ops=("max",),
+        data=to_storage(v, "f32"), seed=seed, axis_shape=(outer, length, inner),
+        recipe="N(0,1) quantised to 16 levels, f32, reduced over the middle axis",
+    )
+
+
 def config_workloads(which: str) -> list[Workload]:
     """The workload(s) of one named configuration, at full size."""
     if which == "c1":
@@ -233,6 +262,8 @@ def config_workloads(which: str) -> list[Workload]:
         return [c5a_many_rows_f32()]
     if which == "c5b":
         return [c5b_narrow_rows_f16()]
+    if which == "axis":
+        return [axis_many_outputs_f32(), axis_few_outputs_f32()]
     raise KeyError(which)
 
 

@@ -77,21 +77,31 @@ class Case:
         for i in range(self.n_rot):
             self.x[i].copy_(one)
         self.ptrs = [self.x[i].data_ptr() for i in range(self.n_rot)]
-        self.out = torch.empty(self.rows, dtype=torch.int64, device="cuda")
-        self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
-        self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
         self.stream = torch.cuda.current_stream().cuda_stream
-        self.fn = B.lib().argreduce_lastaxis
         self.dt = B.DTYPE_NAMES[w.dtype]
         self.opc = B.OP_NAMES[op]
-        self.bytes = algorithmic_bytes(self.rows, self.cols, w.data.itemsize)
-        self.plan = B.argreduce_plan(self.rows, self.cols, w.dtype)
+        if w.axis_shape is None:
+            n_out = self.rows
+            self.shape = (self.rows, self.cols)
+            self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
+            self.fn = B.lib().argreduce_lastaxis
+            self.plan = B.argreduce_plan(self.rows, self.cols, w.dtype)
+        else:
+            outer, length, inner = w.axis_shape
+            n_out = outer * inner
+            self.shape = (outer, length, inner)
+            self.need = B.argreduce_axis_scratch_bytes(outer, length, inner, w.dtype)
+            self.fn = B.lib().argreduce_axis
+            self.plan = B.argreduce_axis_plan(outer, length, inner, w.dtype)
+        self.out = torch.empty(n_out, dtype=torch.int64, device="cuda")
+        self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
+        self.bytes = w.nbytes + n_out * 8  # input read once, one int64 per output
 
     def call(self, i: int) -> None:
-        rc = self.fn(self.ptrs[i % self.n_rot], self.dt, self.rows, self.cols, self.opc,
+        rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
                      self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
         if rc != 0:
-            raise RuntimeError(f"argreduce_lastaxis failed with status {rc}")
+            raise RuntimeError(f"argreduce call failed with status {rc}")
 
     def timed(self, steps: int, warmup: int, rotate: bool = True) -> float:
         """Microseconds per call over exactly `steps` calls."""
@@ -221,14 +231,16 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     kus = c.kernel_timed(min(steps, 1000))
     gus = c.graph_timed(min(steps, 200), max(1, steps // 200)) if graph else None
     rec = {
-        "workload": w.name, "op": op, "dtype": w.dtype, "rows": c.rows, "cols": c.cols,
+        "workload": w.name, "op": op, "dtype": w.dtype, "shape": list(c.shape),
         "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
         "graph_us_per_call": None if gus is None else round(gus, 3),
         "kernel_event_us": round(kus, 3),
         "gbps_per_call": round(c.bytes / (us * 1e-6) / 1e9, 1),
         "pct_hbm_peak_per_call": round(100 * c.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes": c.bytes, "rotated_copies": c.n_rot, "plan": c.plan,
-        "roofline": roofline(c.bytes, us, w.name if op == "max" else ""),
+        # per-launch duration of the scanning kernel itself (HIP events recorded around each
+        # launch on its stream), the figure rocprofv3's kernel trace reports as well
+        "roofline": roofline(c.bytes, kus, w.name if op == "max" else ""),
     }
     log(f"[bench]   {json.dumps(rec)}")
     rec["_case"] = c
@@ -322,7 +334,7 @@ def main() -> int:
 
     extra = []
     if args.all:
-        for name in W.CONFIG_NAMES:
+        for name in W.CONFIG_NAMES + ("axis",):
             for w in W.config_workloads(name):
                 for op in w.ops:
                     r = measure(w, op, max(200, args.steps // 4), args.warmup // 4 + 1, graph=False)

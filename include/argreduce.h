@@ -121,7 +121,9 @@ typedef enum {
     ARGREDUCE_PATH_AUTO = -1,
     ARGREDUCE_PATH_SUBWAVE = 0, /* a group of 1..64 lanes of one wavefront per row */
     ARGREDUCE_PATH_BLOCK = 1,   /* one workgroup per row, rows looped over the grid */
-    ARGREDUCE_PATH_SPLIT = 2    /* several workgroups per row; the last one to finish merges */
+    ARGREDUCE_PATH_SPLIT = 2,   /* several workgroups per row; the highest-id one merges */
+    ARGREDUCE_PATH_AXIS = 3     /* middle-axis reduction: a tile of consecutive outputs per
+                                   workgroup, thread rows along the axis (argreduce_axis) */
 } argreduce_path_t;
 
 typedef struct {
@@ -131,10 +133,15 @@ typedef struct {
     int32_t block_threads;    /* threads per workgroup */
     int64_t grid_blocks;      /* workgroups launched */
     int64_t grid_rows;        /* rows in flight at once (rows beyond are looped over) */
-    int32_t unroll;           /* 16-byte loads each lane keeps in flight per step */
-    int32_t reserved;
+    int32_t unroll;           /* loads each lane keeps in flight per step */
+    int32_t outputs_per_block;/* outputs one workgroup produces at a time */
     int64_t device_threads;   /* thread capacity the plan was made for */
     size_t scratch_bytes;     /* == argreduce_scratch_bytes() for the same arguments */
+    int32_t load_bytes;       /* bytes of one lane load in the body of the scan: 16, or the
+                                 element size for an AXIS plan whose `inner` row is not a
+                                 multiple of 16 bytes */
+    int32_t dispatches;       /* kernels one call launches: 1, or 2 for an AXIS plan whose
+                                 workgroups store partials that a second kernel merges */
 } argreduce_plan_t;
 
 /* The plan argreduce_lastaxis would use for these arguments on the current device. */
@@ -149,6 +156,38 @@ int argreduce_debug_set_capacity(int64_t threads);
  * A forced path keeps its own geometry rules; a forced SPLIT uses at least two workgroups
  * per row, however short the row. */
 int argreduce_debug_force_path(int path);
+
+/* ----------------------------------------------------------------------------------------
+ * Reduction over a middle axis.
+ *
+ * out_idx[o * inner + i] = ArgMax / ArgMin over r in [0, len) of x[o][r][i], for a contiguous
+ * row-major [outer, len, inner] tensor (flat position (o * len + r) * inner + i): ONNX's
+ * ArgMax/ArgMin over any axis after collapsing the dimensions before it into `outer` and
+ * those after it into `inner`. The first page (Semantics) notes that its CUDA provider
+ * sends non-last axes to a fallback; the semantics here are exactly those of
+ * argreduce_lastaxis applied to each (o, i) column, for every op. inner == 1 IS
+ * argreduce_lastaxis (rows = outer, cols = len), with the same scratch and plan.
+ *
+ *   outer >= 0 (0 is a no-op), 1 <= len <= INT32_MAX, inner >= 1. Pointers, alignment,
+ *   scratch, stream and status codes as for argreduce_lastaxis; out_idx holds
+ *   outer * inner int64 values.
+ *
+ *   When few outputs leave the device idle, the axis is split over several workgroups per
+ *   tile of outputs: each stores a (value, index) partial per output in scratch, and a
+ *   second kernel, enqueued on the same stream, merges them (the plan's `dispatches` is
+ *   then 2; nothing waits on another workgroup, so no output is ever -1). 16-byte loads
+ *   are used when inner * element size is a multiple of 16 and x is 16-byte aligned; the
+ *   scratch size returned covers both cases.
+ */
+size_t argreduce_axis_scratch_bytes(int64_t outer, int64_t len, int64_t inner,
+                                    argreduce_dtype_t dtype);
+int argreduce_axis(const void *x, argreduce_dtype_t dtype, int64_t outer, int64_t len,
+                   int64_t inner, argreduce_op_t op, int64_t *out_idx, void *scratch,
+                   size_t scratch_bytes, void *stream);
+/* The plan argreduce_axis would use for a 16-byte aligned x (path ARGREDUCE_PATH_AXIS
+ * unless inner == 1). */
+int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inner, argreduce_dtype_t dtype,
+                        argreduce_plan_t *plan);
 
 /* Measurement hook: the launch floor. Enqueues one empty kernel (one workgroup of 64
  * threads) on `stream`, the same way argreduce_lastaxis enqueues its kernels, so that a

@@ -14,6 +14,7 @@ MI355X_THREADS = 256 * 2048
 H200_THREADS = 132 * 2048
 INT32_MAX = 2 ** 31 - 1
 FAKE = 1 << 20  # an aligned, never-dereferenced address
+ESIZE = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}
 
 
 @pytest.fixture
@@ -172,3 +173,55 @@ def test_forced_paths(mi355x):
     assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 64
     assert B.argreduce_debug_force_path(5) == -1
     assert B.argreduce_debug_set_capacity(-5) == -1
+
+
+@pytest.mark.parametrize("outer,length,inner,dtype,code", [
+    (-1, 10, 4, B.F32, -1), (2, 0, 4, B.F32, -1), (2, 10, 0, B.F32, -1),
+    (2, 10, 4, 9, -2), (1, INT32_MAX + 1, 2, B.F16, -3),
+])
+def test_axis_invalid_arguments(lib, outer, length, inner, dtype, code):
+    assert B.argreduce_axis(FAKE, dtype, outer, length, inner, B.MAX, FAKE, 0, 0, 0) == code
+
+
+def test_axis_zero_outer_and_op_check(lib):
+    assert B.argreduce_axis(0, B.F32, 0, 10, 4, B.MAX, 0, 0, 0, 0) == 0
+    assert B.argreduce_axis(FAKE, B.F32, 2, 10, 4, 7, FAKE, 0, 0, 0) == -1
+
+
+def test_axis_plans(mi355x):
+    # inner == 1 is the last-axis reduction, with its plan and scratch
+    assert B.argreduce_axis_plan(1, 202048, 1, B.F32) == B.argreduce_plan(1, 202048, B.F32)
+    assert B.argreduce_axis_scratch_bytes(1, 202048, 1, B.F32) == B.argreduce_scratch_bytes(1, 202048, B.F32)
+    p = B.argreduce_axis_plan(4096, 512, 256, B.F32)  # more tiles than resident workgroups
+    assert p["path"] == B.PATH_AXIS and p["blocks_per_row"] == 1 and p["scratch_bytes"] == 0
+    assert p["outputs_per_block"] == 256 and p["load_bytes"] == 16 and p["dispatches"] == 1
+    p = B.argreduce_axis_plan(1, 1 << 20, 32, B.F32)  # few outputs, long axis: split
+    assert p["path"] == B.PATH_AXIS and p["blocks_per_row"] > 1 and p["dispatches"] == 2
+    assert p["scratch_bytes"] == 15 + p["blocks_per_row"] * 32 * 8
+    assert p["grid_blocks"] <= MI355X_THREADS // 256
+    # lanes: the next power of two of the vectors (16-byte loads) or elements per inner row
+    for (inner, dtype), (tile, load) in {
+        (3, B.F16): (4, 2), (9, B.F16): (16, 2), (16, B.F16): (16, 16), (8, B.BF16): (8, 16),
+        (6, B.F64): (8, 16), (4, B.F32): (4, 16), (260, B.F32): (256, 16), (250, B.F32): (64, 4),
+        (2, B.F32): (2, 4), (1000, B.F64): (128, 16),
+    }.items():
+        p = B.argreduce_axis_plan(3, 100, inner, dtype)
+        assert (p["outputs_per_block"], p["load_bytes"]) == (tile, load), (inner, dtype, p)
+        lanes = tile // (16 // ESIZE[dtype] if load == 16 else 1)  # lanes along inner
+        assert p["lanes_per_row"] == p["blocks_per_row"] * (256 // lanes)  # threads per output
+
+
+def test_axis_forced_paths(mi355x):
+    B.argreduce_debug_force_path(B.PATH_SPLIT)
+    assert B.argreduce_axis_plan(64, 100, 256, B.F32)["blocks_per_row"] >= 2
+    B.argreduce_debug_force_path(B.PATH_BLOCK)
+    assert B.argreduce_axis_plan(1, 1 << 20, 32, B.F32)["blocks_per_row"] == 1
+
+
+def test_axis_scratch_too_small(mi355x):
+    need = B.argreduce_axis_scratch_bytes(1, 1 << 20, 32, B.F32)
+    assert 0 < need < (1 << 20)
+    # FAKE is 16-byte aligned: the call takes the aligned plan
+    aligned = B.argreduce_axis_plan(1, 1 << 20, 32, B.F32)["scratch_bytes"]
+    assert 0 < aligned <= need
+    assert B.argreduce_axis(FAKE, B.F32, 1, 1 << 20, 32, B.MAX, FAKE, FAKE, aligned - 1, 0) == -4

@@ -258,3 +258,90 @@ def test_int32_max_wide_rows():
             assert rc == 0 and got.tolist() == want, (rows, cols, op, got)
         del x
         torch.cuda.empty_cache()
+
+
+def check_axis(oracle_lib, arr, dtype, op, what, **kw):
+    import torch
+
+    announce(f"{what} axis dtype={dtype} op={op} shape={arr.shape} plan="
+             f"{B.argreduce_axis_plan(*arr.shape, dtype)}")
+    outer, length, inner = arr.shape
+    t = to_device(arr.reshape(outer, length * inner), dtype, kw.get("offset", 0))
+    need = B.argreduce_axis_scratch_bytes(outer, length, inner, dtype)
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    if need and kw.get("dirty"):
+        scratch.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda"))
+    out = torch.full((outer * inner,), -7, dtype=torch.int64, device="cuda")
+    rc = B.argreduce_axis(t.data_ptr(), dtype, outer, length, inner, op, out.data_ptr(),
+                          scratch.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0, f"{what}: status {rc}"
+    got = out.cpu().numpy().reshape(outer, inner)
+    want = oracle_lib.argreduce_axis(arr, dtype, op)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (f"{what} {dtype} {op} {arr.shape}: {len(bad)} outputs differ; first "
+                           f"{tuple(bad[0])}: got {got[tuple(bad[0])]}, oracle {want[tuple(bad[0])]}")
+
+
+# inner spans the 4 / 16 / 64-lane tiles of element loads and the 8 / 32 / 64-lane tiles of
+# 16-byte loads (an inner row of 16, 32, 48 ... bytes), ragged last tiles, and, with a long
+# axis and few outputs, both the one-dispatch (polled) and the two-dispatch split.
+AXIS_SHAPES = [(1, 1, 2), (3, 7, 3), (2, 300, 5), (4, 33, 16), (2, 1000, 17), (5, 64, 64),
+               (2, 129, 100), (1, 20000, 32), (3, 5000, 4), (1, 70001, 2), (8, 512, 257),
+               (2, 700, 256), (1, 3000, 520), (1, 300000, 8)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_axis_shapes_all_ops(oracle_lib, hooks, dtype):
+    rng = np.random.default_rng(400 + DTYPES.index(dtype))
+    for outer, length, inner in AXIS_SHAPES:
+        for kind in ("ties", "mixed"):
+            arr = W.random_rows(rng, outer * length, inner, dtype, kind).reshape(outer, length, inner)
+            for op in OPS:
+                # offset 1: a base that is not 16-byte aligned takes the element loads
+                for offset in (0, 1):
+                    check_axis(oracle_lib, arr, dtype, op, f"axis kind={kind} offset={offset}",
+                               offset=offset)
+
+
+@pytest.mark.parametrize("path", [B.PATH_BLOCK, B.PATH_SPLIT])
+@pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
+def test_axis_forced_split_and_capacities(oracle_lib, hooks, path, cap):
+    rng = np.random.default_rng(500 + path + cap % 89)
+    B.argreduce_debug_set_capacity(cap)
+    B.argreduce_debug_force_path(path)
+    for dtype in DTYPES:
+        for outer, length, inner in [(3, 7, 3), (2, 1000, 17), (1, 20000, 32), (6, 300, 70)]:
+            arr = W.random_rows(rng, outer * length, inner, dtype, "special").reshape(outer, length, inner)
+            for op in OPS:
+                check_axis(oracle_lib, arr, dtype, op, f"axis forced={path} cap={cap}", dirty=True)
+
+
+def test_axis_torch_wrapper_dims(oracle_lib):
+    import torch
+    import argmin_reduction_wide_amd as ar
+
+    rng = np.random.default_rng(9)
+    arr = W.random_rows(rng, 4 * 6, 50, "f32", "ties").reshape(4, 6, 50)
+    t = to_device(arr.reshape(24, 50), "f32").view(4, 6, 50)
+    for dim in (0, 1, 2, -1, -2):
+        d = dim % 3
+        shp = arr.shape
+        outer = int(np.prod(shp[:d])); length = shp[d]; inner = int(np.prod(shp[d + 1:]))
+        want = oracle_lib.argreduce_axis(np.ascontiguousarray(arr).reshape(outer, length, inner), "f32", "max")
+        announce(f"torch wrapper dim={dim}")
+        got = ar.argmax(t, dim=dim)
+        assert got.shape == tuple(s for k, s in enumerate(shp) if k != d)
+        assert np.array_equal(got.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
+        got = ar.argmin(t, dim=dim, select_last_index=True)
+        want = oracle_lib.argreduce_axis(np.ascontiguousarray(arr).reshape(outer, length, inner), "f32", "min_last")
+        assert np.array_equal(got.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
+
+
+def test_axis_workloads_full_size(oracle_lib):
+    """The two middle-axis bench workloads at full size, every output against the oracle."""
+    for w in W.config_workloads("axis"):
+        outer, length, inner = w.axis_shape
+        arr = w.data.reshape(outer, length, inner)
+        for op in w.ops + tuple(o + "_last" for o in w.ops):
+            check_axis(oracle_lib, arr, w.dtype, op, f"axis workload {w.name}")

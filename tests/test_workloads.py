@@ -59,3 +59,14 @@ def test_planted_counts():
     c3 = W.c3_rows32_f16_bf16("f16")
     assert set(c3.planted["max"].values()) >= {0, 202047}
     assert 202046 in c3.planted["min"].values()
+
+
+def test_axis_workloads_shapes(oracle_lib):
+    ws = W.config_workloads("axis")
+    assert [w.axis_shape for w in ws] == [(64, 4096, 256), (1, 1 << 20, 32)]
+    for w in ws:
+        outer, length, inner = w.axis_shape
+        assert w.data.shape == (outer, length * inner) and w.data.dtype == np.float32
+        got = oracle_lib.argreduce_axis(w.data.reshape(outer, length, inner), "f32", "max")
+        want = np.argmax(w.data.reshape(outer, length, inner), axis=1)  # NaN-free: first occurrence
+        assert np.array_equal(got, want)
