@@ -8,12 +8,15 @@ this package imports nothing from the product path.
 The arithmetic lives in ``argreduce_oracle.c``: the sequential strict-compare scan seeded
 at element 0 that the ONNX Runtime pages use as the definition of the result
 ("[CUDA] Parallelize ArgMax/ArgMin over wide last axes", Description / Semantics;
-"[CUDA] Parallelize ArgMax/ArgMin over the reduction axis", Semantics). This module only
+"[CUDA] Parallelize ArgMax/ArgMin over the reduction axis", Semantics), and the same scan
+reported at every position for cummax / cummin (the PaddlePaddle issue on the cummax /
+cummin kernel, fix proposals: an ArgMax-style (value, index) operator, ties to the
+earlier index). This module only
 compiles it with gcc and marshals numpy arrays into it.
 
 Element formats are given as strings: ``"f32"`` (numpy float32), ``"f16"`` (numpy
-float16), ``"bf16"`` (numpy uint16 holding bfloat16 bit patterns) and ``"f64"`` (numpy
-float64). Ops are ``"max"`` (ArgMax), ``"min"`` (ArgMin), and ``"max_last"`` /
+float16), ``"bf16"`` (numpy uint16 holding bfloat16 bit patterns), ``"f64"`` (numpy
+float64) and, for the cumulative scan only, ``"i32"`` / ``"i64"`` (numpy int32 / int64). Ops are ``"max"`` (ArgMax), ``"min"`` (ArgMin), and ``"max_last"`` /
 ``"min_last"`` (ties to the last index, ONNX's select_last_index = 1: the same scan with
 a non-strict comparison).
 """
@@ -29,9 +32,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "argreduce_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_argreduce.so")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f64": 3, "i32": 4, "i64": 5}
 OP_CODE = {"max": 0, "min": 1, "max_last": 2, "min_last": 3}
-NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64}
+NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64,
+                 "i32": np.int32, "i64": np.int64}
 
 # -O2, IEEE semantics: no -ffast-math, no -ffinite-math-only, no flush-to-zero.
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-Wall", "-Wextra"]
@@ -59,6 +63,11 @@ class Oracle:
                       ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
         a.restype = ctypes.c_int
         self._a = a
+        c = lib.oracle_cumulative
+        c.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                      ctypes.c_void_p, ctypes.c_void_p]
+        c.restype = ctypes.c_int
+        self._c = c
         d = lib.oracle_widen
         d.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
         d.restype = ctypes.c_int
@@ -88,6 +97,20 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle rejected shape {x.shape} dtype={dtype} op={op}")
         return out
+
+    def cumulative(self, x: np.ndarray, dtype: str, op: str) -> tuple[np.ndarray, np.ndarray]:
+        """Running extremum of every row prefix of the 2-D array ``x``: (values, indices),
+        values in ``x``'s storage format, indices int64, both of ``x``'s shape. ``op`` is
+        ``"max"`` (cummax) or ``"min"`` (cummin)."""
+        x = _as_storage(x, dtype)
+        rows, cols = x.shape
+        vals = np.empty_like(x)
+        idx = np.empty((rows, cols), dtype=np.int64)
+        rc = self._c(x.ctypes.data, DTYPE_CODE[dtype], rows, cols, OP_CODE[op], vals.ctypes.data,
+                     idx.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle rejected rows={rows} cols={cols} dtype={dtype} op={op}")
+        return vals, idx
 
     def widen(self, x: np.ndarray, dtype: str) -> np.ndarray:
         """Every element of ``x`` as the oracle's scan sees it (float64)."""

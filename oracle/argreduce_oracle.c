@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the last-axis ArgMax / ArgMin reduction.
+ * CPU oracle for the last-axis ArgMax / ArgMin reduction, its middle-axis form, and the
+ * cumulative (running) extremum with indices at the end of this file.
  *
  * TEST INFRASTRUCTURE ONLY. This library exists to check the HIP library, and is
  * loaded only by tests/, by __graft_entry__.smoke() and by the cpu_baseline leg of
@@ -39,11 +40,14 @@
 #include <stdint.h>
 #include <string.h>
 
-/* Element formats, numbered as the Python wrapper of this file numbers them. */
+/* Element formats, numbered as the Python wrapper of this file numbers them. The integer
+ * formats are read only by the cumulative scan at the end of this file. */
 #define ORACLE_F32 0
 #define ORACLE_F16 1
 #define ORACLE_BF16 2
 #define ORACLE_F64 3
+#define ORACLE_I32 4
+#define ORACLE_I64 5
 
 #define ORACLE_ARGMAX 0
 #define ORACLE_ARGMIN 1
@@ -185,5 +189,84 @@ int oracle_widen(const void *x, int dtype, int64_t n, double *out)
         return -1;
     for (int64_t k = 0; k < n; ++k)
         out[k] = element(x, dtype, k);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Cumulative maximum / minimum with indices along the last axis (the PaddlePaddle issue on
+ * the cummax/cummin CUDA kernel: "[Performance] cummax/cummin ... dim3(16,32)": the scan
+ * returns, for every position, the running extremum and its index; its fix proposals
+ * describe the reduce operator as ArgMax semantics with ties going to the earlier index).
+ *
+ * Definition written out: for every row and every position j, the result at j is what the
+ * sequential ArgMax (cummax) / ArgMin (cummin) scan above returns for the prefix of
+ * elements 0 .. j: the running best starts as element 0 with index 0 and moves only to a
+ * strictly greater (smaller) element, so ties keep the earlier index, a NaN never becomes
+ * the running best except as element 0, and a leading NaN stays the running best for the
+ * whole row. out_idx[r][j] is that index; out_val[r][j] is a copy of the storage bytes of
+ * the element at that index (so a leading NaN is reported with its own bit pattern).
+ *
+ * The running best is kept as an index, and every comparison reads both elements in their
+ * own format: floating-point elements widened to double as above (exact), integers as
+ * int64_t (exact; a double would round integers beyond 2^53).
+ * --------------------------------------------------------------------------------------- */
+
+static int elem_size(int dtype)
+{
+    switch (dtype) {
+    case ORACLE_F32: return 4;
+    case ORACLE_F16: return 2;
+    case ORACLE_BF16: return 2;
+    case ORACLE_F64: return 8;
+    case ORACLE_I32: return 4;
+    case ORACLE_I64: return 8;
+    default: return 0;
+    }
+}
+
+static int64_t int_element(const void *x, int dtype, int64_t k)
+{
+    if (dtype == ORACLE_I32) {
+        int32_t v;
+        memcpy(&v, (const char *)x + k * 4, 4);
+        return v;
+    }
+    int64_t v;
+    memcpy(&v, (const char *)x + k * 8, 8);
+    return v;
+}
+
+/* Whether element ka of x moves the scan from its running best, element kb. */
+static int scan_moves(const void *x, int dtype, int op, int64_t ka, int64_t kb)
+{
+    if (dtype == ORACLE_I32 || dtype == ORACLE_I64) {
+        const int64_t a = int_element(x, dtype, ka), b = int_element(x, dtype, kb);
+        return op == ORACLE_ARGMAX ? a > b : a < b;
+    }
+    return moves(op, element(x, dtype, ka), element(x, dtype, kb));
+}
+
+/*
+ * out_val (same format as x) and out_idx (int64), both [rows, cols], as defined above.
+ * op: ORACLE_ARGMAX = cummax, ORACLE_ARGMIN = cummin. Returns 0, or -1 for arguments the
+ * definition does not cover (cols < 1, unknown format, other ops).
+ */
+int oracle_cumulative(const void *x, int dtype, int64_t rows, int64_t cols, int op,
+                      void *out_val, int64_t *out_idx)
+{
+    const int size = elem_size(dtype);
+    if (rows < 0 || cols < 1 || size == 0 || (op != ORACLE_ARGMAX && op != ORACLE_ARGMIN))
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t row0 = r * cols;
+        int64_t best = 0; /* index of the running best within the row */
+        for (int64_t j = 0; j < cols; ++j) {
+            if (j > 0 && scan_moves(x, dtype, op, row0 + j, row0 + best))
+                best = j;
+            out_idx[row0 + j] = best;
+            memcpy((char *)out_val + (row0 + j) * size, (const char *)x + (row0 + best) * size,
+                   (size_t)size);
+        }
+    }
     return 0;
 }

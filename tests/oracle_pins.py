@@ -230,6 +230,178 @@ def pin_rejects_empty_rows(o) -> None:
     raise AssertionError("an empty row has no index; the oracle must refuse cols == 0")
 
 
+# ----------------------------------------------------------------------------------------
+# cumulative extremum with indices (cummax / cummin)
+#
+# Every position j reports the ArgMax / ArgMin scan of the prefix 0 .. j and the element
+# stored at that index. The checks below compute that from outside the oracle: the closed
+# form above (floats) or numpy's exact integer argmax / argmin (integers) on every prefix,
+# numpy's running maximum / minimum on NaN-free data, the page's two-pass tile + carry
+# recipe for the values, and the page's examples with results known by construction.
+
+CUM_DTYPES = ("f32", "f16", "bf16", "f64", "i32", "i64")
+CUM_OPS = ("max", "min")
+INT_INFO = {"i32": np.iinfo(np.int32), "i64": np.iinfo(np.int64)}
+INT_NP = {"i32": np.int32, "i64": np.int64}
+CUM_GOLDEN = os.path.join(HERE, "golden", "cumulative_cases.json")
+
+
+def int_alphabet(dtype: str) -> np.ndarray:
+    i = INT_INFO[dtype]
+    return np.array([i.min, i.min + 1, -1, 0, 1, i.max - 1, i.max], dtype=INT_NP[dtype])
+
+
+def storage_bits(a: np.ndarray) -> np.ndarray:
+    """The raw bit patterns of a storage array (so NaN payloads and zero signs compare)."""
+    return np.ascontiguousarray(a).view({1: np.uint8, 2: np.uint16, 4: np.uint32,
+                                         8: np.uint64}[a.dtype.itemsize])
+
+
+def prefix_indices(vals: np.ndarray, dtype: str, op: str) -> np.ndarray:
+    """Index of the scan over every prefix, from outside the oracle: the closed form for
+    floating point, numpy's first-occurrence argmax / argmin on the exact integers."""
+    rows, cols = vals.shape
+    out = np.empty((rows, cols), dtype=np.int64)
+    for j in range(cols):
+        if dtype in INT_NP:
+            f = np.argmax if op == "max" else np.argmin
+            out[:, j] = f(vals[:, :j + 1], axis=1)
+        else:
+            out[:, j] = closed_form(vals[:, :j + 1], op)
+    return out
+
+
+def cum_storage(vals, dtype: str) -> np.ndarray:
+    if dtype in INT_NP:
+        return np.ascontiguousarray(np.asarray(vals, dtype=INT_NP[dtype]))
+    return exact_storage(vals, dtype)
+
+
+def check_cumulative(o, vals, dtype: str, op: str, want_idx: np.ndarray, what: str) -> None:
+    x = cum_storage(vals, dtype)
+    got_v, got_i = o.cumulative(x, dtype, op)
+    bad = np.argwhere(got_i != want_idx)
+    assert bad.size == 0, (f"{what} {dtype} {op}: index differs at {tuple(bad[0])}: "
+                           f"got {got_i[tuple(bad[0])]}, want {want_idx[tuple(bad[0])]}")
+    want_v = np.take_along_axis(x, want_idx, axis=1)
+    assert np.array_equal(storage_bits(got_v), storage_bits(want_v)), f"{what} {dtype} {op}: values"
+
+
+def pin_cum_brute_force(o, dtype: str, op: str, max_len: int = 4) -> None:
+    """Every row of length 1..max_len over a special-value alphabet."""
+    alpha = int_alphabet(dtype) if dtype in INT_NP else alphabet9(dtype)
+    for n in range(1, max_len + 1):
+        sym = np.array(list(itertools.product(range(alpha.size), repeat=n)), dtype=np.int64)
+        vals = alpha[sym]
+        check_cumulative(o, vals, dtype, op, prefix_indices(vals, dtype, op), f"brute len {n}")
+
+
+def cum_nan_free_rows(rng, dtype: str, rows: int, cols: int, kind: str) -> np.ndarray:
+    if dtype in INT_NP:
+        i = INT_INFO[dtype]
+        if kind == "ties":
+            return rng.integers(-3, 4, size=(rows, cols)).astype(INT_NP[dtype])
+        v = rng.integers(i.min, i.max, size=(rows, cols), dtype=INT_NP[dtype], endpoint=True)
+        return v
+    z = rng.standard_normal((rows, cols))
+    v = np.clip(np.rint(4 * z), -8, 7) / 4 if kind == "ties" else z
+    if dtype == "bf16":
+        v = ((v.astype(np.float32).view(np.uint32) >> np.uint32(16)) << np.uint32(16)).view(np.float32)
+    return v.astype({"f32": np.float32, "f16": np.float16, "bf16": np.float32,
+                     "f64": np.float64}[dtype]).astype(np.float64)
+
+
+def pin_cum_numpy_accumulate(o, dtype: str, op: str) -> None:
+    """NaN-free rows: the values are numpy's running maximum / minimum, and the index is
+    the first position (within the prefix) holding that running value."""
+    rng = np.random.default_rng(41 + CUM_DTYPES.index(dtype))
+    acc = np.maximum.accumulate if op == "max" else np.minimum.accumulate
+    for rows, cols in ((40, 1), (17, 130), (3, 700)):
+        for kind in ("normal", "ties"):
+            v = cum_nan_free_rows(rng, dtype, rows, cols, kind)
+            x = cum_storage(v, dtype)
+            got_v, got_i = o.cumulative(x, dtype, op)
+            run = acc(v, axis=1)
+            num = got_v.astype(np.float64) if dtype == "bf16" else got_v
+            if dtype == "bf16":
+                num = (got_v.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+            assert np.array_equal(num, run), f"{dtype} {op} {kind}: values vs numpy accumulate"
+            pos = np.arange(cols)
+            for j in range(cols):
+                first = np.argmax((v == run[:, j:j + 1]) & (pos <= j), axis=1)
+                assert np.array_equal(got_i[:, j], first), f"{dtype} {op} {kind}: index at {j}"
+
+
+def pin_cum_two_pass(o, dtype: str, op: str) -> None:
+    """The page's two-pass recipe for the values of a long 1-D scan: running extremum
+    within tiles, running extremum of the tile ends shifted by one tile (the carry, the
+    format's lowest (highest) value first), and the elementwise extremum of the two. The
+    page reports it bit-equal to the one-pass scan (on NaN-free data)."""
+    rng = np.random.default_rng(53 + CUM_DTYPES.index(dtype))
+    tiles, width = 64, 48
+    v = cum_nan_free_rows(rng, dtype, 1, tiles * width, "ties")[0]
+    acc = np.maximum.accumulate if op == "max" else np.minimum.accumulate
+    pick = np.maximum if op == "max" else np.minimum
+    if dtype in INT_NP:
+        edge = INT_INFO[dtype].min if op == "max" else INT_INFO[dtype].max
+    else:
+        edge = -np.inf if op == "max" else np.inf
+    part = acc(v.reshape(tiles, width), axis=1)
+    carry = acc(part[:, -1])
+    carry = np.concatenate([np.array([edge], dtype=v.dtype), carry[:-1]])
+    want = pick(part, carry[:, None]).reshape(-1)
+    got_v, _ = o.cumulative(cum_storage(v[None, :], dtype), dtype, op)
+    num = got_v[0]
+    if dtype == "bf16":
+        num = (num.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    assert np.array_equal(num.astype(v.dtype), want), f"{dtype} {op}: two-pass recipe"
+
+
+def pin_cum_page_examples(o) -> None:
+    """The page's own data, with results known by construction: cummax / cummin of an
+    int64 arange of 65536 elements (reproduction script), and the document-start forward
+    fill cummax(is_boundary * positions) of its real-impact section."""
+    n = 65536
+    a = np.arange(n, dtype=np.int64)[None, :]
+    v, i = o.cumulative(a, "i64", "max")
+    assert np.array_equal(v[0], a[0]) and np.array_equal(i[0], a[0]), "arange cummax"
+    v, i = o.cumulative(a, "i64", "min")
+    assert not v.any() and not i.any(), "arange cummin"
+    rng = np.random.default_rng(61)
+    starts = np.sort(rng.choice(np.arange(1, n), size=40, replace=False))
+    x = np.zeros(n, dtype=np.int64)
+    x[starts] = starts
+    want = np.zeros(n, dtype=np.int64)  # start of the document holding each position
+    for s in starts:
+        want[s:] = s
+    v, i = o.cumulative(x[None, :], "i64", "max")
+    assert np.array_equal(v[0], want), "document starts: values"
+    assert np.array_equal(i[0], want), "document starts: indices (a start is its own index)"
+
+
+def pin_cum_fixed_cases(o, section: str = "cases") -> None:
+    with open(CUM_GOLDEN) as f:
+        cases = json.load(f)[section]
+    for case in cases:
+        for dtype in case["dtypes"]:
+            for spec, want in zip(case["rows"], case["expect"]):
+                if dtype in INT_NP:
+                    row = np.array([int(s) for s in spec], dtype=object).astype(INT_NP[dtype])
+                else:
+                    row = golden_row(spec, dtype)
+                check_cumulative(o, row[None, :], dtype, case["op"],
+                                 np.array([want], dtype=np.int64), case["name"])
+
+
+def pin_cum_rejects(o) -> None:
+    for bad in ((np.zeros((2, 0), np.float32), "f32", "max"), (np.zeros((2, 3), np.float32), "f32", "max_last")):
+        try:
+            o.cumulative(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"the oracle must refuse {bad[1]} {bad[2]} of shape {bad[0].shape}")
+
+
 def all_pins(o, fast: bool = False):
     """(name, thunk) for every pin; ``fast`` trims the brute force to length 4."""
     max_len = 4 if fast else 5
@@ -246,4 +418,14 @@ def all_pins(o, fast: bool = False):
             pins.append((f"numpy_{dtype}_{op}",
                          lambda d=dtype, p=op: pin_numpy_first_occurrence(o, d, p)))
             pins.append((f"axis_{dtype}_{op}", lambda d=dtype, p=op: pin_axis(o, d, p)))
+    pins += [("cum_fixed_cases", lambda: pin_cum_fixed_cases(o, "cases")),
+             ("cum_readings", lambda: pin_cum_fixed_cases(o, "readings")),
+             ("cum_page_examples", lambda: pin_cum_page_examples(o)),
+             ("cum_rejects", lambda: pin_cum_rejects(o))]
+    for dtype in CUM_DTYPES:
+        for op in CUM_OPS:
+            pins.append((f"cum_brute_{dtype}_{op}",
+                         lambda d=dtype, p=op: pin_cum_brute_force(o, d, p, 3 if fast else 4)))
+            pins.append((f"cum_numpy_{dtype}_{op}", lambda d=dtype, p=op: pin_cum_numpy_accumulate(o, d, p)))
+            pins.append((f"cum_two_pass_{dtype}_{op}", lambda d=dtype, p=op: pin_cum_two_pass(o, d, p)))
     return pins

@@ -29,15 +29,37 @@ MUTANTS = [
     ("identity_seed_instead_of_element0",
      "double best = element(x, dtype, row0);",
      "double best = (op == ORACLE_ARGMAX) ? -INFINITY : INFINITY;"),
-    ("row_stride_off_by_one", "const int64_t row0 = r * cols;", "const int64_t row0 = r * (cols - 1);"),
+    ("row_stride_off_by_one", "const int64_t row0 = r * cols;\n        double best",
+     "const int64_t row0 = r * (cols - 1);\n        double best"),
     ("f16_subnormals_flushed", "mag = ldexp((double)frac, -24);", "mag = 0.0;"),
     ("f16_exponent_bias", "expo - 25);", "expo - 24);"),
     ("bf16_wrong_shift", "(uint32_t)b << 16;", "(uint32_t)b << 15;"),
-    ("f64_read_as_f32_stride", "(const char *)x + k * 8, 8);", "(const char *)x + k * 4, 8);"),
+    ("f64_read_as_f32_stride", "memcpy(&d, (const char *)x + k * 8, 8);",
+     "memcpy(&d, (const char *)x + k * 4, 8);"),
     ("last_column_skipped", "for (int64_t j = 1; j < cols; ++j)", "for (int64_t j = 1; j < cols - 1; ++j)"),
-    ("empty_rows_accepted", "cols < 1 ||", "cols < 0 ||"),
+    ("empty_rows_accepted", "cols < 1 || dtype", "cols < 0 || dtype"),
     ("axis_stride_wrong", "element(x, dtype, base + r * inner)", "element(x, dtype, base + r * len)"),
     ("axis_output_transposed", "out[o * inner + i] = idx;", "out[i * outer + o] = idx;"),
+    # cumulative extremum with indices
+    ("cum_int_ties_to_later_index", "return op == ORACLE_ARGMAX ? a > b : a < b;",
+     "return op == ORACLE_ARGMAX ? a >= b : a < b;"),
+    ("cum_int_cummin_as_cummax", "return op == ORACLE_ARGMAX ? a > b : a < b;", "return a > b;"),
+    ("cum_float_ties_to_later_index", "return moves(op, element(x, dtype, ka), element(x, dtype, kb));",
+     "return moves(op + 2, element(x, dtype, ka), element(x, dtype, kb));"),
+    ("cum_nan_propagates", "return moves(op, element(x, dtype, ka), element(x, dtype, kb));",
+     "return isnan(element(x, dtype, ka)) || moves(op, element(x, dtype, ka), element(x, dtype, kb));"),
+    ("cum_value_from_position_not_index", "(const char *)x + (row0 + best) * size",
+     "(const char *)x + (row0 + j) * size"),
+    ("cum_integers_compared_as_double",
+     "const int64_t a = int_element(x, dtype, ka), b = int_element(x, dtype, kb);",
+     "const double a = (double)int_element(x, dtype, ka), b = (double)int_element(x, dtype, kb);"),
+    ("cum_i32_read_as_i64", "if (dtype == ORACLE_I32) {", "if (dtype == -1) {"),
+    ("cum_position_1_skipped", "if (j > 0 && scan_moves", "if (j > 1 && scan_moves"),
+    ("cum_empty_rows_accepted", "cols < 1 || size == 0", "cols < 0 || size == 0"),
+    ("cum_row_stride_off_by_one", "const int64_t row0 = r * cols;\n        int64_t best = 0;",
+     "const int64_t row0 = r * (cols - 1);\n        int64_t best = 0;"),
+    ("cum_i64_read_with_i32_stride", "memcpy(&v, (const char *)x + k * 8, 8);",
+     "memcpy(&v, (const char *)x + k * 4, 8);"),
 ]
 
 
