@@ -1,4 +1,4 @@
-"""MI355X (gfx950) last-axis ArgMax / ArgMin.
+"""MI355X (gfx950) ArgMax / ArgMin (last or middle axis) and cummax / cummin with indices.
 
 The computation runs in the HIP library ``libargreduce.so`` (C ABI: include/argreduce.h);
 ``binding`` marshals arguments into it. Importing this package loads nothing; the library
@@ -15,5 +15,10 @@ from .binding import (  # noqa: F401
     argreduce_debug_set_capacity,
     argreduce_lastaxis,
     argreduce_plan,
+    argreduce_scan_lastaxis,
+    argreduce_scan_plan,
+    argreduce_scan_scratch_bytes,
     argreduce_scratch_bytes,
+    cummax,
+    cummin,
 )

@@ -16,9 +16,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libargreduce.so")
 
 # enums of include/argreduce.h
-F32, F16, BF16, F64 = 0, 1, 2, 3
+F32, F16, BF16, F64, I32, I64 = 0, 1, 2, 3, 4, 5
 MAX, MIN, MAX_LAST, MIN_LAST = 0, 1, 2, 3
-PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS = -1, 0, 1, 2, 3
+PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS, PATH_SCAN = -1, 0, 1, 2, 3, 4
 OK = 0
 ERRORS = {
     -1: "ARGREDUCE_ERR_INVALID_ARG",
@@ -28,7 +28,7 @@ ERRORS = {
     -5: "ARGREDUCE_ERR_HIP",
     -6: "ARGREDUCE_ERR_NO_DEVICE",
 }
-DTYPE_NAMES = {"f32": F32, "f16": F16, "bf16": BF16, "f64": F64}
+DTYPE_NAMES = {"f32": F32, "f16": F16, "bf16": BF16, "f64": F64, "i32": I32, "i64": I64}
 OP_NAMES = {"max": MAX, "min": MIN, "max_last": MAX_LAST, "min_last": MIN_LAST}
 SIZE_MAX = ctypes.c_size_t(-1).value
 
@@ -36,7 +36,8 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_debug_set_capacity", "argreduce_debug_force_path",
            "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events",
-           "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan")
+           "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
+           "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan")
 
 
 class ArgreduceError(RuntimeError):
@@ -97,6 +98,12 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_axis_plan.argtypes = [i64, i64, i64, c_int,
                                                   ctypes.POINTER(argreduce_plan_t)]
                 h.argreduce_axis_plan.restype = c_int
+                h.argreduce_scan_scratch_bytes.argtypes = [i64, i64, c_int]
+                h.argreduce_scan_scratch_bytes.restype = sz
+                h.argreduce_scan_lastaxis.argtypes = [vp, c_int, i64, i64, c_int, vp, vp, vp, sz, vp]
+                h.argreduce_scan_lastaxis.restype = c_int
+                h.argreduce_scan_plan.argtypes = [i64, i64, c_int, ctypes.POINTER(argreduce_plan_t)]
+                h.argreduce_scan_plan.restype = c_int
                 h.argreduce_debug_launch_empty.argtypes = [vp]
                 h.argreduce_debug_launch_empty.restype = c_int
                 h.argreduce_debug_set_kernel_events.argtypes = [vp, vp]
@@ -155,6 +162,24 @@ def argreduce_axis_plan(outer: int, length: int, inner: int, dtype) -> dict:
     return p.as_dict()
 
 
+def argreduce_scan_scratch_bytes(rows: int, cols: int, dtype) -> int:
+    return lib().argreduce_scan_scratch_bytes(rows, cols, _dtype_code(dtype))
+
+
+def argreduce_scan_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, values_ptr: int,
+                            idx_ptr: int, scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
+    return lib().argreduce_scan_lastaxis(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
+                                         values_ptr, idx_ptr, scratch_ptr, scratch_bytes, stream)
+
+
+def argreduce_scan_plan(rows: int, cols: int, dtype) -> dict:
+    p = argreduce_plan_t()
+    rc = lib().argreduce_scan_plan(rows, cols, _dtype_code(dtype), ctypes.byref(p))
+    if rc != OK:
+        raise ArgreduceError(rc, "argreduce_scan_plan")
+    return p.as_dict()
+
+
 def argreduce_debug_set_capacity(threads: int) -> int:
     return lib().argreduce_debug_set_capacity(threads)
 
@@ -183,7 +208,7 @@ def _torch_dtype_code(t) -> int:
 
     if _TORCH_DTYPES is None:
         _TORCH_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
-                         torch.float64: F64}
+                         torch.float64: F64, torch.int32: I32, torch.int64: I64}
     try:
         return _TORCH_DTYPES[t.dtype]
     except KeyError:
@@ -233,3 +258,46 @@ def argmin(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = F
     """Index of the minimum along `dim` (first occurrence, or the last with
     select_last_index; NaN is never selected, a leading NaN gives 0)."""
     return _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch, dim)
+
+
+def _scan(t, op: int, dim: int, scratch=None):
+    import torch
+
+    if not t.is_cuda:
+        raise ValueError("the scan runs on the GPU only; got a CPU tensor")
+    if t.dim() == 0:
+        raise ValueError("the scan needs at least one dimension")
+    if not t.is_contiguous():
+        raise ValueError("the scan needs a contiguous tensor")
+    if dim % t.dim() != t.dim() - 1:
+        raise ValueError("the scan runs along the last dimension only")
+    dtype = _torch_dtype_code(t)
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else 0
+    values = torch.empty_like(t)
+    indices = torch.empty(t.shape, dtype=torch.int64, device=t.device)
+    need = argreduce_scan_scratch_bytes(rows, cols, dtype)
+    if need == SIZE_MAX:
+        raise ArgreduceError(-1, f"argreduce_scan_scratch_bytes({rows}, {cols})")
+    if need and (scratch is None or scratch.numel() * scratch.element_size() < need):
+        scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
+    sptr = scratch.data_ptr() if need else 0
+    sbytes = scratch.numel() * scratch.element_size() if need else 0
+    stream = torch.cuda.current_stream(t.device).cuda_stream
+    rc = argreduce_scan_lastaxis(t.data_ptr(), dtype, rows, cols, op, values.data_ptr(),
+                                 indices.data_ptr(), sptr, sbytes, stream)
+    if rc != OK:
+        raise ArgreduceError(rc, f"argreduce_scan_lastaxis(rows={rows}, cols={cols})")
+    return values, indices
+
+
+def cummax(t, dim: int = -1, scratch=None):
+    """(values, indices) of the running maximum along the last dimension: at every position
+    the ArgMax of the prefix (ties keep the earlier index, NaN never taken after position 0,
+    a leading NaN holds) and the element there."""
+    return _scan(t, MAX, dim, scratch)
+
+
+def cummin(t, dim: int = -1, scratch=None):
+    """(values, indices) of the running minimum along the last dimension (as cummax)."""
+    return _scan(t, MIN, dim, scratch)

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libargreduce.so")
-SOURCES = [os.path.join(CSRC, "argreduce_kernels.hip"), os.path.join(CSRC, "argreduce_api.cpp")]
+SOURCES = [os.path.join(CSRC, "argreduce_kernels.hip"), os.path.join(CSRC, "argreduce_scan.hip"),
+           os.path.join(CSRC, "argreduce_api.cpp")]
 ARCH = "gfx950"
 
 
@@ -40,12 +41,33 @@ def flags() -> list[str]:
 
 
 def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    cmd = [hipcc(), *flags(), *(extra or []), *SOURCES, "-o", out + ".tmp"]
+    """Compile every source to an object (in parallel), then link the shared library."""
+    objdir = os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in flags() if f != "-shared"]
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [hipcc(), *compile_flags, *(extra or []), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+    failed = []
+    for src, proc in procs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            failed.append(f"{os.path.basename(src)} ({proc.returncode}):\n{err[-6000:]}")
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
+    cmd = [hipcc(), *flags(), *(extra or []), *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-8000:]}")
+        raise RuntimeError(f"link failed ({proc.returncode}):\n{proc.stderr[-8000:]}")
     os.replace(out + ".tmp", out)
     return out
 

@@ -263,11 +263,48 @@ void fill_plan(const Plan& p, argreduce_plan_t* out) {
     out->dispatches = 1;
 }
 
+// Cumulative scan: every format, integers included.
+int64_t scan_elem_size(int dtype) {
+    switch (dtype) {
+        case ARGREDUCE_I32: return 4;
+        case ARGREDUCE_I64: return 8;
+        default: return elem_size(dtype);
+    }
+}
+
+int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan* p) {
+    const int64_t es = scan_elem_size(dtype);
+    if (es == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || cols < 1) return ARGREDUCE_ERR_INVALID_ARG;
+    if (cols > std::numeric_limits<int32_t>::max()) return ARGREDUCE_ERR_TOO_WIDE;
+    if (rows > std::numeric_limits<int64_t>::max() / (cols * 8)) return ARGREDUCE_ERR_INVALID_ARG;
+    int64_t cap = 0;
+    const int rc = device_threads(&cap);
+    if (rc != ARGREDUCE_OK) return rc;
+    *p = ScanPlan{};
+    p->rows = rows;
+    p->cols = cols;
+    p->tile_elems = kBlock * kScanUnroll * (16 / es);
+    p->tiles_per_row = ceil_div(cols, p->tile_elems);
+    if (rows > 0 && rows > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / p->tiles_per_row)
+        return ARGREDUCE_ERR_TOO_WIDE;
+    p->grid_blocks = rows * p->tiles_per_row;
+    p->vecio = (aligned && (cols * es) % 16 == 0) ? 1 : 0;
+    p->device_threads = cap;
+    if (p->tiles_per_row > 1) {
+        p->state_words = static_cast<size_t>(rows) * static_cast<size_t>(p->tiles_per_row) *
+                         scan_state_words(dtype);
+        p->scratch_bytes = 15 + p->state_words * sizeof(uint64_t);
+    }
+    return ARGREDUCE_OK;
+}
+
 }  // namespace
 }  // namespace argreduce
 
 using argreduce::AxisPlan;
 using argreduce::Plan;
+using argreduce::ScanPlan;
 
 ARGREDUCE_EXPORT size_t argreduce_scratch_bytes(int64_t rows, int64_t cols,
                                                 argreduce_dtype_t dtype) {
@@ -401,5 +438,74 @@ ARGREDUCE_EXPORT int argreduce_axis(const void* x, argreduce_dtype_t dtype, int6
     }
     const hipError_t err = argreduce::launch_axis(p, x, dtype, op, out_idx, scratch16,
                                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ARGREDUCE_OK : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT size_t argreduce_scan_scratch_bytes(int64_t rows, int64_t cols,
+                                                     argreduce_dtype_t dtype) {
+    ScanPlan p;
+    if (argreduce::make_scan_plan(rows, cols, dtype, true, &p) != ARGREDUCE_OK)
+        return std::numeric_limits<size_t>::max();
+    return p.scratch_bytes;  // the same for aligned and unaligned buffers
+}
+
+ARGREDUCE_EXPORT int argreduce_scan_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype,
+                                         argreduce_plan_t* out) {
+    if (out == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    ScanPlan p;
+    const int rc = argreduce::make_scan_plan(rows, cols, dtype, true, &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    out->path = ARGREDUCE_PATH_SCAN;
+    out->lanes_per_row = static_cast<int32_t>(p.tiles_per_row * argreduce::kBlock);
+    out->blocks_per_row = static_cast<int32_t>(p.tiles_per_row);
+    out->block_threads = static_cast<int32_t>(argreduce::kBlock);
+    out->grid_blocks = p.grid_blocks;
+    out->grid_rows = rows;
+    out->unroll = argreduce::kScanUnroll;
+    out->outputs_per_block = static_cast<int32_t>(p.tile_elems);
+    out->device_threads = p.device_threads;
+    out->scratch_bytes = p.scratch_bytes;
+    out->load_bytes = p.vecio ? 16 : static_cast<int32_t>(argreduce::scan_elem_size(dtype));
+    out->dispatches = 1;
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_scan_lastaxis(const void* x, argreduce_dtype_t dtype, int64_t rows,
+                                             int64_t cols, argreduce_op_t op, void* out_values,
+                                             int64_t* out_idx, void* scratch,
+                                             size_t scratch_bytes, void* stream) {
+    const int64_t es = argreduce::scan_elem_size(dtype);
+    if (es == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
+    if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN) return ARGREDUCE_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 1) return ARGREDUCE_ERR_INVALID_ARG;
+    if (cols > std::numeric_limits<int32_t>::max()) return ARGREDUCE_ERR_TOO_WIDE;
+    if (rows == 0) return ARGREDUCE_OK;
+    if (x == nullptr || out_values == nullptr || out_idx == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t va = reinterpret_cast<uintptr_t>(out_values);
+    const uintptr_t ia = reinterpret_cast<uintptr_t>(out_idx);
+    if (xa % es != 0 || va % es != 0 || ia % 8 != 0) return ARGREDUCE_ERR_INVALID_ARG;
+    if (rows > std::numeric_limits<int64_t>::max() / (cols * 8)) return ARGREDUCE_ERR_INVALID_ARG;
+    // the outputs must not overlap the input
+    const uintptr_t n = static_cast<uintptr_t>(rows) * static_cast<uintptr_t>(cols);
+    const auto overlap = [](uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) {
+        return a < b + bn && b < a + an;
+    };
+    if (overlap(xa, n * es, va, n * es) || overlap(xa, n * es, ia, n * 8) ||
+        overlap(va, n * es, ia, n * 8))
+        return ARGREDUCE_ERR_INVALID_ARG;
+    const bool aligned = xa % 16 == 0 && va % 16 == 0 && ia % 16 == 0;
+    ScanPlan p;
+    const int rc = argreduce::make_scan_plan(rows, cols, dtype, aligned, &p);
+    if (rc != ARGREDUCE_OK) return rc;
+    uint8_t* scratch16 = nullptr;
+    if (p.scratch_bytes > 0) {
+        if (scratch == nullptr || scratch_bytes < p.scratch_bytes)
+            return ARGREDUCE_ERR_SCRATCH_TOO_SMALL;
+        scratch16 = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(scratch) + 15u) &
+                                               ~static_cast<uintptr_t>(15u));
+    }
+    const hipError_t err = argreduce::launch_cum(p, x, dtype, op, out_values, out_idx, scratch16,
+                                                 static_cast<hipStream_t>(stream));
     return err == hipSuccess ? ARGREDUCE_OK : ARGREDUCE_ERR_HIP;
 }

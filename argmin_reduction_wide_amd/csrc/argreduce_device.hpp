@@ -116,6 +116,36 @@ struct F64 {
     }
 };
 
+// Integer formats (the cumulative scan): compared exactly in their own type.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef long i64x2 __attribute__((ext_vector_type(2)));
+
+struct I32 {
+    using C = int32_t;
+    using Vec = i32x4;
+    static constexpr int kSize = 4;
+    static constexpr int VW = 4;
+    __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const int32_t*>(p); }
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
+        e[0] = q.x;
+        e[1] = q.y;
+        e[2] = q.z;
+        e[3] = q.w;
+    }
+};
+
+struct I64 {
+    using C = int64_t;
+    using Vec = i64x2;
+    static constexpr int kSize = 8;
+    static constexpr int VW = 2;
+    __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const int64_t*>(p); }
+    __device__ static void unpack(const Vec q, C (&e)[VW]) {
+        e[0] = q.x;
+        e[1] = q.y;
+    }
+};
+
 // ---------------------------------------------------------------------------------------
 // (value, index) candidate.
 
@@ -189,6 +219,40 @@ struct Cand {
         const bool t = (kLast && oi == kNaN0Last) || better(ov, v) || (ov == v && tie_wins(oi, i));
         v = t ? ov : v;
         i = t ? oi : i;
+    }
+};
+
+// ---------------------------------------------------------------------------------------
+// Payload words of one published candidate: the index, then the value's 32-bit halves.
+template <typename C>
+struct Words;
+template <>
+struct Words<float> {
+    static constexpr int kWords = 2;
+    static constexpr int kStride = 2;
+    __device__ static void pack(float v, uint32_t i, uint32_t (&p)[2]) {
+        p[0] = i;
+        p[1] = __float_as_uint(v);
+    }
+    __device__ static void unpack(const uint32_t (&p)[2], float& v, uint32_t& i) {
+        i = p[0];
+        v = __uint_as_float(p[1]);
+    }
+};
+template <>
+struct Words<double> {
+    static constexpr int kWords = 3;
+    static constexpr int kStride = 4;
+    __device__ static void pack(double v, uint32_t i, uint32_t (&p)[3]) {
+        const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+        p[0] = i;
+        p[1] = static_cast<uint32_t>(b);
+        p[2] = static_cast<uint32_t>(b >> 32);
+    }
+    __device__ static void unpack(const uint32_t (&p)[3], double& v, uint32_t& i) {
+        i = p[0];
+        v = __longlong_as_double(
+            static_cast<long long>((static_cast<uint64_t>(p[2]) << 32) | p[1]));
     }
 };
 

@@ -39,6 +39,28 @@ struct AxisPlan {
     size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
 };
 
+// Cumulative extremum with indices (cummax / cummin) along the last axis.
+constexpr int kScanUnroll = 4;  // 16-byte chunks per lane per tile
+
+struct ScanPlan {
+    int64_t rows, cols;
+    int64_t tiles_per_row;   // T; > 1: tiles chained by look-back through scratch
+    int64_t tile_elems;      // 256 * kScanUnroll * VW
+    int64_t grid_blocks;     // rows * T
+    int vecio;               // 16-byte loads and stores of full chunks
+    size_t state_words;      // 64-bit scratch words of all tile states (0 if T == 1)
+    int64_t device_threads;
+    size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
+};
+
+// Enqueues the cumulative scan of `plan` on `stream` (and, when the stream is being
+// captured into a graph, a clear of the tile states before it).
+hipError_t launch_cum(const ScanPlan& plan, const void* x, int dtype, int op, void* out_val,
+                      int64_t* out_idx, uint8_t* scratch16, hipStream_t stream);
+
+// 64-bit scratch words of one tile's states (aggregate + inclusive prefix).
+size_t scan_state_words(int dtype);
+
 // Enqueues the middle-axis kernel of `plan` on `stream`.
 hipError_t launch_axis(const AxisPlan& plan, const void* x, int dtype, int op, int64_t* out,
                        uint8_t* scratch16, hipStream_t stream);

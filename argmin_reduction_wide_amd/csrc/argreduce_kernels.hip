@@ -43,43 +43,11 @@
 
 #include "argreduce_device.hpp"
 #include "argreduce_internal.hpp"
+#include "argreduce_launch.hpp"
 
 namespace argreduce {
 
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one slot before giving up (~1 s)
-
-// Payload words of one published candidate: the index, then the value's 32-bit halves.
-template <typename C>
-struct Words;
-template <>
-struct Words<float> {
-    static constexpr int kWords = 2;
-    static constexpr int kStride = 2;
-    __device__ static void pack(float v, uint32_t i, uint32_t (&p)[2]) {
-        p[0] = i;
-        p[1] = __float_as_uint(v);
-    }
-    __device__ static void unpack(const uint32_t (&p)[2], float& v, uint32_t& i) {
-        i = p[0];
-        v = __uint_as_float(p[1]);
-    }
-};
-template <>
-struct Words<double> {
-    static constexpr int kWords = 3;
-    static constexpr int kStride = 4;
-    __device__ static void pack(double v, uint32_t i, uint32_t (&p)[3]) {
-        const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
-        p[0] = i;
-        p[1] = static_cast<uint32_t>(b);
-        p[2] = static_cast<uint32_t>(b >> 32);
-    }
-    __device__ static void unpack(const uint32_t (&p)[3], double& v, uint32_t& i) {
-        i = p[0];
-        v = __longlong_as_double(
-            static_cast<long long>((static_cast<uint64_t>(p[2]) << 32) | p[1]));
-    }
-};
 
 template <typename Fmt, int OP, int G, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
@@ -404,11 +372,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
 
 __global__ void k_empty() {}
 
-namespace {
-
 std::atomic<uint32_t> g_nonce{0};
 
-// A fresh per-call nonce; never 0 (the value slots are reset to) nor 0xffffffff.
 uint32_t next_nonce() {
     uint32_t n;
     do {
@@ -420,17 +385,7 @@ uint32_t next_nonce() {
 std::atomic<hipEvent_t> g_ev_start{nullptr};
 std::atomic<hipEvent_t> g_ev_stop{nullptr};
 
-// Launch of a row-scanning kernel; with the measurement events set, the HIP extension
-// launch records them around the kernel on the same stream.
-template <typename... KArgs, typename... Args>
-void launch_scan(void (*kernel)(KArgs...), dim3 grid, hipStream_t s, Args... args) {
-    hipEvent_t e0 = g_ev_start.load(std::memory_order_relaxed);
-    hipEvent_t e1 = g_ev_stop.load(std::memory_order_relaxed);
-    if (e0 != nullptr && e1 != nullptr)
-        hipExtLaunchKernelGGL(kernel, grid, dim3(kBlockThreads), 0, s, e0, e1, 0, args...);
-    else
-        hipLaunchKernelGGL(kernel, grid, dim3(kBlockThreads), 0, s, args...);
-}
+namespace {
 
 template <typename Fmt, int OP, int G, int U>
 void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,

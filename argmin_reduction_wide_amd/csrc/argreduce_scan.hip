@@ -1,0 +1,560 @@
+// gfx950 kernels of the cumulative extremum with indices (cummax / cummin) along the last
+// axis, and their launchers.
+//
+// What is computed (the PaddlePaddle issue on the cummax/cummin CUDA kernel: its
+// reproduction measures cummax along the last axis, and its fix proposals describe the
+// operator as a (value, index) reduce with ArgMax semantics, ties to the earlier index):
+// every position j of a row reports the sequential ArgMax (cummax) / ArgMin (cummin) scan
+// of the prefix 0 .. j, i.e. the index the running best holds after element j and the
+// element stored there.
+//
+// The scan as an associative operator. Each element becomes a pair (value, position):
+// position 0 enters as (fix(x0), 0) with fix(NaN) = the op's absorbing value (+inf for
+// cummax) and, for a NaN, the marker index kNaN0, so that a leading NaN holds for the
+// whole row; an element that is NaN anywhere else enters with the op's identity value
+// (-inf for cummax), so it can never be taken. Two adjacent pieces a (earlier) and b
+// (later) combine to b when b's value is strictly better, else to a: the leftmost best
+// element, which is the sequential strict-compare scan. A piece with no elements is the
+// pair (identity, kEmpty) and combines as the identity.
+//
+// Layout of one call: a row is cut into tiles of 256 * U 16-byte chunks; workgroup g
+// takes tile g % T of row g / T (T tiles per row). Wave w of the workgroup owns U rows of
+// 64 consecutive chunks (one 16-byte vector per lane per row of chunks, so every load and
+// store of a wavefront is contiguous); it scans each row of chunks across its lanes on the
+// DPP crossbar (row shifts 1, 2, 4, 8, then the row broadcasts of lanes 15 and 31), carries
+// between its rows of chunks, and the four waves carry through LDS.
+//
+// Rows longer than one tile chain their tiles with a single-pass decoupled look-back
+// (Merrill and Garland's scheme, as cub's DeviceScan implements it): a tile publishes its
+// aggregate, then finds its exclusive prefix from the published states of the tiles
+// before it (64 at a time, one per lane of a wavefront: the nearest tile that has
+// published its inclusive prefix ends the walk, the aggregates of the tiles after it are
+// folded in), then publishes its inclusive prefix. The states are the same self-checking
+// words as the split ArgMax path: 64-bit agent-scope atomic stores of (nonce << 32) |
+// payload, one word per 32 bits of (index, value), each word validated on its own, so no
+// fence orders them. A fresh nonce per call makes earlier calls' words invalid; a call
+// captured into a HIP graph, whose nonce is fixed across replays, first clears its words
+// with a small kernel (a graph node, not a memset). Forward progress: a tile waits only
+// on tiles of lower workgroup id, which were dispatched before it and publish their
+// aggregate without waiting; the wait is bounded all the same (indices -1 on a timeout,
+// never expected).
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <limits>
+#include <type_traits>
+
+#include "argreduce_device.hpp"
+#include "argreduce_internal.hpp"
+#include "argreduce_launch.hpp"
+
+namespace argreduce {
+namespace {
+
+constexpr uint32_t kEmpty = 0xffffffffu;  // index of the empty piece
+constexpr uint32_t kNaN0 = 0x7fffffffu;   // index of a leading NaN (reported as 0)
+constexpr uint32_t kFail = 0xfffffffeu;   // published by a tile whose look-back timed out
+constexpr uint32_t kScanSpinLimit = 1u << 20;
+
+// Storage bits of an output value, per format.
+template <typename Fmt>
+struct Out;
+template <>
+struct Out<F32> {
+    using S = uint32_t;
+    __device__ static S bits(float v) { return __float_as_uint(v); }
+};
+template <>
+struct Out<F16> {
+    using S = uint16_t;
+    __device__ static S bits(float v) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v)); }
+};
+template <>
+struct Out<BF16> {
+    using S = uint16_t;
+    // the value was widened from bfloat16, so its low 16 bits are zero
+    __device__ static S bits(float v) { return static_cast<uint16_t>(__float_as_uint(v) >> 16); }
+};
+template <>
+struct Out<F64> {
+    using S = uint64_t;
+    __device__ static S bits(double v) { return static_cast<uint64_t>(__double_as_longlong(v)); }
+};
+template <>
+struct Out<I32> {
+    using S = uint32_t;
+    __device__ static S bits(int32_t v) { return static_cast<uint32_t>(v); }
+};
+template <>
+struct Out<I64> {
+    using S = uint64_t;
+    __device__ static S bits(int64_t v) { return static_cast<uint64_t>(v); }
+};
+
+// The operator on (value, index) pairs.
+template <typename C, int OP>
+struct ScanOp {
+    static constexpr bool kMaxOp = op_is_max(OP);
+    __device__ static C identity() {
+        if constexpr (std::is_floating_point<C>::value)
+            return kMaxOp ? -__builtin_huge_val() : __builtin_huge_val();
+        else
+            return kMaxOp ? std::numeric_limits<C>::min() : std::numeric_limits<C>::max();
+    }
+    __device__ static C absorbing() {
+        return kMaxOp ? __builtin_huge_val() : -__builtin_huge_val();
+    }
+    __device__ static bool is_nan(C a) {
+        if constexpr (std::is_floating_point<C>::value)
+            return a != a;
+        else
+            return false;
+    }
+    __device__ static bool better(C a, C b) { return kMaxOp ? (a > b) : (a < b); }
+    // (av, ai) := (av, ai) then (bv, bi): the later piece wins only when strictly better.
+    __device__ static void combine(C& av, uint32_t& ai, C bv, uint32_t bi) {
+        const bool t = (ai == kEmpty) || better(bv, av);
+        av = t ? bv : av;
+        ai = t ? bi : ai;
+    }
+    // The one-element piece of element e at position p.
+    __device__ static void single(C e, uint32_t p, C& v, uint32_t& i) {
+        const bool nan = is_nan(e);
+        if constexpr (std::is_floating_point<C>::value) {
+            v = p == 0 ? (nan ? absorbing() : e) : (nan ? identity() : e);
+            i = (p == 0 && nan) ? kNaN0 : p;
+        } else {
+            v = e;
+            i = p;
+        }
+    }
+};
+
+// 32-bit word access to values for the cross-lane moves.
+template <typename C>
+__device__ inline uint32_t lo_word(C v) {
+    if constexpr (sizeof(C) == 4)
+        return __builtin_bit_cast(uint32_t, v);
+    else
+        return static_cast<uint32_t>(__builtin_bit_cast(uint64_t, v));
+}
+template <typename C>
+__device__ inline uint32_t hi_word(C v) {
+    if constexpr (sizeof(C) == 4)
+        return 0u;
+    else
+        return static_cast<uint32_t>(__builtin_bit_cast(uint64_t, v) >> 32);
+}
+template <typename C>
+__device__ inline C from_words(uint32_t lo, uint32_t hi) {
+    if constexpr (sizeof(C) == 4)
+        return __builtin_bit_cast(C, lo);
+    else
+        return __builtin_bit_cast(C, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// DPP move with an explicit value for lanes that get no source.
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp_or(uint32_t old, uint32_t src) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(old), static_cast<int>(src), CTRL, ROW_MASK, 0xf, false));
+}
+
+// One step of the wavefront's inclusive scan: take the piece of the source lane (the empty
+// piece where there is none) as the earlier operand.
+template <int CTRL, int ROW_MASK, typename C, int OP>
+__device__ inline void scan_dpp_step(C& v, uint32_t& i) {
+    using Op = ScanOp<C, OP>;
+    const C id = Op::identity();
+    C lv = from_words<C>(dpp_or<CTRL, ROW_MASK>(lo_word(id), lo_word(v)),
+                         sizeof(C) == 8 ? dpp_or<CTRL, ROW_MASK>(hi_word(id), hi_word(v)) : 0u);
+    uint32_t li = dpp_or<CTRL, ROW_MASK>(kEmpty, i);
+    Op::combine(lv, li, v, i);
+    v = lv;
+    i = li;
+}
+
+// Inclusive scan over the 64 lanes of a wavefront, in lane order.
+template <typename C, int OP>
+__device__ inline void wave_scan(C& v, uint32_t& i) {
+    scan_dpp_step<0x111, 0xf, C, OP>(v, i);  // row_shr:1
+    scan_dpp_step<0x112, 0xf, C, OP>(v, i);  // row_shr:2
+    scan_dpp_step<0x114, 0xf, C, OP>(v, i);  // row_shr:4
+    scan_dpp_step<0x118, 0xf, C, OP>(v, i);  // row_shr:8
+    scan_dpp_step<0x142, 0xa, C, OP>(v, i);  // row_bcast:15 into rows 1 and 3
+    scan_dpp_step<0x143, 0xc, C, OP>(v, i);  // row_bcast:31 into rows 2 and 3
+}
+
+template <typename C>
+__device__ inline C shfl_val(C v, int src) {
+    const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(lo_word(v)), src));
+    const uint32_t hi = sizeof(C) == 8 ? static_cast<uint32_t>(__shfl(static_cast<int>(hi_word(v)), src)) : 0u;
+    return from_words<C>(lo, hi);
+}
+template <typename C>
+__device__ inline C readlane_val(C v, int lane) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo_word(v)), lane));
+    const uint32_t hi = sizeof(C) == 8
+                            ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi_word(v)), lane))
+                            : 0u;
+    return from_words<C>(lo, hi);
+}
+
+// Published tile state: (nonce << 32) | payload words: the index, then the value's 32-bit
+// halves. 2 words for 32-bit values, 3 for 64-bit ones (stride 4).
+template <typename C>
+struct StateWords {
+    static constexpr int kWords = sizeof(C) == 8 ? 3 : 2;
+    static constexpr int kStride = sizeof(C) == 8 ? 4 : 2;
+};
+
+template <typename C>
+__device__ inline void publish(uint64_t* w, uint32_t nonce, C v, uint32_t i) {
+    const uint64_t tag = static_cast<uint64_t>(nonce) << 32;
+    __hip_atomic_store(&w[0], tag | i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&w[1], tag | lo_word(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (sizeof(C) == 8)
+        __hip_atomic_store(&w[2], tag | hi_word(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reads a published state; true when every word carries this call's nonce.
+template <typename C>
+__device__ inline bool read_state(const uint64_t* w, uint32_t nonce, C& v, uint32_t& i) {
+    const uint64_t w0 = __hip_atomic_load(&w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w1 = __hip_atomic_load(&w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t w2 = 0;
+    if constexpr (sizeof(C) == 8)
+        w2 = __hip_atomic_load(&w[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = (w0 >> 32) == nonce && (w1 >> 32) == nonce;
+    if constexpr (sizeof(C) == 8) ok = ok && (w2 >> 32) == nonce;
+    i = static_cast<uint32_t>(w0);
+    v = from_words<C>(static_cast<uint32_t>(w1), static_cast<uint32_t>(w2));
+    return ok;
+}
+
+// Exclusive prefix of tile t (>= 1) of a row whose tile states start at `row_states`:
+// decoupled look-back by one wavefront. Uniform result in every lane of the calling wave.
+template <typename C, int OP>
+__device__ inline bool look_back(const uint64_t* row_states, uint32_t t, uint32_t nonce, C& accv,
+                                 uint32_t& acci) {
+    using Op = ScanOp<C, OP>;
+    using SW = StateWords<C>;
+    const uint32_t lane = threadIdx.x % kWave;
+    accv = Op::identity();
+    acci = kEmpty;
+    int64_t hi = static_cast<int64_t>(t) - 1;  // nearest tile not folded in yet
+    for (;;) {
+        const int64_t j = hi - lane;
+        C v = Op::identity();
+        uint32_t i = kEmpty;
+        bool inc = j < 0;  // before the row start: an empty inclusive prefix
+        bool agg = false;
+        uint64_t mask_inc = 0;
+        uint32_t spins = 0;
+        for (;;) {
+            if (!inc && !agg) {
+                const uint64_t* st = row_states + static_cast<size_t>(j) * 2 * SW::kStride;
+                C pv;
+                uint32_t pi;
+                if (read_state(st + SW::kStride, nonce, pv, pi)) {  // inclusive prefix
+                    inc = true;
+                    v = pv;
+                    i = pi;
+                } else if (read_state(st, nonce, pv, pi)) {  // aggregate
+                    agg = true;
+                    v = pv;
+                    i = pi;
+                }
+            }
+            mask_inc = __ballot(inc);
+            const int lp = mask_inc ? __ffsll(static_cast<unsigned long long>(mask_inc)) - 1 : kWave;
+            // decidable when every lane before the nearest inclusive prefix has its aggregate
+            const bool need = static_cast<int>(lane) < lp;
+            if (__ballot(need && !agg) == 0) break;
+            if (++spins > kScanSpinLimit) return false;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const int lp = mask_inc ? __ffsll(static_cast<unsigned long long>(mask_inc)) - 1 : kWave;
+        // a predecessor that failed makes this tile fail too, rather than use its state
+        if (__ballot(static_cast<int>(lane) <= lp && i == kFail) != 0) return false;
+        if (lp < kWave) {  // lanes past the nearest inclusive prefix repeat it (idempotent)
+            const C pv = readlane_val(v, lp);
+            const uint32_t pi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(i), lp));
+            if (static_cast<int>(lane) > lp) {
+                v = pv;
+                i = pi;
+            }
+        }
+        // ordered fold: lane l holds tile hi - l, so higher lanes are earlier tiles
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            C ov = shfl_val(v, static_cast<int>(lane) + off);
+            uint32_t oi = static_cast<uint32_t>(__shfl(static_cast<int>(i), static_cast<int>(lane) + off));
+            if (static_cast<int>(lane) + off < kWave) {
+                Op::combine(ov, oi, v, i);
+                v = ov;
+                i = oi;
+            }
+        }
+        C wv = readlane_val(v, 0);
+        uint32_t wi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(i), 0));
+        Op::combine(wv, wi, accv, acci);  // the window is earlier than what is folded so far
+        accv = wv;
+        acci = wi;
+        if (lp < kWave) return true;
+        hi -= kWave;
+    }
+}
+
+// One call: workgroup g scans tile g % T of row g / T. VECIO: rows start 16-byte aligned in
+// x and out_val (and out_idx), so full chunks move as 16-byte vectors.
+template <typename Fmt, int OP, int U, bool VECIO>
+__global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict__ x, uint32_t cols,
+                                                       uint32_t T, uint8_t* __restrict__ out_val,
+                                                       int64_t* __restrict__ out_idx,
+                                                       uint64_t* __restrict__ states, uint32_t nonce) {
+    using C = typename Fmt::C;
+    using Op = ScanOp<C, OP>;
+    using S = typename Out<Fmt>::S;
+    using SW = StateWords<C>;
+    constexpr int VW = Fmt::VW;
+    constexpr int kWaves = kBlockThreads / kWave;
+    constexpr uint32_t kTile = kBlockThreads * U * VW;  // elements per tile
+    __shared__ C s_v[kWaves + 1];
+    __shared__ uint32_t s_i[kWaves + 1];
+    __shared__ int s_fail;
+
+    const uint32_t g = blockIdx.x;
+    const uint32_t r = g / T;
+    const uint32_t t = g - r * T;
+    const uint32_t wave = threadIdx.x / kWave;
+    const uint32_t lane = threadIdx.x % kWave;
+    const size_t row_off = static_cast<size_t>(r) * cols;
+    const uint8_t* row = x + row_off * Fmt::kSize;
+    uint8_t* vrow = out_val + row_off * sizeof(S);
+    int64_t* irow = out_idx + row_off;
+    const uint32_t tile0 = t * kTile;
+    // first position of chunk u of this lane
+    auto chunk_pos = [&](int u) -> uint32_t {
+        return tile0 + ((wave * U + static_cast<uint32_t>(u)) * kWave + lane) * VW;
+    };
+    if (threadIdx.x == 0) s_fail = 0;
+
+    // load: U chunks of VW elements (positions past the row end are not read)
+    C e[U][VW];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t p0 = chunk_pos(u);
+        if (VECIO && p0 + VW <= cols) {
+            const typename Fmt::Vec q = __builtin_nontemporal_load(
+                reinterpret_cast<const typename Fmt::Vec*>(row + static_cast<size_t>(p0) * Fmt::kSize));
+            Fmt::unpack(q, e[u]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < VW; ++k)
+                e[u][k] = (p0 + k < cols) ? Fmt::load1(row + static_cast<size_t>(p0 + k) * Fmt::kSize)
+                                          : Op::identity();
+        }
+    }
+
+    // per chunk: the chunk's aggregate, then the wavefront's scan of the aggregates
+    C exv[U], cv[U];
+    uint32_t exi[U], ci[U];
+    C carry_v = Op::identity();
+    uint32_t carry_i = kEmpty;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t p0 = chunk_pos(u);
+        C av = Op::identity();
+        uint32_t ai = kEmpty;
+        if (p0 < cols) {
+            Op::single(e[u][0], p0, av, ai);
+#pragma unroll
+            for (int k = 1; k < VW; ++k) {
+                // strict update: NaN and the padding past the row end never win
+                const bool b = (p0 + k < cols) && Op::better(e[u][k], av);
+                av = b ? e[u][k] : av;
+                ai = b ? p0 + k : ai;
+            }
+        }
+        C iv = av;
+        uint32_t ii = ai;
+        wave_scan<C, OP>(iv, ii);
+        // exclusive: the inclusive piece of the previous lane
+        C pv = shfl_val(iv, static_cast<int>(lane) - 1);
+        uint32_t pi = static_cast<uint32_t>(__shfl(static_cast<int>(ii), static_cast<int>(lane) - 1));
+        exv[u] = lane == 0 ? Op::identity() : pv;
+        exi[u] = lane == 0 ? kEmpty : pi;
+        cv[u] = carry_v;  // carry into this row of chunks (uniform)
+        ci[u] = carry_i;
+        const C tv = readlane_val(iv, kWave - 1);
+        const uint32_t ti = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ii), kWave - 1));
+        Op::combine(carry_v, carry_i, tv, ti);
+    }
+
+    // waves: totals through LDS; s_v[kWaves] receives the tile's exclusive prefix
+    if (lane == 0) {
+        s_v[wave] = carry_v;
+        s_i[wave] = carry_i;
+    }
+    __syncthreads();
+    C wv = Op::identity();  // prefix of the earlier waves
+    uint32_t wi = kEmpty;
+    for (uint32_t w = 0; w < wave; ++w) Op::combine(wv, wi, s_v[w], s_i[w]);
+    if (T > 1 && wave == 0) {
+        C av = Op::identity();  // the tile's aggregate
+        uint32_t ai = kEmpty;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) Op::combine(av, ai, s_v[w], s_i[w]);
+        uint64_t* row_states = states + static_cast<size_t>(r) * T * 2 * SW::kStride;
+        uint64_t* mine = row_states + static_cast<size_t>(t) * 2 * SW::kStride;
+        C pv = Op::identity();
+        uint32_t pi = kEmpty;
+        bool ok = true;
+        if (t > 0) {
+            if (lane == 0) publish(mine, nonce, av, ai);  // aggregate
+            ok = look_back<C, OP>(row_states, t, nonce, pv, pi);
+        }
+        if (lane == 0) {
+            C incv = pv;
+            uint32_t inci = pi;
+            Op::combine(incv, inci, av, ai);
+            publish(mine + SW::kStride, nonce, incv, ok ? inci : kFail);  // inclusive prefix
+            s_v[kWaves] = pv;
+            s_i[kWaves] = pi;
+            if (!ok) s_fail = 1;
+        }
+    }
+    __syncthreads();
+    C tv = Op::identity();  // the tile's exclusive prefix, then this wave's
+    uint32_t ti = kEmpty;
+    if (T > 1) {
+        tv = s_v[kWaves];
+        ti = s_i[kWaves];
+    }
+    Op::combine(tv, ti, wv, wi);
+    const bool fail = s_fail != 0;
+    // x[0] of the row, for positions that report a leading NaN
+    S x0 = 0;
+    if constexpr (std::is_floating_point<C>::value) x0 = *reinterpret_cast<const S*>(row);
+
+    // outputs
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t p0 = chunk_pos(u);
+        if (p0 >= cols) continue;
+        C rv = tv;
+        uint32_t ri = ti;
+        Op::combine(rv, ri, cv[u], ci[u]);
+        Op::combine(rv, ri, exv[u], exi[u]);
+        C sv;
+        uint32_t si;
+        Op::single(e[u][0], p0, sv, si);
+        Op::combine(rv, ri, sv, si);
+        S ov[VW];
+        int64_t oi[VW];
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+            if (k > 0) {
+                const bool b = Op::better(e[u][k], rv);
+                rv = b ? e[u][k] : rv;
+                ri = b ? p0 + k : ri;
+            }
+            const bool nan0 = ri == kNaN0;
+            ov[k] = nan0 ? x0 : Out<Fmt>::bits(rv);
+            oi[k] = fail ? int64_t{-1} : (nan0 ? int64_t{0} : static_cast<int64_t>(ri));
+        }
+        if (VECIO && p0 + VW <= cols) {
+            u32x4 w;
+            __builtin_memcpy(&w, ov, 16);
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(vrow + static_cast<size_t>(p0) * sizeof(S)));
+#pragma unroll
+            for (int k = 0; k < VW; k += 2) {
+                i64x2 q;
+                q.x = oi[k];
+                q.y = oi[k + 1];
+                __builtin_nontemporal_store(q, reinterpret_cast<i64x2*>(irow + p0 + k));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VW; ++k) {
+                if (p0 + k < cols) {
+                    reinterpret_cast<S*>(vrow)[p0 + k] = ov[k];
+                    irow[p0 + k] = oi[k];
+                }
+            }
+        }
+    }
+}
+
+// Clears the tile states of a call captured into a graph (replays share one nonce).
+__global__ __launch_bounds__(kBlockThreads) void k_cum_clear(uint64_t* __restrict__ states,
+                                                             size_t words) {
+    for (size_t k = static_cast<size_t>(blockIdx.x) * kBlockThreads + threadIdx.x; k < words;
+         k += static_cast<size_t>(gridDim.x) * kBlockThreads)
+        states[k] = 0;
+}
+
+template <typename Fmt, int OP>
+hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_t* out_idx,
+                         uint8_t* scratch16, hipStream_t s) {
+    constexpr int U = kScanUnroll;
+    uint64_t* states = p.tiles_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
+    uint32_t nonce = 0;
+    if (states != nullptr) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) return hipErrorInvalidValue;
+        if (cs == hipStreamCaptureStatusActive) {
+            // replays of the graph repeat this nonce: clear the words before each replay
+            const size_t words = p.state_words;
+            const size_t blocks = (words + kBlockThreads - 1) / kBlockThreads;
+            hipLaunchKernelGGL(k_cum_clear, dim3(static_cast<uint32_t>(blocks < 1024 ? blocks : 1024)),
+                               dim3(kBlockThreads), 0, s, states, words);
+            nonce = 1u;
+        } else {
+            nonce = next_nonce();
+        }
+    }
+    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    uint8_t* vb = static_cast<uint8_t*>(out_val);
+    const uint32_t cols = static_cast<uint32_t>(p.cols);
+    const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
+    if (p.vecio)
+        launch_scan(k_cum<Fmt, OP, U, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+    else
+        launch_scan(k_cum<Fmt, OP, U, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+    return hipGetLastError();
+}
+
+template <typename Fmt>
+hipError_t launch_cum_fmt(const ScanPlan& p, const void* x, int op, void* out_val,
+                          int64_t* out_idx, uint8_t* scratch16, hipStream_t s) {
+    switch (op) {
+        case ARGREDUCE_MAX: return launch_cum_op<Fmt, kMax>(p, x, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_MIN: return launch_cum_op<Fmt, kMin>(p, x, out_val, out_idx, scratch16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cum(const ScanPlan& p, const void* x, int dtype, int op, void* out_val,
+                      int64_t* out_idx, uint8_t* scratch16, hipStream_t s) {
+    switch (dtype) {
+        case ARGREDUCE_F32: return launch_cum_fmt<F32>(p, x, op, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_F16: return launch_cum_fmt<F16>(p, x, op, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_BF16: return launch_cum_fmt<BF16>(p, x, op, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_F64: return launch_cum_fmt<F64>(p, x, op, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_I32: return launch_cum_fmt<I32>(p, x, op, out_val, out_idx, scratch16, s);
+        case ARGREDUCE_I64: return launch_cum_fmt<I64>(p, x, op, out_val, out_idx, scratch16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+size_t scan_state_words(int dtype) {
+    const bool wide = dtype == ARGREDUCE_F64 || dtype == ARGREDUCE_I64;
+    return 2 * static_cast<size_t>(wide ? StateWords<double>::kStride : StateWords<float>::kStride);
+}
+
+}  // namespace argreduce

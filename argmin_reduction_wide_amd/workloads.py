@@ -28,8 +28,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64}
-ITEMSIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "f64": np.float64,
+           "i32": np.int32, "i64": np.int64}
+ITEMSIZE = {"f32": 4, "f16": 2, "bf16": 2, "f64": 8, "i32": 4, "i64": 8}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -78,6 +79,9 @@ class Workload:
     # For a reduction over a middle axis: (outer, len, inner); data is then stored as
     # (outer, len * inner) and the reduced axis is `len`.
     axis_shape: tuple | None = None
+    # "argreduce" (ArgMax / ArgMin, one index per row) or "scan" (cummax / cummin: a value
+    # and an index per element)
+    kind: str = "argreduce"
 
     @property
     def rows(self) -> int:
@@ -248,6 +252,91 @@ def axis_few_outputs_f32(seed: int = 8, outer: int = 1, length: int = 1 << 20,
     )
 
 
+# ----------------------------------------------------------------------------------------
+# cummax / cummin workloads. The PaddlePaddle issue on the cummax/cummin kernel measures
+# [1, N] and [rows, 65536 / rows] int64 scans along the last axis (reproduction A, B), a
+# dtype table at [1, 65536] (F), and names its real use: cummax(is_boundary * positions)
+# over a [65536] int64 tensor in long-context pre-training (real impact). Its inputs are
+# arange tensors; seeded random values stand in here, so that ties, new extrema and (for
+# floats) both ops are exercised. The long row and the many-row shape are ours: they make
+# the scan bandwidth-bound.
+
+
+def scan_doc_starts_i64(seed: int = 9, n: int = 65536, mean_doc: int = 2048) -> Workload:
+    """cummax of is_boundary * positions over one [1, 65536] int64 row: each position gets
+    the start of its document. Boundaries: position 0 and a Bernoulli(1/mean_doc) draw at
+    every other position. Expected by construction: values = indices = the last boundary at
+    or before each position."""
+    rng = np.random.default_rng(seed)
+    is_b = rng.random(n) < 1.0 / mean_doc
+    is_b[0] = True
+    x = (is_b.astype(np.int64) * np.arange(n, dtype=np.int64))[None, :]
+    starts = np.flatnonzero(is_b)
+    return Workload(
+        name=f"cummax_i64_doc_starts_1x{n}", dtype="i64", ops=("max",), data=np.ascontiguousarray(x),
+        seed=seed, kind="scan", planted={"starts": starts},
+        recipe=f"is_boundary (position 0, then Bernoulli(1/{mean_doc})) * positions, int64",
+    )
+
+
+def scan_rows_i64(rows: int, cols: int, seed: int = 10) -> Workload:
+    """cummax / cummin int64 over [rows, cols] (65536 elements in the page's table):
+    uniform draws in [-2^62, 2^62)."""
+    rng = np.random.default_rng(seed + rows)
+    x = rng.integers(-(1 << 62), 1 << 62, size=(rows, cols), dtype=np.int64)
+    return Workload(name=f"cummax_cummin_i64_{rows}x{cols}", dtype="i64", ops=("max", "min"),
+                    data=np.ascontiguousarray(x), seed=seed + rows, kind="scan",
+                    recipe="uniform int64 in [-2^62, 2^62)")
+
+
+def scan_row_65536(dtype: str, seed: int = 11, n: int = 65536) -> Workload:
+    """cummax of one [1, 65536] row per format of the page's dtype table: N(0,1) for
+    floating point, uniform int32 for i32."""
+    rng = np.random.default_rng(seed)
+    if dtype == "i32":
+        x = rng.integers(np.iinfo(np.int32).min, np.iinfo(np.int32).max, size=(1, n),
+                         dtype=np.int32, endpoint=True)
+        recipe = "uniform int32"
+    else:
+        x = to_storage(rng.standard_normal((1, n)), dtype)
+        recipe = f"iid N(0,1) -> {dtype}"
+    return Workload(name=f"cummax_{dtype}_1x{n}", dtype=dtype, ops=("max",),
+                    data=np.ascontiguousarray(x), seed=seed, kind="scan", recipe=recipe)
+
+
+def scan_long_row_f32(seed: int = 12, n: int = 1 << 24) -> Workload:
+    """cummax / cummin f32 over one row of 2^24 elements (64 MiB in, 192 MiB out)."""
+    rng = np.random.default_rng(seed)
+    return Workload(name=f"cummax_cummin_f32_1x{n}", dtype="f32", ops=("max", "min"),
+                    data=to_storage(rng.standard_normal((1, n)), "f32"), seed=seed, kind="scan",
+                    recipe="iid N(0,1) -> f32")
+
+
+def scan_many_rows_f32(seed: int = 13, rows: int = 4096, cols: int = 4096) -> Workload:
+    """cummax f32 over [4096, 4096]: one tile per row, no look-back."""
+    rng = np.random.default_rng(seed)
+    return Workload(name=f"cummax_f32_{rows}x{cols}", dtype="f32", ops=("max",),
+                    data=to_storage(rng.standard_normal((rows, cols)), "f32"), seed=seed,
+                    kind="scan", recipe="iid N(0,1) -> f32")
+
+
+def random_int_rows(rng: np.random.Generator, rows: int, cols: int, dtype: str, kind: str) -> np.ndarray:
+    """A (rows, cols) int32 / int64 array: "ties" (values in [-3, 3]), "full" (the whole
+    range, extremes included) or "constant"."""
+    t = STORAGE[dtype]
+    info = np.iinfo(t)
+    if kind == "ties":
+        return rng.integers(-3, 4, size=(rows, cols)).astype(t)
+    if kind == "full":
+        v = rng.integers(info.min, info.max, size=(rows, cols), dtype=t, endpoint=True)
+        ext = rng.random((rows, cols)) < 0.01
+        v[ext] = np.where(rng.random(int(ext.sum())) < 0.5, info.min, info.max).astype(t)
+        return v
+    if kind == "constant":
+        return np.repeat(rng.integers(info.min, info.max, size=(rows, 1), dtype=t), cols, axis=1)
+    raise KeyError(kind)
+
+
 def config_workloads(which: str) -> list[Workload]:
     """The workload(s) of one named configuration, at full size."""
     if which == "c1":
@@ -264,6 +353,10 @@ def config_workloads(which: str) -> list[Workload]:
         return [c5b_narrow_rows_f16()]
     if which == "axis":
         return [axis_many_outputs_f32(), axis_few_outputs_f32()]
+    if which == "scan":
+        return ([scan_doc_starts_i64()] + [scan_rows_i64(r, 65536 // r) for r in (1, 4, 64, 1024)]
+                + [scan_row_65536(d) for d in ("i32", "f32", "f64")]
+                + [scan_long_row_f32(), scan_many_rows_f32()])
     raise KeyError(which)
 
 

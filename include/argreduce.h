@@ -46,7 +46,11 @@ typedef enum {
     ARGREDUCE_F32 = 0,  /* IEEE binary32, 4-byte aligned */
     ARGREDUCE_F16 = 1,  /* IEEE binary16, 2-byte aligned */
     ARGREDUCE_BF16 = 2, /* bfloat16 (upper half of a binary32), 2-byte aligned */
-    ARGREDUCE_F64 = 3   /* IEEE binary64, 8-byte aligned */
+    ARGREDUCE_F64 = 3,  /* IEEE binary64, 8-byte aligned */
+    /* Integer formats: accepted by argreduce_scan_lastaxis only (the other entry points
+     * return ARGREDUCE_ERR_UNSUPPORTED_DTYPE); compared exactly. */
+    ARGREDUCE_I32 = 4,  /* int32, 4-byte aligned */
+    ARGREDUCE_I64 = 5   /* int64, 8-byte aligned */
 } argreduce_dtype_t;
 
 typedef enum {
@@ -122,8 +126,10 @@ typedef enum {
     ARGREDUCE_PATH_SUBWAVE = 0, /* a group of 1..64 lanes of one wavefront per row */
     ARGREDUCE_PATH_BLOCK = 1,   /* one workgroup per row, rows looped over the grid */
     ARGREDUCE_PATH_SPLIT = 2,   /* several workgroups per row; the highest-id one merges */
-    ARGREDUCE_PATH_AXIS = 3     /* middle-axis reduction: a tile of consecutive outputs per
+    ARGREDUCE_PATH_AXIS = 3,    /* middle-axis reduction: a tile of consecutive outputs per
                                    workgroup, thread rows along the axis (argreduce_axis) */
+    ARGREDUCE_PATH_SCAN = 4     /* cumulative scan: a tile of a row per workgroup, tiles of
+                                   a row chained by look-back (argreduce_scan_lastaxis) */
 } argreduce_path_t;
 
 typedef struct {
@@ -189,6 +195,46 @@ int argreduce_axis(const void *x, argreduce_dtype_t dtype, int64_t outer, int64_
 int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inner, argreduce_dtype_t dtype,
                         argreduce_plan_t *plan);
 
+/* ----------------------------------------------------------------------------------------
+ * Cumulative extremum with indices along the last axis: cummax / cummin.
+ *
+ * The PaddlePaddle issue on the cummax/cummin CUDA kernel (its reproduction scans the last
+ * axis of [rows, cols] tensors; its fix proposals describe the operator as a (value,
+ * index) reduce with ArgMax semantics, ties to the earlier index). For every row r and
+ * position j:
+ *   out_idx[r*cols + j]    = the index the ArgMax (op ARGREDUCE_MAX: cummax) / ArgMin
+ *                            (ARGREDUCE_MIN: cummin) scan of x[r][0..j] returns, with the
+ *                            semantics of argreduce_lastaxis: ties keep the earlier index,
+ *                            a NaN after position 0 is never taken, a NaN at position 0
+ *                            holds for the whole row (index 0);
+ *   out_values[r*cols + j] = a copy of the element x[r][out_idx[r*cols + j]] (same format
+ *                            and bits as x; a leading NaN keeps its own bit pattern).
+ *
+ *   Formats: F32, F16, BF16, F64, I32, I64 (integers compared exactly). Ops: ARGREDUCE_MAX
+ *   and ARGREDUCE_MIN only. 1 <= cols <= INT32_MAX, rows >= 0 (0 is a no-op). x and
+ *   out_values aligned to the element size, out_idx to 8 bytes; 16-byte aligned rows
+ *   (x, out_values and out_idx 16-byte aligned and cols * element size a multiple of 16)
+ *   move as 16-byte vectors. out_values and out_idx hold rows * cols elements each and must
+ *   not overlap x.
+ *
+ *   Scratch: rows longer than one tile (argreduce_scan_plan's outputs_per_block elements)
+ *   chain their tiles through per-tile state words in scratch (any contents on entry);
+ *   argreduce_scan_scratch_bytes gives the size (0 when every row fits in one tile;
+ *   SIZE_MAX for invalid arguments). One dispatch per call; when `stream` is being
+ *   captured into a HIP graph, a small kernel that clears the state words is enqueued
+ *   before it, so that graph replays stay correct. Status codes as argreduce_lastaxis;
+ *   ARGREDUCE_ERR_TOO_WIDE also when rows * tiles per row exceeds 2^32 - 1.
+ */
+size_t argreduce_scan_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dtype);
+int argreduce_scan_lastaxis(const void *x, argreduce_dtype_t dtype, int64_t rows, int64_t cols,
+                            argreduce_op_t op, void *out_values, int64_t *out_idx,
+                            void *scratch, size_t scratch_bytes, void *stream);
+/* The plan argreduce_scan_lastaxis would use for 16-byte aligned buffers (path
+ * ARGREDUCE_PATH_SCAN; blocks_per_row = tiles per row, outputs_per_block = elements per
+ * tile). */
+int argreduce_scan_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype,
+                        argreduce_plan_t *plan);
+
 /* Measurement hook: the launch floor. Enqueues one empty kernel (one workgroup of 64
  * threads) on `stream`, the same way argreduce_lastaxis enqueues its kernels, so that a
  * benchmark can time bare launch latency in the same harness ("[CUDA] Parallelize
@@ -196,8 +242,8 @@ int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inner, argreduce_dty
  * launch). Returns ARGREDUCE_OK or ARGREDUCE_ERR_HIP. */
 int argreduce_debug_launch_empty(void *stream);
 
-/* Measurement hook: when both are non-NULL, every later argreduce_lastaxis call launches
- * its row-scanning kernel (not the counter reset) with `start` recorded just before and
+/* Measurement hook: when both are non-NULL, every later call launches its main kernel
+ * (not a merge or clear kernel) with `start` recorded just before and
  * `stop` just after it on the same stream (hipEvent_t values created by the caller with
  * timing enabled); NULL, NULL turns this off. Process-wide; for benchmarks only. */
 int argreduce_debug_set_kernel_events(void *start, void *stop);

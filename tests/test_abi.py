@@ -225,3 +225,61 @@ def test_axis_scratch_too_small(mi355x):
     aligned = B.argreduce_axis_plan(1, 1 << 20, 32, B.F32)["scratch_bytes"]
     assert 0 < aligned <= need
     assert B.argreduce_axis(FAKE, B.F32, 1, 1 << 20, 32, B.MAX, FAKE, FAKE, aligned - 1, 0) == -4
+
+
+# cumulative scan (cummax / cummin)
+
+
+@pytest.mark.parametrize("dtype,rows,cols,op,code", [
+    (9, 2, 8, B.MAX, -2), (B.F32, 2, 8, B.MAX_LAST, -1), (B.F32, 2, 8, 7, -1),
+    (B.F32, 2, 0, B.MAX, -1), (B.F32, -1, 8, B.MAX, -1), (B.I64, 1, INT32_MAX + 1, B.MAX, -3),
+])
+def test_scan_invalid_arguments(lib, dtype, rows, cols, op, code):
+    assert B.argreduce_scan_lastaxis(FAKE, dtype, rows, cols, op, FAKE * 4, FAKE * 8, 0, 0, 0) == code
+
+
+def test_scan_pointer_checks(lib):
+    x, v, i = FAKE, FAKE * 4, FAKE * 8
+    assert B.argreduce_scan_lastaxis(0, B.F32, 0, 8, B.MAX, 0, 0, 0, 0, 0) == 0  # no rows
+    assert B.argreduce_scan_lastaxis(0, B.F32, 2, 8, B.MAX, v, i, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, 0, i, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, v, 0, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x + 2, B.F32, 2, 8, B.MAX, v, i, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.I64, 2, 8, B.MAX, v + 4, i, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, v, i + 4, 0, 0, 0) == -1
+    # outputs overlapping the input or each other
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, x + 32, i, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, v, x + 8, 0, 0, 0) == -1
+    assert B.argreduce_scan_lastaxis(x, B.F32, 2, 8, B.MAX, v, v + 16, 0, 0, 0) == -1
+
+
+def test_other_entry_points_refuse_integers(lib):
+    for dt in (B.I32, B.I64):
+        assert B.argreduce_lastaxis(FAKE, dt, 2, 8, B.MAX, FAKE, 0, 0, 0) == -2
+        assert B.argreduce_axis(FAKE, dt, 2, 8, 3, B.MAX, FAKE, 0, 0, 0) == -2
+        assert B.argreduce_scratch_bytes(2, 8, dt) == B.SIZE_MAX
+
+
+def test_scan_plans_and_scratch(mi355x):
+    # tiles: 256 lanes x 4 chunks of 16 bytes
+    p = B.argreduce_scan_plan(1, 65536, B.I64)
+    assert p["path"] == B.PATH_SCAN and p["outputs_per_block"] == 2048
+    assert p["blocks_per_row"] == 32 and p["grid_blocks"] == 32 and p["load_bytes"] == 16
+    assert p["scratch_bytes"] == 15 + 32 * 2 * 4 * 8  # aggregate + prefix, 4 words each
+    assert B.argreduce_scan_scratch_bytes(1, 65536, B.I64) == p["scratch_bytes"]
+    p = B.argreduce_scan_plan(4096, 4096, B.F32)  # one tile per row: no look-back, no scratch
+    assert p["blocks_per_row"] == 1 and p["grid_blocks"] == 4096 and p["scratch_bytes"] == 0
+    p = B.argreduce_scan_plan(3, 8193, B.F16)
+    assert p["outputs_per_block"] == 8192 and p["blocks_per_row"] == 2 and p["load_bytes"] == 2
+    assert p["scratch_bytes"] == 15 + 3 * 2 * 2 * 2 * 8
+    assert B.argreduce_scan_plan(2, 1 << 24, B.F32)["blocks_per_row"] == 4096
+    assert B.argreduce_scan_scratch_bytes(2, 0, B.F32) == B.SIZE_MAX
+    assert B.argreduce_scan_scratch_bytes(2, 8, 9) == B.SIZE_MAX
+
+
+def test_scan_scratch_too_small(mi355x):
+    need = B.argreduce_scan_scratch_bytes(1, 65536, B.I64)
+    assert B.argreduce_scan_lastaxis(FAKE, B.I64, 1, 65536, B.MAX, FAKE * 4, FAKE * 8, FAKE,
+                                     need - 1, 0) == -4
+    assert B.argreduce_scan_lastaxis(FAKE, B.I64, 1, 65536, B.MAX, FAKE * 4, FAKE * 8, 0,
+                                     need, 0) == -4

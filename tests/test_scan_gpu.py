@@ -1,0 +1,205 @@
+"""GPU parity of cummax / cummin with indices: the HIP library against the CPU oracle, bit for
+bit (values as storage bits, int64 indices).
+
+Covers row lengths around the tile size and the look-back window (64 tiles), many rows,
+every format (f32, f16, bf16, f64, i32, i64), special values (NaN anywhere, +-inf, +-0,
+subnormals, integer extremes), aligned and misaligned buffers, dirty scratch, the page's
+workloads at full size, HIP graph capture with replays on new inputs, and the torch
+wrapper. Each case is printed before it runs.
+"""
+import numpy as np
+import pytest
+
+import argmin_reduction_wide_amd.binding as B
+from argmin_reduction_wide_amd import workloads as W
+from gpu_helpers import announce, to_device
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "f16", "bf16", "f64", "i32", "i64")
+OPS = ("max", "min")
+INTS = ("i32", "i64")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU; none is visible"
+    B.argreduce_debug_set_capacity(0)
+    B.argreduce_debug_force_path(B.PATH_AUTO)
+
+
+def storage_of(t, dtype: str) -> np.ndarray:
+    import torch
+
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view({2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
+
+
+def inputs(rng, rows: int, cols: int, dtype: str, kind: str) -> np.ndarray:
+    if dtype in INTS:
+        return W.random_int_rows(rng, rows, cols, dtype, {"ties": "ties", "special": "full",
+                                                          "mixed": "full", "constant": "constant",
+                                                          "normal": "full"}[kind])
+    return W.random_rows(rng, rows, cols, dtype, kind)
+
+
+def run_scan(arr: np.ndarray, dtype: str, op: str, offset: int = 0, dirty: bool = False,
+             scratch_offset: int = 0, scratch=None):
+    """Call argreduce_scan_lastaxis; returns (status, values storage array, int64 indices)."""
+    import torch
+
+    rows, cols = arr.shape
+    t = to_device(arr, dtype, offset)
+    vals = torch.empty_like(t)
+    if offset:  # misaligned outputs too
+        vbuf = torch.empty(t.numel() + offset, dtype=t.dtype, device="cuda")
+        vals = vbuf[offset:].view(t.shape)
+    idx = torch.full((rows, cols), -7, dtype=torch.int64, device="cuda")
+    need = B.argreduce_scan_scratch_bytes(rows, cols, dtype)
+    assert need != B.SIZE_MAX
+    if scratch is None:
+        scratch = torch.empty(max(need + scratch_offset, 1), dtype=torch.uint8, device="cuda")
+    if dirty and need:
+        scratch.copy_(torch.randint(0, 256, scratch.shape, dtype=torch.uint8, device="cuda"))
+    rc = B.argreduce_scan_lastaxis(t.data_ptr(), dtype, rows, cols, op, vals.data_ptr(),
+                                   idx.data_ptr(), scratch.data_ptr() + scratch_offset, need,
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return rc, storage_of(vals, dtype), idx.cpu().numpy()
+
+
+def check_scan(oracle_lib, arr: np.ndarray, dtype: str, op: str, what: str, **kw):
+    rows, cols = arr.shape
+    announce(f"scan {what} dtype={dtype} op={op} shape={arr.shape} {kw} plan="
+             f"{B.argreduce_scan_plan(rows, cols, dtype)}")
+    rc, got_v, got_i = run_scan(arr, dtype, op, **kw)
+    assert rc == 0, f"{what}: status {rc}"
+    want_v, want_i = oracle_lib.cumulative(arr, dtype, op)
+    bad = np.argwhere(got_i != want_i)
+    assert bad.size == 0, (f"{what} {dtype} {op} {arr.shape}: {len(bad)} indices differ; first "
+                           f"{tuple(bad[0])}: got {got_i[tuple(bad[0])]}, oracle {want_i[tuple(bad[0])]}")
+    badv = np.argwhere(bits(got_v) != bits(want_v))
+    assert badv.size == 0, (f"{what} {dtype} {op} {arr.shape}: {len(badv)} values differ; first "
+                            f"{tuple(badv[0])}")
+    return got_v, got_i
+
+
+# rows of 1 .. several tiles (a tile is 4096 f32 / 8192 f16 / 2048 64-bit elements), row
+# lengths that are not multiples of a 16-byte chunk, and rows of more than 64 tiles (a
+# second look-back window)
+SHAPES = [(1, 1), (1, 7), (3, 5), (2, 100), (4, 2047), (2, 2048), (3, 2049), (1, 4095),
+          (2, 4096), (1, 4097), (2, 8191), (1, 8193), (1, 20000), (3, 65536), (1, 140001)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_scan_shapes_all_ops(oracle_lib, dtype):
+    rng = np.random.default_rng(700 + DTYPES.index(dtype))
+    for rows, cols in SHAPES:
+        for kind in ("ties", "mixed"):
+            arr = inputs(rng, rows, cols, dtype, kind)
+            for op in OPS:
+                check_scan(oracle_lib, arr, dtype, op, f"shape kind={kind}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_scan_special_values_and_offsets(oracle_lib, dtype):
+    """Special-value alphabet (NaN first or anywhere, +-inf, +-0, subnormals; integer
+    extremes), constant rows; buffers 16-byte aligned and misaligned by one element; state
+    words dirty on entry and at a 16-byte-unaligned scratch offset."""
+    rng = np.random.default_rng(800 + DTYPES.index(dtype))
+    for rows, cols in [(5, 33), (2, 5000), (1, 70000), (64, 96)]:
+        for kind in ("special", "constant"):
+            arr = inputs(rng, rows, cols, dtype, kind)
+            if dtype not in INTS and kind == "special":
+                arr[0, 0] = W.to_storage(np.array([np.nan]), dtype)[0]  # a leading NaN row
+            for op in OPS:
+                for offset in (0, 1):
+                    check_scan(oracle_lib, arr, dtype, op, f"special kind={kind}", offset=offset,
+                               dirty=True, scratch_offset=3)
+
+
+def test_scan_long_rows_many_windows(oracle_lib):
+    """Rows of several hundred tiles: the look-back folds many 64-tile windows of
+    aggregates when the nearer tiles have not published their prefixes yet."""
+    rng = np.random.default_rng(901)
+    for dtype, cols in (("f32", 3 << 20), ("i64", 1 << 20), ("f16", 5 << 20)):
+        arr = inputs(rng, 1, cols, dtype, "ties")
+        for op in OPS:
+            check_scan(oracle_lib, arr, dtype, op, "long row")
+
+
+def test_scan_workloads_full_size(oracle_lib):
+    for w in W.config_workloads("scan"):
+        for op in w.ops:
+            got_v, got_i = check_scan(oracle_lib, w.data, w.dtype, op, f"workload {w.name}")
+            if "starts" in w.planted:  # known by construction: the start of each document
+                want = np.zeros(w.cols, dtype=np.int64)
+                for s in w.planted["starts"]:
+                    want[s:] = s
+                assert np.array_equal(got_i[0], want) and np.array_equal(got_v[0], want)
+
+
+def test_scan_graph_capture_replays(oracle_lib):
+    """A captured call (its tile states cleared by a kernel node) replayed on new inputs."""
+    import torch
+
+    rng = np.random.default_rng(902)
+    for dtype, rows, cols in (("f32", 1, 100000), ("i64", 3, 9000), ("bf16", 2, 30000)):
+        announce(f"scan graph dtype={dtype} shape=({rows},{cols})")
+        first = inputs(rng, rows, cols, dtype, "ties")
+        x = to_device(first, dtype)
+        vals = torch.empty_like(x)
+        idx = torch.empty((rows, cols), dtype=torch.int64, device="cuda")
+        need = B.argreduce_scan_scratch_bytes(rows, cols, dtype)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                rc = B.argreduce_scan_lastaxis(x.data_ptr(), dtype, rows, cols, "max",
+                                               vals.data_ptr(), idx.data_ptr(), scratch.data_ptr(),
+                                               need, s.cuda_stream)
+        assert rc == 0
+        for rep in range(4):
+            arr = inputs(rng, rows, cols, dtype, "ties" if rep % 2 else "mixed")
+            x.copy_(to_device(arr, dtype))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            want_v, want_i = oracle_lib.cumulative(arr, dtype, "max")
+            assert np.array_equal(idx.cpu().numpy(), want_i), (dtype, rep)
+            assert np.array_equal(bits(storage_of(vals, dtype)), bits(want_v)), (dtype, rep)
+            # an eager call in between, on the same scratch
+            rc, _, got_i = run_scan(arr, dtype, "min", scratch=scratch)
+            assert rc == 0 and np.array_equal(got_i, oracle_lib.cumulative(arr, dtype, "min")[1])
+
+
+def test_scan_torch_wrapper(oracle_lib):
+    import torch
+
+    import argmin_reduction_wide_amd as ar
+
+    rng = np.random.default_rng(903)
+    arr = W.random_rows(rng, 6, 5000, "f32", "ties")
+    t = to_device(arr, "f32").view(2, 3, 5000)
+    announce("scan torch wrapper cummax / cummin on [2,3,5000]")
+    v, i = ar.cummax(t)
+    want_v, want_i = oracle_lib.cumulative(arr, "f32", "max")
+    assert v.shape == t.shape and i.dtype == torch.int64
+    assert np.array_equal(i.reshape(6, 5000).cpu().numpy(), want_i)
+    assert np.array_equal(v.reshape(6, 5000).cpu().numpy(), want_v)
+    v, i = ar.cummin(t, dim=2)
+    assert np.array_equal(i.reshape(6, 5000).cpu().numpy(), oracle_lib.cumulative(arr, "f32", "min")[1])
+    with pytest.raises(ValueError):
+        ar.cummax(t, dim=1)
+    ti = torch.arange(65536, device="cuda", dtype=torch.int64)
+    v, i = ar.cummax(ti)
+    assert torch.equal(v, ti) and torch.equal(i, ti)
