@@ -284,7 +284,10 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
     *p = ScanPlan{};
     p->rows = rows;
     p->cols = cols;
-    p->tile_elems = kBlock * kScanUnroll * (16 / es);
+    // U = 8 only for rows of many U = 4 tiles (there the look-back's depth matters; with a
+    // few tiles per row, the smaller tile keeps more workgroups in flight)
+    p->unroll = cols <= 64 * kBlock * kScanUnrollShort * (16 / es) ? kScanUnrollShort : kScanUnrollLong;
+    p->tile_elems = kBlock * p->unroll * (16 / es);
     p->tiles_per_row = ceil_div(cols, p->tile_elems);
     if (rows > 0 && rows > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / p->tiles_per_row)
         return ARGREDUCE_ERR_TOO_WIDE;
@@ -461,7 +464,7 @@ ARGREDUCE_EXPORT int argreduce_scan_plan(int64_t rows, int64_t cols, argreduce_d
     out->block_threads = static_cast<int32_t>(argreduce::kBlock);
     out->grid_blocks = p.grid_blocks;
     out->grid_rows = rows;
-    out->unroll = argreduce::kScanUnroll;
+    out->unroll = p.unroll;
     out->outputs_per_block = static_cast<int32_t>(p.tile_elems);
     out->device_threads = p.device_threads;
     out->scratch_bytes = p.scratch_bytes;

@@ -40,12 +40,16 @@ struct AxisPlan {
 };
 
 // Cumulative extremum with indices (cummax / cummin) along the last axis.
-constexpr int kScanUnroll = 4;  // 16-byte chunks per lane per tile
+// 16-byte chunks per lane per tile: 4, or 8 for rows of more than 64 such tiles (bigger
+// tiles: fewer tiles for the look-back to walk through).
+constexpr int kScanUnrollShort = 4;
+constexpr int kScanUnrollLong = 8;
 
 struct ScanPlan {
     int64_t rows, cols;
     int64_t tiles_per_row;   // T; > 1: tiles chained by look-back through scratch
-    int64_t tile_elems;      // 256 * kScanUnroll * VW
+    int unroll;              // chunks per lane per tile (U)
+    int64_t tile_elems;      // 256 * U * VW
     int64_t grid_blocks;     // rows * T
     int vecio;               // 16-byte loads and stores of full chunks
     size_t state_words;      // 64-bit scratch words of all tile states (0 if T == 1)

@@ -29,7 +29,10 @@
 // aggregate, then finds its exclusive prefix from the published states of the tiles
 // before it (64 at a time, one per lane of a wavefront: the nearest tile that has
 // published its inclusive prefix ends the walk, the aggregates of the tiles after it are
-// folded in), then publishes its inclusive prefix. The states are the same self-checking
+// folded in), then publishes its inclusive prefix. Inclusive prefixes travel back one
+// window per round of polls, so the window (and the tile size) sets the rate of a long
+// row's first tiles. Wider windows (several tiles per lane) measured slower: every poll
+// round then reads several times more state words. The states are the same self-checking
 // words as the split ArgMax path: 64-bit agent-scope atomic stores of (nonce << 32) |
 // payload, one word per 32 bits of (index, value), each word validated on its own, so no
 // fence orders them. A fresh nonce per call makes earlier calls' words invalid; a call
@@ -55,6 +58,7 @@ constexpr uint32_t kEmpty = 0xffffffffu;  // index of the empty piece
 constexpr uint32_t kNaN0 = 0x7fffffffu;   // index of a leading NaN (reported as 0)
 constexpr uint32_t kFail = 0xfffffffeu;   // published by a tile whose look-back timed out
 constexpr uint32_t kScanSpinLimit = 1u << 20;
+constexpr int kLookBackTiles = 1;  // tiles per lane of the look-back window
 
 // Storage bits of an output value, per format.
 template <typename Fmt>
@@ -233,8 +237,11 @@ __device__ inline bool read_state(const uint64_t* w, uint32_t nonce, C& v, uint3
 }
 
 // Exclusive prefix of tile t (>= 1) of a row whose tile states start at `row_states`:
-// decoupled look-back by one wavefront. Uniform result in every lane of the calling wave.
-template <typename C, int OP>
+// decoupled look-back by one wavefront, K tiles per lane (a window of 64 * K tiles per
+// round of polls; lane l looks at tiles hi - l * K - k, k = 0 the nearest). The walk ends
+// at the nearest tile that has published its inclusive prefix; every nearer tile must have
+// published its aggregate. The uniform result is in every lane of the calling wave.
+template <typename C, int OP, int K>
 __device__ inline bool look_back(const uint64_t* row_states, uint32_t t, uint32_t nonce, C& accv,
                                  uint32_t& acci) {
     using Op = ScanOp<C, OP>;
@@ -244,65 +251,98 @@ __device__ inline bool look_back(const uint64_t* row_states, uint32_t t, uint32_
     acci = kEmpty;
     int64_t hi = static_cast<int64_t>(t) - 1;  // nearest tile not folded in yet
     for (;;) {
-        const int64_t j = hi - lane;
-        C v = Op::identity();
-        uint32_t i = kEmpty;
-        bool inc = j < 0;  // before the row start: an empty inclusive prefix
-        bool agg = false;
-        uint64_t mask_inc = 0;
+        C v[K];
+        uint32_t i[K];
+        int st[K];  // 0: nothing published yet, 1: aggregate, 2: inclusive prefix
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            v[k] = Op::identity();
+            i[k] = kEmpty;
+            // before the row start: an empty inclusive prefix
+            st[k] = hi - static_cast<int64_t>(lane) * K - k < 0 ? 2 : 0;
+        }
+        int fk = K;  // this lane's nearest inclusive prefix (K: none)
+        int lp = kWave;
         uint32_t spins = 0;
         for (;;) {
-            if (!inc && !agg) {
-                const uint64_t* st = row_states + static_cast<size_t>(j) * 2 * SW::kStride;
-                C pv;
-                uint32_t pi;
-                if (read_state(st + SW::kStride, nonce, pv, pi)) {  // inclusive prefix
-                    inc = true;
-                    v = pv;
-                    i = pi;
-                } else if (read_state(st, nonce, pv, pi)) {  // aggregate
-                    agg = true;
-                    v = pv;
-                    i = pi;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                if (st[k] != 0) continue;
+                const int64_t j = hi - static_cast<int64_t>(lane) * K - k;
+                const uint64_t* w = row_states + static_cast<size_t>(j) * 2 * SW::kStride;
+                // both states are read in one round trip (not the aggregate after the prefix)
+                C pv, av;
+                uint32_t pi, ai;
+                const bool has_p = read_state(w + SW::kStride, nonce, pv, pi);  // inclusive prefix
+                const bool has_a = read_state(w, nonce, av, ai);                // aggregate
+                if (has_p) {
+                    st[k] = 2;
+                    v[k] = pv;
+                    i[k] = pi;
+                } else if (has_a) {
+                    st[k] = 1;
+                    v[k] = av;
+                    i[k] = ai;
                 }
             }
-            mask_inc = __ballot(inc);
-            const int lp = mask_inc ? __ffsll(static_cast<unsigned long long>(mask_inc)) - 1 : kWave;
-            // decidable when every lane before the nearest inclusive prefix has its aggregate
-            const bool need = static_cast<int>(lane) < lp;
-            if (__ballot(need && !agg) == 0) break;
+            fk = K;
+            bool ready = true;  // every tile nearer than fk has its aggregate
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k)
+                if (st[k] == 2) fk = k;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (k < fk && st[k] == 0) ready = false;
+            const uint64_t mask = __ballot(fk < K);
+            lp = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : kWave;
+            if (__ballot(static_cast<int>(lane) <= lp && !ready) == 0) break;
             if (++spins > kScanSpinLimit) return false;
             __builtin_amdgcn_s_sleep(2);
         }
-        const int lp = mask_inc ? __ffsll(static_cast<unsigned long long>(mask_inc)) - 1 : kWave;
         // a predecessor that failed makes this tile fail too, rather than use its state
-        if (__ballot(static_cast<int>(lane) <= lp && i == kFail) != 0) return false;
-        if (lp < kWave) {  // lanes past the nearest inclusive prefix repeat it (idempotent)
-            const C pv = readlane_val(v, lp);
-            const uint32_t pi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(i), lp));
-            if (static_cast<int>(lane) > lp) {
-                v = pv;
-                i = pi;
+        bool failed = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (k <= fk && i[k] == kFail) failed = true;
+        if (__ballot(static_cast<int>(lane) <= lp && failed) != 0) return false;
+        // the lane's piece: its tiles from the inclusive prefix (or the farthest) to the nearest
+        C lv = Op::identity();
+        uint32_t li = kEmpty;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {
+            if (k == fk) {
+                lv = v[k];
+                li = i[k];
+            } else if (k < fk) {
+                Op::combine(lv, li, v[k], i[k]);
             }
         }
-        // ordered fold: lane l holds tile hi - l, so higher lanes are earlier tiles
+        if (lp < kWave) {  // lanes past the nearest inclusive prefix repeat it (idempotent)
+            const C pv = readlane_val(lv, lp);
+            const uint32_t pi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(li), lp));
+            if (static_cast<int>(lane) > lp) {
+                lv = pv;
+                li = pi;
+            }
+        }
+        // ordered fold: higher lanes hold earlier tiles
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
-            C ov = shfl_val(v, static_cast<int>(lane) + off);
-            uint32_t oi = static_cast<uint32_t>(__shfl(static_cast<int>(i), static_cast<int>(lane) + off));
+            C ov = shfl_val(lv, static_cast<int>(lane) + off);
+            uint32_t oi = static_cast<uint32_t>(__shfl(static_cast<int>(li), static_cast<int>(lane) + off));
             if (static_cast<int>(lane) + off < kWave) {
-                Op::combine(ov, oi, v, i);
-                v = ov;
-                i = oi;
+                Op::combine(ov, oi, lv, li);
+                lv = ov;
+                li = oi;
             }
         }
-        C wv = readlane_val(v, 0);
-        uint32_t wi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(i), 0));
+        C wv = readlane_val(lv, 0);
+        uint32_t wi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(li), 0));
         Op::combine(wv, wi, accv, acci);  // the window is earlier than what is folded so far
         accv = wv;
         acci = wi;
         if (lp < kWave) return true;
-        hi -= kWave;
+        hi -= static_cast<int64_t>(kWave) * K;
     }
 }
 
@@ -323,6 +363,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
     __shared__ C s_v[kWaves + 1];
     __shared__ uint32_t s_i[kWaves + 1];
     __shared__ int s_fail;
+    __shared__ int32_t s_x[kWaves][kWave * VW];  // one wavefront's indices of a row of chunks
 
     const uint32_t g = blockIdx.x;
     const uint32_t r = g / T;
@@ -340,20 +381,28 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
     };
     if (threadIdx.x == 0) s_fail = 0;
 
-    // load: U chunks of VW elements (positions past the row end are not read)
-    C e[U][VW];
+    // load: U chunks of VW elements, kept as raw 16-byte vectors (half the registers of
+    // widened values for 2-byte formats) and unpacked where used. No load sits under a lane
+    // condition (that would make it a branch, and the loads would wait on each other):
+    // positions past the row end read the row's last chunk / element again, and every use
+    // of them is guarded.
+    using Vec = typename Fmt::Vec;
+    Vec q[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t p0 = chunk_pos(u);
-        if (VECIO && p0 + VW <= cols) {
-            const typename Fmt::Vec q = __builtin_nontemporal_load(
-                reinterpret_cast<const typename Fmt::Vec*>(row + static_cast<size_t>(p0) * Fmt::kSize));
-            Fmt::unpack(q, e[u]);
+        if constexpr (VECIO) {  // cols is a multiple of VW: chunks are whole or past the end
+            const uint32_t pc = p0 < cols ? p0 : cols - VW;
+            q[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const Vec*>(row + static_cast<size_t>(pc) * Fmt::kSize));
         } else {
+            S raw[VW];
 #pragma unroll
-            for (int k = 0; k < VW; ++k)
-                e[u][k] = (p0 + k < cols) ? Fmt::load1(row + static_cast<size_t>(p0 + k) * Fmt::kSize)
-                                          : Op::identity();
+            for (int k = 0; k < VW; ++k) {
+                const uint32_t pk = p0 + k < cols ? p0 + k : cols - 1;
+                raw[k] = *reinterpret_cast<const S*>(row + static_cast<size_t>(pk) * Fmt::kSize);
+            }
+            __builtin_memcpy(&q[u], raw, sizeof(Vec));
         }
     }
 
@@ -368,12 +417,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
         C av = Op::identity();
         uint32_t ai = kEmpty;
         if (p0 < cols) {
-            Op::single(e[u][0], p0, av, ai);
+            C e[VW];
+            Fmt::unpack(q[u], e);
+            Op::single(e[0], p0, av, ai);
 #pragma unroll
             for (int k = 1; k < VW; ++k) {
-                // strict update: NaN and the padding past the row end never win
-                const bool b = (p0 + k < cols) && Op::better(e[u][k], av);
-                av = b ? e[u][k] : av;
+                // strict update: NaN never wins; the padding past the row end is skipped
+                const bool b = (p0 + k < cols) && Op::better(e[k], av);
+                av = b ? e[k] : av;
                 ai = b ? p0 + k : ai;
             }
         }
@@ -413,7 +464,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
         bool ok = true;
         if (t > 0) {
             if (lane == 0) publish(mine, nonce, av, ai);  // aggregate
-            ok = look_back<C, OP>(row_states, t, nonce, pv, pi);
+            ok = look_back<C, OP, kLookBackTiles>(row_states, t, nonce, pv, pi);
         }
         if (lane == 0) {
             C incv = pv;
@@ -442,39 +493,59 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t p0 = chunk_pos(u);
-        if (p0 >= cols) continue;
+        const uint32_t ubase = p0 - lane * VW;  // first position of this row of chunks
+        if (ubase >= cols) continue;            // uniform in the wavefront
         C rv = tv;
         uint32_t ri = ti;
         Op::combine(rv, ri, cv[u], ci[u]);
         Op::combine(rv, ri, exv[u], exi[u]);
+        // with the long tiles, an opaque copy keeps the compiler from holding the first
+        // pass's widened values live until here (it unpacks again: a few cheap instructions)
+        Vec qu = q[u];
+        if constexpr (U > kScanUnrollShort) asm volatile("" : "+v"(qu));
+        C e[VW];
+        Fmt::unpack(qu, e);
         C sv;
         uint32_t si;
-        Op::single(e[u][0], p0, sv, si);
+        Op::single(e[0], p0, sv, si);
         Op::combine(rv, ri, sv, si);
         S ov[VW];
-        int64_t oi[VW];
+        int32_t oi[VW];  // positions < 2^31 (or -1)
 #pragma unroll
         for (int k = 0; k < VW; ++k) {
             if (k > 0) {
-                const bool b = Op::better(e[u][k], rv);
-                rv = b ? e[u][k] : rv;
+                const bool b = (VECIO || p0 + k < cols) && Op::better(e[k], rv);
+                rv = b ? e[k] : rv;
                 ri = b ? p0 + k : ri;
             }
             const bool nan0 = ri == kNaN0;
             ov[k] = nan0 ? x0 : Out<Fmt>::bits(rv);
-            oi[k] = fail ? int64_t{-1} : (nan0 ? int64_t{0} : static_cast<int64_t>(ri));
+            oi[k] = fail ? -1 : (nan0 ? 0 : static_cast<int32_t>(ri));
         }
-        if (VECIO && p0 + VW <= cols) {
-            u32x4 w;
-            __builtin_memcpy(&w, ov, 16);
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(vrow + static_cast<size_t>(p0) * sizeof(S)));
-#pragma unroll
-            for (int k = 0; k < VW; k += 2) {
-                i64x2 q;
-                q.x = oi[k];
-                q.y = oi[k + 1];
-                __builtin_nontemporal_store(q, reinterpret_cast<i64x2*>(irow + p0 + k));
+        if (VECIO) {
+            if (p0 < cols) {  // with VECIO, cols is a multiple of VW: the chunk is whole
+                u32x4 w;
+                __builtin_memcpy(&w, ov, 16);
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(vrow + static_cast<size_t>(p0) * sizeof(S)));
             }
+            // Indices: VW * 8 bytes per lane. Stored lane by lane, a wavefront's 16-byte
+            // stores would hit memory VW * 8 bytes apart and leave every line partly
+            // written per store; so they pass through LDS and leave transposed, each
+            // store of the wavefront covering 1 KiB (two consecutive indices per lane).
+#pragma unroll
+            for (int k = 0; k < VW; ++k) s_x[wave][lane * VW + k] = oi[k];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+            for (int q = 0; q < VW / 2; ++q) {
+                const uint32_t pos = static_cast<uint32_t>(q) * 2 * kWave + 2 * lane;
+                if (ubase + pos < cols) {  // cols is even: the pair is whole
+                    i64x2 pair;
+                    pair.x = s_x[wave][pos];
+                    pair.y = s_x[wave][pos + 1];
+                    __builtin_nontemporal_store(pair, reinterpret_cast<i64x2*>(irow + ubase + pos));
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         } else {
 #pragma unroll
             for (int k = 0; k < VW; ++k) {
@@ -498,7 +569,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum_clear(uint64_t* __restric
 template <typename Fmt, int OP>
 hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_t* out_idx,
                          uint8_t* scratch16, hipStream_t s) {
-    constexpr int U = kScanUnroll;
     uint64_t* states = p.tiles_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
     uint32_t nonce = 0;
     if (states != nullptr) {
@@ -520,10 +590,15 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     uint8_t* vb = static_cast<uint8_t*>(out_val);
     const uint32_t cols = static_cast<uint32_t>(p.cols);
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
-    if (p.vecio)
-        launch_scan(k_cum<Fmt, OP, U, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+    constexpr int US = kScanUnrollShort, UL = kScanUnrollLong;
+    if (p.unroll == US && p.vecio)
+        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+    else if (p.unroll == US)
+        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+    else if (p.vecio)
+        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
     else
-        launch_scan(k_cum<Fmt, OP, U, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
     return hipGetLastError();
 }
 

@@ -10,10 +10,10 @@ enqueues), on inputs already resident in HBM.
 Timing: W untimed warm-up calls, then exactly K calls between two HIP events on the stream
 the library launches on, synchronised on both sides; the inputs rotate through copies that
 together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeats one
-buffer and is reported beside it). Every call is exactly one launch of one kernel, so the
-timed region divided by K is that kernel's average launch duration; the roofline uses it.
-HIP events recorded around the kernel alone (the library's measurement hook) give a second
-view, reported as kernel_event_us. The launch floor is an empty kernel launched the same
+buffer and is reported beside it). The timed region divided by K is the per-call time
+(`value`). HIP events recorded around the main kernel of each call (the library's
+measurement hook) give that kernel's own per-launch duration, `kernel_event_us`, which the
+roofline divides into the algorithmic bytes. The launch floor is an empty kernel launched the same
 way. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this host
 on a bounded sample of calls of the same workload.
 
@@ -39,6 +39,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 KERNEL_SOURCES = ("argmin_reduction_wide_amd/csrc/argreduce_kernels.hip",
+                  "argmin_reduction_wide_amd/csrc/argreduce_scan.hip",
+                  "argmin_reduction_wide_amd/csrc/argreduce_launch.hpp",
                   "argmin_reduction_wide_amd/csrc/argreduce_device.hpp",
                   "argmin_reduction_wide_amd/csrc/argreduce_api.cpp",
                   "argmin_reduction_wide_amd/csrc/argreduce_internal.hpp",
@@ -48,11 +50,6 @@ ROTATE_BYTES = 1 << 29  # 512 MiB of rotated inputs, twice the Infinity Cache
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
-
-
-def algorithmic_bytes(rows: int, cols: int, itemsize: int) -> int:
-    """Input read once plus one int64 index written per row."""
-    return rows * cols * itemsize + rows * 8
 
 
 class Case:
@@ -67,7 +64,7 @@ class Case:
         self.w, self.op, self.B = w, op, B
         self.rows, self.cols = w.rows, w.cols
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "f64": torch.float64}[w.dtype]
+               "f64": torch.float64, "i32": torch.int32, "i64": torch.int64}[w.dtype]
         flat = w.data.reshape(-1)
         host = (torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
                 if w.dtype == "bf16" else torch.from_numpy(flat.copy()))
@@ -80,7 +77,15 @@ class Case:
         self.stream = torch.cuda.current_stream().cuda_stream
         self.dt = B.DTYPE_NAMES[w.dtype]
         self.opc = B.OP_NAMES[op]
-        if w.axis_shape is None:
+        self.vals = None
+        if w.kind == "scan":
+            n_out = self.rows * self.cols
+            self.shape = (self.rows, self.cols)
+            self.need = B.argreduce_scan_scratch_bytes(self.rows, self.cols, w.dtype)
+            self.fn = B.lib().argreduce_scan_lastaxis
+            self.plan = B.argreduce_scan_plan(self.rows, self.cols, w.dtype)
+            self.vals = torch.empty((self.rows, self.cols), dtype=tdt, device="cuda")
+        elif w.axis_shape is None:
             n_out = self.rows
             self.shape = (self.rows, self.cols)
             self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
@@ -95,11 +100,17 @@ class Case:
             self.plan = B.argreduce_axis_plan(outer, length, inner, w.dtype)
         self.out = torch.empty(n_out, dtype=torch.int64, device="cuda")
         self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
-        self.bytes = w.nbytes + n_out * 8  # input read once, one int64 per output
+        # input read once, one int64 per output (and, for a scan, one value per element)
+        self.bytes = w.nbytes + n_out * 8 + (w.nbytes if self.vals is not None else 0)
 
     def call(self, i: int) -> None:
-        rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
-                     self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
+        if self.vals is not None:
+            rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
+                         self.vals.data_ptr(), self.out.data_ptr(), self.scratch.data_ptr(),
+                         self.need, self.stream)
+        else:
+            rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
+                         self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
         if rc != 0:
             raise RuntimeError(f"argreduce call failed with status {rc}")
 
@@ -225,7 +236,7 @@ def roofline(bytes_per_call: int, kernel_us: float, workload: str = "") -> dict:
 
 def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     c = Case(w, op)
-    log(f"[bench] {w.name} arg{op}: plan {c.plan}, {c.n_rot} rotated copies")
+    log(f"[bench] {w.name} {op}: plan {c.plan}, {c.n_rot} rotated copies")
     us = c.timed(steps, warmup, rotate=True)
     hot = c.timed(steps, warmup // 4 + 1, rotate=False)
     kus = c.kernel_timed(min(steps, 1000))
@@ -334,7 +345,7 @@ def main() -> int:
 
     extra = []
     if args.all:
-        for name in W.CONFIG_NAMES + ("axis",):
+        for name in W.CONFIG_NAMES + ("axis", "scan"):
             for w in W.config_workloads(name):
                 for op in w.ops:
                     r = measure(w, op, max(200, args.steps // 4), args.warmup // 4 + 1, graph=False)

@@ -91,9 +91,9 @@ def check_scan(oracle_lib, arr: np.ndarray, dtype: str, op: str, what: str, **kw
     return got_v, got_i
 
 
-# rows of 1 .. several tiles (a tile is 4096 f32 / 8192 f16 / 2048 64-bit elements), row
-# lengths that are not multiples of a 16-byte chunk, and rows of more than 64 tiles (a
-# second look-back window)
+# rows of 1 .. several tiles (a tile is 4096 f32 / 8192 f16 / 2048 64-bit elements, twice
+# that for rows of more than 64 such tiles), row lengths that are not multiples of a
+# 16-byte chunk
 SHAPES = [(1, 1), (1, 7), (3, 5), (2, 100), (4, 2047), (2, 2048), (3, 2049), (1, 4095),
           (2, 4096), (1, 4097), (2, 8191), (1, 8193), (1, 20000), (3, 65536), (1, 140001)]
 
@@ -114,7 +114,7 @@ def test_scan_special_values_and_offsets(oracle_lib, dtype):
     extremes), constant rows; buffers 16-byte aligned and misaligned by one element; state
     words dirty on entry and at a 16-byte-unaligned scratch offset."""
     rng = np.random.default_rng(800 + DTYPES.index(dtype))
-    for rows, cols in [(5, 33), (2, 5000), (1, 70000), (64, 96)]:
+    for rows, cols in [(5, 33), (2, 5000), (1, 70000), (64, 96), (1, 600001)]:
         for kind in ("special", "constant"):
             arr = inputs(rng, rows, cols, dtype, kind)
             if dtype not in INTS and kind == "special":
@@ -126,10 +126,10 @@ def test_scan_special_values_and_offsets(oracle_lib, dtype):
 
 
 def test_scan_long_rows_many_windows(oracle_lib):
-    """Rows of several hundred tiles: the look-back folds many 64-tile windows of
+    """Rows of several hundred tiles: the look-back folds several 256-tile windows of
     aggregates when the nearer tiles have not published their prefixes yet."""
     rng = np.random.default_rng(901)
-    for dtype, cols in (("f32", 3 << 20), ("i64", 1 << 20), ("f16", 5 << 20)):
+    for dtype, cols in (("f32", 3 << 20), ("i64", 1 << 20), ("f16", 5 << 20), ("f32", 9 << 20)):
         arr = inputs(rng, 1, cols, dtype, "ties")
         for op in OPS:
             check_scan(oracle_lib, arr, dtype, op, "long row")
