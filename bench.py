@@ -263,8 +263,9 @@ COPY_BYTES = 256 << 20
 
 def pmc_pass() -> int:
     """Fixed kernel sequence for counter collection: a device-to-device copy of COPY_BYTES
-    (the calibration: it reads and writes exactly that many bytes), then 100 calls of the
-    [1,202048] and [4096,4096] fp32 ArgMax workloads on rotated inputs."""
+    (the calibration: it reads and writes exactly that many bytes), then 100 calls each of
+    the [1,202048] and [4096,4096] fp32 ArgMax workloads, the [64,4096,256] middle-axis
+    ArgMax and the [4096,4096] and [1,2^24] fp32 cummax workloads, on rotated inputs."""
     import torch
 
     from argmin_reduction_wide_amd import workloads as W
@@ -277,7 +278,8 @@ def pmc_pass() -> int:
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    for w in (W.c2_row202048_f32(), W.c4_square_f32_f64("f32")):
+    for w in (W.c2_row202048_f32(), W.c4_square_f32_f64("f32"), W.axis_many_outputs_f32(),
+              W.scan_many_rows_f32(), W.scan_long_row_f32()):
         c = Case(w, "max")
         for i in range(100):
             c.call(i)
