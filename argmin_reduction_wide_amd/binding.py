@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libargreduce.so")
 # enums of include/argreduce.h
 F32, F16, BF16, F64, I32, I64 = 0, 1, 2, 3, 4, 5
 MAX, MIN, MAX_LAST, MIN_LAST = 0, 1, 2, 3
-PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS, PATH_SCAN = -1, 0, 1, 2, 3, 4
+PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS, PATH_SCAN, PATH_WIDE = -1, 0, 1, 2, 3, 4, 5
 OK = 0
 ERRORS = {
     -1: "ARGREDUCE_ERR_INVALID_ARG",
@@ -37,7 +37,8 @@ EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_debug_set_capacity", "argreduce_debug_force_path",
            "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events",
            "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
-           "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan")
+           "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
+           "argreduce_debug_set_window")
 
 
 class ArgreduceError(RuntimeError):
@@ -52,7 +53,8 @@ class argreduce_plan_t(ctypes.Structure):
                 ("grid_blocks", ctypes.c_int64), ("grid_rows", ctypes.c_int64),
                 ("unroll", ctypes.c_int32), ("outputs_per_block", ctypes.c_int32),
                 ("device_threads", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t),
-                ("load_bytes", ctypes.c_int32), ("dispatches", ctypes.c_int32)]
+                ("load_bytes", ctypes.c_int32), ("dispatches", ctypes.c_int32),
+                ("window", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -104,6 +106,8 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_scan_lastaxis.restype = c_int
                 h.argreduce_scan_plan.argtypes = [i64, i64, c_int, ctypes.POINTER(argreduce_plan_t)]
                 h.argreduce_scan_plan.restype = c_int
+                h.argreduce_debug_set_window.argtypes = [i64]
+                h.argreduce_debug_set_window.restype = c_int
                 h.argreduce_debug_launch_empty.argtypes = [vp]
                 h.argreduce_debug_launch_empty.restype = c_int
                 h.argreduce_debug_set_kernel_events.argtypes = [vp, vp]
@@ -182,6 +186,10 @@ def argreduce_scan_plan(rows: int, cols: int, dtype) -> dict:
 
 def argreduce_debug_set_capacity(threads: int) -> int:
     return lib().argreduce_debug_set_capacity(threads)
+
+
+def argreduce_debug_set_window(elements: int) -> int:
+    return lib().argreduce_debug_set_window(elements)
 
 
 def argreduce_debug_force_path(path: int) -> int:

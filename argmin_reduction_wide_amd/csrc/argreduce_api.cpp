@@ -10,6 +10,7 @@
 // vector loads as the unit of work of a lane.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <limits>
 
@@ -49,6 +50,8 @@ constexpr int64_t kMaxUnrollBlocks = 8;
 std::atomic<int64_t> g_device_threads[kMaxDevices];
 std::atomic<int64_t> g_capacity_override{0};
 std::atomic<int> g_force_path{ARGREDUCE_PATH_AUTO};
+std::atomic<int64_t> g_window{0};
+constexpr int64_t kMaxWindow = int64_t{1} << 30;
 
 int64_t elem_size(int dtype) {
     switch (dtype) {
@@ -98,9 +101,42 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int check_shape(int64_t rows, int64_t cols, int dtype) {
     if (elem_size(dtype) == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
     if (rows < 0 || cols < 1) return ARGREDUCE_ERR_INVALID_ARG;
-    if (cols > std::numeric_limits<int32_t>::max()) return ARGREDUCE_ERR_TOO_WIDE;
-    if (rows > std::numeric_limits<int64_t>::max() / (cols * elem_size(dtype)))
+    // rows * cols * element size must fit in int64 (cols * 8 cannot overflow first)
+    if (cols > std::numeric_limits<int64_t>::max() / 8 ||
+        rows > std::numeric_limits<int64_t>::max() / (cols * elem_size(dtype)))
         return ARGREDUCE_ERR_INVALID_ARG;
+    return ARGREDUCE_OK;
+}
+
+// Window plan of rows wider than INT32_MAX (or of any row when the path is forced).
+int make_wide_plan(int64_t rows, int64_t cols, int dtype, int64_t cap, Plan* p) {
+    const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
+    const int64_t rows1 = rows > 0 ? rows : 1;
+    int64_t W = g_window.load(std::memory_order_relaxed);
+    if (W <= 0) {
+        // about one resident workgroup per window over the device, in whole 4096-element
+        // blocks, at most 2^30 elements (positions inside a window stay 32-bit)
+        const int64_t per_row = cap_blocks / rows1 > 0 ? cap_blocks / rows1 : 1;
+        W = ceil_div(ceil_div(cols, per_row), 4096) * 4096;
+        W = W < kMaxWindow ? W : kMaxWindow;
+    }
+    const int64_t G = ceil_div(cols, W);
+    if (rows1 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / G)
+        return ARGREDUCE_ERR_TOO_WIDE;
+    *p = Plan{};
+    p->path = ARGREDUCE_PATH_WIDE;
+    p->block_threads = static_cast<int>(kBlock);
+    p->device_threads = cap;
+    p->window = W;
+    p->windows = G;
+    p->blocks_per_row = static_cast<int>(G < std::numeric_limits<int>::max() ? G : std::numeric_limits<int>::max());
+    p->lanes_per_row = static_cast<int>(std::min<int64_t>(G * kBlock, std::numeric_limits<int>::max()));
+    // 8 vectors per lane per step once a window spans many steps of 256 lanes
+    p->unroll = W * elem_size(dtype) >= kBlock * 16 * 8 ? 8 : 2;
+    p->grid_rows = rows1;
+    p->grid_blocks = rows1 * G;
+    p->entry_bytes = wide_partial_bytes(dtype);
+    p->scratch_bytes = 15 + static_cast<size_t>(rows1) * static_cast<size_t>(G) * p->entry_bytes;
     return ARGREDUCE_OK;
 }
 
@@ -110,6 +146,10 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     int64_t cap = 0;
     rc = device_threads(&cap);
     if (rc != ARGREDUCE_OK) return rc;
+
+    if (cols > std::numeric_limits<int32_t>::max() ||
+        g_force_path.load(std::memory_order_relaxed) == ARGREDUCE_PATH_WIDE)
+        return make_wide_plan(rows, cols, dtype, cap, p);
 
     const int64_t vec_row = ceil_div(cols * elem_size(dtype), 16);  // 16-byte vectors per row
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
@@ -260,7 +300,8 @@ void fill_plan(const Plan& p, argreduce_plan_t* out) {
     out->device_threads = p.device_threads;
     out->scratch_bytes = p.scratch_bytes;
     out->load_bytes = 16;
-    out->dispatches = 1;
+    out->dispatches = p.path == ARGREDUCE_PATH_WIDE ? 2 : 1;
+    out->window = p.path == ARGREDUCE_PATH_WIDE ? p.window : 0;
 }
 
 // Cumulative scan: every format, integers included.
@@ -361,8 +402,15 @@ ARGREDUCE_EXPORT int argreduce_debug_set_capacity(int64_t threads) {
     return ARGREDUCE_OK;
 }
 
+ARGREDUCE_EXPORT int argreduce_debug_set_window(int64_t elements) {
+    if (elements < 0 || elements > argreduce::kMaxWindow) return ARGREDUCE_ERR_INVALID_ARG;
+    argreduce::g_window.store(elements, std::memory_order_relaxed);
+    return ARGREDUCE_OK;
+}
+
 ARGREDUCE_EXPORT int argreduce_debug_force_path(int path) {
-    if (path < ARGREDUCE_PATH_AUTO || path > ARGREDUCE_PATH_SPLIT) return ARGREDUCE_ERR_INVALID_ARG;
+    if (path < ARGREDUCE_PATH_AUTO || (path > ARGREDUCE_PATH_SPLIT && path != ARGREDUCE_PATH_WIDE))
+        return ARGREDUCE_ERR_INVALID_ARG;
     argreduce::g_force_path.store(path, std::memory_order_relaxed);
     return ARGREDUCE_OK;
 }
@@ -409,6 +457,7 @@ ARGREDUCE_EXPORT int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inn
     out->scratch_bytes = p.scratch_bytes;
     out->load_bytes = p.vec ? 16 : static_cast<int32_t>(argreduce::elem_size(dtype));
     out->dispatches = p.blocks_per_tile > 1 ? 2 : 1;
+    out->window = 0;
     return ARGREDUCE_OK;
 }
 
@@ -470,6 +519,7 @@ ARGREDUCE_EXPORT int argreduce_scan_plan(int64_t rows, int64_t cols, argreduce_d
     out->scratch_bytes = p.scratch_bytes;
     out->load_bytes = p.vecio ? 16 : static_cast<int32_t>(argreduce::scan_elem_size(dtype));
     out->dispatches = 1;
+    out->window = 0;
     return ARGREDUCE_OK;
 }
 

@@ -199,8 +199,10 @@ struct Cand {
         }
     }
     // Visit of one element by a lane, positions increasing.
-    __device__ void visit(C e, uint32_t pos) {
-        if (pos == 0) {
+    // `origin`: position 0 of this scan is position 0 of the row (false for the windows
+    // after the first of a row wider than INT32_MAX, whose first element is ordinary).
+    __device__ void visit(C e, uint32_t pos, bool origin = true) {
+        if (pos == 0 && origin) {
             take_first(e);
         } else {
             update(e, pos);
@@ -345,7 +347,7 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
 template <typename Fmt, int OP, int U, bool kGuard>
 __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base, uint32_t rem,
                                  uint32_t lane, uint32_t team, uint32_t head,
-                                 Cand<typename Fmt::C, OP> (&s)[Fmt::VW]) {
+                                 Cand<typename Fmt::C, OP> (&s)[Fmt::VW], bool origin) {
     using C = typename Fmt::C;
     using Vec = typename Fmt::Vec;
     // In the last, partial step (kGuard) a lane past the end re-reads the last vector
@@ -380,7 +382,7 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
                 t0.update(e[0], pos);
                 Cand<C, OP> f0;
                 f0.take_first(e[0]);
-                const bool first = (pos == 0);
+                const bool first = (pos == 0) && origin;
                 s[0].v = first ? f0.v : t0.v;
                 s[0].i = first ? f0.i : t0.i;
             } else {
@@ -392,9 +394,11 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
     }
 }
 
+// `origin`: false when `row` is a window of a longer row that does not start at the row's
+// position 0 (its first element is then an ordinary element).
 template <typename Fmt, int OP, int U>
 __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, uint32_t lane,
-                                uint32_t team, Cand<typename Fmt::C, OP>& c) {
+                                uint32_t team, Cand<typename Fmt::C, OP>& c, bool origin = true) {
     using C = typename Fmt::C;
     c.init();
     Cand<C, OP> s[Fmt::VW];
@@ -407,23 +411,23 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
     const uint32_t tail0 = head + nvec * Fmt::VW;
 
     for (uint32_t k = lane; k < head; k += team)
-        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
 
     const uint8_t* body = row + static_cast<size_t>(head) * Fmt::kSize;  // 16-byte aligned
     const uint32_t step = team * U;
     for (uint32_t base = 0; base < nvec; base += step) {
         const uint32_t rem = nvec - base;
         if (rem >= step) {
-            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, s);
+            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, s, origin);
         } else {
-            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, s);
+            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, s, origin);
             break;
         }
         if (rem == step) break;
     }
 
     for (uint32_t k = tail0 + lane; k < cols; k += team)
-        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
 
 #pragma unroll
     for (int k = 0; k < Fmt::VW; ++k)

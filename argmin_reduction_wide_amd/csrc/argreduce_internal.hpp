@@ -21,6 +21,8 @@ struct Plan {
     int64_t device_threads;
     size_t scratch_bytes;    // including 15 bytes of alignment slack; 0 if none needed
     size_t entry_bytes;      // split path: bytes per published (nonce, index) slot
+    int64_t window;          // WIDE: elements per window
+    int64_t windows;         // WIDE: windows per row (G)
 };
 
 // Launch plan of a reduction over the middle axis of [outer, len, inner], inner > 1.
@@ -79,6 +81,9 @@ hipError_t launch_empty(hipStream_t stream);
 
 // Events recorded around the row-scanning kernel of every launch when both are set.
 void set_kernel_events(hipEvent_t start, hipEvent_t stop);
+
+// Bytes of one (value, 64-bit index) window candidate of a row wider than INT32_MAX.
+size_t wide_partial_bytes(int dtype);
 
 // Bytes of one (value, index) partial of a two-dispatch middle-axis reduction.
 size_t axis_partial_bytes(int dtype);

@@ -370,6 +370,97 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
     }
 }
 
+// Rows wider than INT32_MAX (and any row, when a window size is forced for testing): each
+// row is cut into G windows of at most W <= 2^30 elements. Workgroup (row, w) scans window w
+// with the ordinary 32-bit positions of scan_row, relative to the window's start (the
+// positions stay 32-bit, the overflow fix's reasoning in "[CUDA] Parallelize ArgMax/ArgMin
+// over wide last axes": no per-element 64-bit positions), and stores the window's candidate
+// with its 64-bit global index; a second dispatch merges the G candidates of each row. Only
+// window 0 holds the row's position 0 (a leading NaN or the first element's seed).
+template <typename C>
+struct Wide {
+    C v;
+    int64_t i;  // global index; kWideEmpty: no candidate; kWideNaN0: last-index leading NaN
+};
+constexpr int64_t kWideNaN0 = -2;
+
+template <typename C, int OP>
+__device__ inline int64_t wide_empty() {
+    // loses every tie: the highest index for first-index ops, -1 for last-index ones
+    return op_is_last(OP) ? int64_t{-1} : INT64_MAX;
+}
+
+template <typename C, int OP>
+__device__ inline void wide_merge(C& av, int64_t& ai, C bv, int64_t bi) {
+    using K = Cand<C, OP>;
+    constexpr bool kLast = op_is_last(OP);
+    const bool a_nan0 = kLast && ai == kWideNaN0;
+    const bool b_nan0 = kLast && bi == kWideNaN0;
+    const bool t = b_nan0 || (!a_nan0 && (K::better(bv, av) || (bv == av && (kLast ? bi > ai : bi < ai))));
+    av = t ? bv : av;
+    ai = t ? bi : ai;
+}
+
+template <typename Fmt, int OP, int U>
+__global__ __launch_bounds__(kBlockThreads) void k_wide(const uint8_t* __restrict__ x, int64_t cols,
+                                                        uint32_t W, uint32_t G,
+                                                        Wide<typename Fmt::C>* __restrict__ part) {
+    using C = typename Fmt::C;
+    using K = Cand<C, OP>;
+    const uint32_t g = blockIdx.x;
+    const uint32_t r = g / G;
+    const uint32_t w = g - r * G;
+    const int64_t start = static_cast<int64_t>(w) * W;
+    const int64_t left = cols - start;
+    const uint32_t len = left < static_cast<int64_t>(W) ? static_cast<uint32_t>(left) : W;
+    const uint8_t* win = x + (static_cast<size_t>(r) * static_cast<size_t>(cols) + static_cast<size_t>(start)) * Fmt::kSize;
+    K c;
+    scan_row<Fmt, OP, U>(win, len, threadIdx.x, kBlockThreads, c, w == 0);
+    block_merge(c);
+    if (threadIdx.x == 0) {
+        int64_t gi;
+        if (c.i == K::kNone)
+            gi = wide_empty<C, OP>();
+        else if (op_is_last(OP) && c.i == kNaN0Last && w == 0)
+            gi = kWideNaN0;
+        else
+            gi = start + static_cast<int64_t>(c.i);
+        part[g].v = c.v;
+        part[g].i = gi;
+    }
+}
+
+// One workgroup per row (rows looped): merges the row's G window candidates.
+template <typename Fmt, int OP>
+__global__ __launch_bounds__(kBlockThreads) void k_wide_merge(const Wide<typename Fmt::C>* __restrict__ part,
+                                                              uint32_t G, int64_t rows,
+                                                              int64_t* __restrict__ out) {
+    using C = typename Fmt::C;
+    __shared__ C s_v[kBlockThreads];
+    __shared__ int64_t s_i[kBlockThreads];
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        C v = Cand<C, OP>::identity();
+        int64_t i = wide_empty<C, OP>();
+        for (uint32_t k = threadIdx.x; k < G; k += kBlockThreads) {
+            const Wide<C> e = part[static_cast<size_t>(r) * G + k];
+            wide_merge<C, OP>(v, i, e.v, e.i);
+        }
+        s_v[threadIdx.x] = v;
+        s_i[threadIdx.x] = i;
+        __syncthreads();
+        for (int h = kBlockThreads / 2; h > 0; h >>= 1) {
+            if (threadIdx.x < static_cast<uint32_t>(h)) {
+                wide_merge<C, OP>(v, i, s_v[threadIdx.x + h], s_i[threadIdx.x + h]);
+                s_v[threadIdx.x] = v;
+                s_i[threadIdx.x] = i;
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) out[r] = i == kWideNaN0 ? int64_t{0} : i;
+        __syncthreads();  // s_v / s_i are rewritten for the next row
+    }
+}
+
 __global__ void k_empty() {}
 
 std::atomic<uint32_t> g_nonce{0};
@@ -423,6 +514,22 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
             case 6408: launch_subwave<Fmt, OP, 64, 8>(p, x, c32, rows, out, s); break;
             default: return hipErrorInvalidValue;
         }
+        return hipGetLastError();
+    }
+    if (p.path == ARGREDUCE_PATH_WIDE) {
+        using Wd = Wide<typename Fmt::C>;
+        Wd* part = reinterpret_cast<Wd*>(scratch16);
+        const uint32_t W = static_cast<uint32_t>(p.window);
+        const uint32_t G = static_cast<uint32_t>(p.windows);
+        const dim3 grid(static_cast<uint32_t>(rows * p.windows));
+        switch (p.unroll) {
+            case 2: launch_scan(k_wide<Fmt, OP, 2>, grid, s, x, cols, W, G, part); break;
+            case 8: launch_scan(k_wide<Fmt, OP, 8>, grid, s, x, cols, W, G, part); break;
+            default: return hipErrorInvalidValue;
+        }
+        const int64_t mgrid = rows < 65536 ? rows : 65536;
+        hipLaunchKernelGGL((k_wide_merge<Fmt, OP>), dim3(static_cast<uint32_t>(mgrid)),
+                           dim3(kBlockThreads), 0, s, static_cast<const Wd*>(part), G, rows, out);
         return hipGetLastError();
     }
     uint64_t* slots = p.blocks_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
@@ -546,6 +653,10 @@ hipError_t launch_empty(hipStream_t s) {
 void set_kernel_events(hipEvent_t start, hipEvent_t stop) {
     g_ev_start.store(start, std::memory_order_relaxed);
     g_ev_stop.store(stop, std::memory_order_relaxed);
+}
+
+size_t wide_partial_bytes(int dtype) {
+    return dtype == ARGREDUCE_F64 ? sizeof(Wide<double>) : sizeof(Wide<float>);
 }
 
 size_t axis_partial_bytes(int dtype) {

@@ -82,18 +82,21 @@ class Workload:
     # "argreduce" (ArgMax / ArgMin, one index per row) or "scan" (cummax / cummin: a value
     # and an index per element)
     kind: str = "argreduce"
+    # Set for inputs too large to hold on the host: ((rows, cols), {flat index: value});
+    # `data` is then one block that fills the tensor by repetition (see device_data).
+    tiled: tuple | None = None
 
     @property
     def rows(self) -> int:
-        return int(self.data.shape[0])
+        return int(self.tiled[0][0] if self.tiled else self.data.shape[0])
 
     @property
     def cols(self) -> int:
-        return int(self.data.shape[1])
+        return int(self.tiled[0][1] if self.tiled else self.data.shape[1])
 
     @property
     def nbytes(self) -> int:
-        return int(self.data.nbytes)
+        return self.rows * self.cols * ITEMSIZE[self.dtype]
 
 
 def c1_row32000_f32(seed: int = 1, cols: int = 32000) -> Workload:
@@ -320,6 +323,48 @@ def scan_many_rows_f32(seed: int = 13, rows: int = 4096, cols: int = 4096) -> Wo
                     kind="scan", recipe="iid N(0,1) -> f32")
 
 
+def wide_row_f16(seed: int = 14, cols: int = (1 << 31) + 4096) -> Workload:
+    """ArgMax / ArgMin fp16 over one row of 2^31 + 4096 elements (4 GiB), wider than
+    INT32_MAX: a seeded block of 2^20 N(0,1) draws repeated over the row, with +8 planted at
+    2^31 + 17 and 2^31 + 100 and -8 at 5 and 2^31 + 4000 (beyond every draw). Expected by
+    construction: ArgMax 2^31 + 17, ArgMin 5. Only the block is held on the host;
+    ``device_data`` builds the row on the GPU."""
+    rng = np.random.default_rng(seed)
+    block = to_storage(rng.standard_normal(1 << 20), "f16")
+    assert np.abs(block.astype(np.float32)).max() < 8.0
+    plants = {(1 << 31) + 17: 8.0, (1 << 31) + 100: 8.0, 5: -8.0, (1 << 31) + 4000: -8.0}
+    return Workload(name=f"argmax_argmin_f16_1x{cols}", dtype="f16", ops=("max", "min"),
+                    data=block[None, :], seed=seed,
+                    planted={"max": {0: (1 << 31) + 17}, "min": {0: 5}},
+                    recipe="2^20 seeded N(0,1) f16 draws repeated over the row; +-8 planted",
+                    tiled=((1, cols), plants))
+
+
+def device_data(w: Workload, device: str = "cuda"):
+    """The workload's input as a contiguous torch tensor on ``device``: a copy of ``data``,
+    or, for a tiled workload, its block repeated to the full shape on the device with the
+    planted values set (no host array of the full size)."""
+    import torch
+
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+           "f64": torch.float64, "i32": torch.int32, "i64": torch.int64}[w.dtype]
+    flat = np.ascontiguousarray(w.data).reshape(-1)
+    host = (torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
+            if w.dtype == "bf16" else torch.from_numpy(flat.copy()))
+    if w.tiled is None:
+        return host.to(device).view(w.data.shape)
+    (rows, cols), plants = w.tiled
+    block = host.to(device)
+    n = rows * cols
+    out = torch.empty(n, dtype=tdt, device=device)
+    whole = n // block.numel() * block.numel()
+    out[:whole].view(-1, block.numel()).copy_(block.expand(whole // block.numel(), -1))
+    out[whole:].copy_(block[:n - whole])
+    for k, v in plants.items():
+        out[k] = v
+    return out.view(rows, cols)
+
+
 def random_int_rows(rng: np.random.Generator, rows: int, cols: int, dtype: str, kind: str) -> np.ndarray:
     """A (rows, cols) int32 / int64 array: "ties" (values in [-3, 3]), "full" (the whole
     range, extremes included) or "constant"."""
@@ -353,6 +398,8 @@ def config_workloads(which: str) -> list[Workload]:
         return [c5b_narrow_rows_f16()]
     if which == "axis":
         return [axis_many_outputs_f32(), axis_few_outputs_f32()]
+    if which == "wide":
+        return [wide_row_f16()]
     if which == "scan":
         return ([scan_doc_starts_i64()] + [scan_rows_i64(r, 65536 // r) for r in (1, 4, 64, 1024)]
                 + [scan_row_65536(d) for d in ("i32", "f32", "f64")]

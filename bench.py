@@ -63,16 +63,18 @@ class Case:
 
         self.w, self.op, self.B = w, op, B
         self.rows, self.cols = w.rows, w.cols
-        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "f64": torch.float64, "i32": torch.int32, "i64": torch.int64}[w.dtype]
-        flat = w.data.reshape(-1)
-        host = (torch.from_numpy(flat.view(np.int16).copy()).view(torch.bfloat16)
-                if w.dtype == "bf16" else torch.from_numpy(flat.copy()))
+        from argmin_reduction_wide_amd import workloads as W
+
+        one = W.device_data(w)
+        tdt = one.dtype
         self.n_rot = max(1, math.ceil(rotate_bytes / w.nbytes))
-        self.x = torch.empty((self.n_rot, self.rows, self.cols), dtype=tdt, device="cuda")
-        one = host.to("cuda").view(self.rows, self.cols)
-        for i in range(self.n_rot):
-            self.x[i].copy_(one)
+        if self.n_rot == 1:
+            self.x = one.view(1, self.rows, self.cols)
+        else:
+            self.x = torch.empty((self.n_rot, self.rows, self.cols), dtype=tdt, device="cuda")
+            for i in range(self.n_rot):
+                self.x[i].copy_(one)
+            del one
         self.ptrs = [self.x[i].data_ptr() for i in range(self.n_rot)]
         self.stream = torch.cuda.current_stream().cuda_stream
         self.dt = B.DTYPE_NAMES[w.dtype]
@@ -347,7 +349,7 @@ def main() -> int:
 
     extra = []
     if args.all:
-        for name in W.CONFIG_NAMES + ("axis", "scan"):
+        for name in W.CONFIG_NAMES + ("axis", "scan", "wide"):
             for w in W.config_workloads(name):
                 for op in w.ops:
                     r = measure(w, op, max(200, args.steps // 4), args.warmup // 4 + 1, graph=False)

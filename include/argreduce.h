@@ -70,7 +70,10 @@ enum {
     ARGREDUCE_ERR_INVALID_ARG = -1,      /* null pointer with rows > 0, rows < 0, cols < 1,
                                             bad op, misaligned x or out_idx */
     ARGREDUCE_ERR_UNSUPPORTED_DTYPE = -2,
-    ARGREDUCE_ERR_TOO_WIDE = -3,         /* cols > INT32_MAX (positions are 32-bit) */
+    ARGREDUCE_ERR_TOO_WIDE = -3,         /* a reduced axis the entry point does not admit:
+                                            len > INT32_MAX (argreduce_axis with inner > 1),
+                                            cols > INT32_MAX (argreduce_scan_lastaxis), or
+                                            more workgroups than a grid holds */
     ARGREDUCE_ERR_SCRATCH_TOO_SMALL = -4,/* scratch_bytes below argreduce_scratch_bytes() */
     ARGREDUCE_ERR_HIP = -5,              /* a HIP call or kernel launch failed */
     ARGREDUCE_ERR_NO_DEVICE = -6         /* no current HIP device to plan for */
@@ -82,9 +85,10 @@ enum {
  * caller allocates the intermediate buffer; its size is bounded by the device's thread
  * capacity, so it stays in the low kilobytes for any shape).
  *
- * Returns 0 when the chosen launch needs no scratch, else 8 bytes per (row, workgroup)
- * of a split row plus 15 bytes of slack, so the buffer may start at any byte address. Returns SIZE_MAX on an
- * invalid argument (rows < 0, cols < 1, cols > INT32_MAX, bad dtype) or when there is no
+ * Returns 0 when the chosen launch needs no scratch, else 16 bytes (32 for F64) per
+ * (row, workgroup) of a split row, or 16 bytes per (row, window) of a row wider than
+ * INT32_MAX, plus 15 bytes of slack, so the buffer may start at any byte address. Returns
+ * SIZE_MAX on an invalid argument (rows < 0, cols < 1, bad dtype) or when there is no
  * current device.
  */
 size_t argreduce_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dtype);
@@ -94,9 +98,13 @@ size_t argreduce_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dty
  *
  *   x             device pointer to rows * cols elements of `dtype`, row-major, rows
  *                 contiguous (row r starts at element r * cols); aligned to the element
- *                 size. Read only.
+ *                 size. Read only. rows * cols * element size must fit in int64.
  *   rows          >= 0; rows == 0 is a no-op that returns ARGREDUCE_OK.
- *   cols          1 .. INT32_MAX (an empty row has no index). rows * cols may exceed 2^31.
+ *   cols          >= 1 (an empty row has no index). rows * cols may exceed 2^31. Rows wider
+ *                 than INT32_MAX are cut into windows of at most 2^30 elements (positions
+ *                 stay 32-bit inside a window; "[CUDA] Parallelize ArgMax/ArgMin over wide
+ *                 last axes", "Why not int64 positions"); each window's candidate carries
+ *                 its 64-bit index to a merge kernel (ARGREDUCE_PATH_WIDE, two dispatches).
  *   out_idx       device pointer to `rows` int64 values, 8-byte aligned. Written only on
  *                 success; each value lies in [0, cols).
  *   scratch       device pointer to at least argreduce_scratch_bytes(rows, cols, dtype)
@@ -128,8 +136,10 @@ typedef enum {
     ARGREDUCE_PATH_SPLIT = 2,   /* several workgroups per row; the highest-id one merges */
     ARGREDUCE_PATH_AXIS = 3,    /* middle-axis reduction: a tile of consecutive outputs per
                                    workgroup, thread rows along the axis (argreduce_axis) */
-    ARGREDUCE_PATH_SCAN = 4     /* cumulative scan: a tile of a row per workgroup, tiles of
+    ARGREDUCE_PATH_SCAN = 4,    /* cumulative scan: a tile of a row per workgroup, tiles of
                                    a row chained by look-back (argreduce_scan_lastaxis) */
+    ARGREDUCE_PATH_WIDE = 5     /* rows wider than INT32_MAX: windows of <= 2^30 elements,
+                                   one workgroup each, merged by a second dispatch */
 } argreduce_path_t;
 
 typedef struct {
@@ -146,8 +156,9 @@ typedef struct {
     int32_t load_bytes;       /* bytes of one lane load in the body of the scan: 16, or the
                                  element size for an AXIS plan whose `inner` row is not a
                                  multiple of 16 bytes */
-    int32_t dispatches;       /* kernels one call launches: 1, or 2 for an AXIS plan whose
-                                 workgroups store partials that a second kernel merges */
+    int32_t dispatches;       /* kernels one call launches: 1, or 2 for an AXIS or WIDE plan
+                                 whose workgroups store partials that a second kernel merges */
+    int64_t window;           /* WIDE: elements per window (one workgroup each); else 0 */
 } argreduce_plan_t;
 
 /* The plan argreduce_lastaxis would use for these arguments on the current device. */
@@ -160,8 +171,13 @@ int argreduce_debug_set_capacity(int64_t threads);
 
 /* Force one path (ARGREDUCE_PATH_AUTO restores the automatic choice). Process-wide.
  * A forced path keeps its own geometry rules; a forced SPLIT uses at least two workgroups
- * per row, however short the row. */
+ * per row, however short the row; a forced WIDE cuts every row into windows (of the size
+ * set below, else the automatic one). SUBWAVE, BLOCK, SPLIT and WIDE can be forced. */
 int argreduce_debug_force_path(int path);
+
+/* Window size of the WIDE path in elements, 1 .. 2^30 (0 = automatic). Process-wide. Lets
+ * tests run the windowed path on rows small enough for the CPU oracle. */
+int argreduce_debug_set_window(int64_t elements);
 
 /* ----------------------------------------------------------------------------------------
  * Reduction over a middle axis.

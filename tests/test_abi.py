@@ -23,6 +23,7 @@ def lib():
     yield h
     B.argreduce_debug_set_capacity(0)
     B.argreduce_debug_force_path(B.PATH_AUTO)
+    B.argreduce_debug_set_window(0)
 
 
 @pytest.fixture
@@ -59,7 +60,7 @@ def test_library_has_no_oracle_dependency():
     (4, 10, -1, B.MAX, -2),
     (4, 10, B.F32, 4, -1),
     (4, 10, B.F32, -1, -1),
-    (1, INT32_MAX + 1, B.F16, B.MAX, -3),
+    (1 << 40, 1 << 30, B.F16, B.MAX, -1),  # rows * cols * element size beyond int64
 ])
 def test_invalid_arguments_rejected_before_any_gpu_call(lib, rows, cols, dtype, op, code):
     assert B.argreduce_lastaxis(FAKE, dtype, rows, cols, op, FAKE, 0, 0, 0) == code
@@ -87,7 +88,7 @@ def test_scratch_too_small_is_detected_before_launch(mi355x):
 def test_scratch_bytes_invalid_arguments(lib):
     assert B.argreduce_scratch_bytes(1, 0, B.F32) == B.SIZE_MAX
     assert B.argreduce_scratch_bytes(-1, 5, B.F32) == B.SIZE_MAX
-    assert B.argreduce_scratch_bytes(1, INT32_MAX + 1, B.F32) == B.SIZE_MAX
+    assert B.argreduce_scratch_bytes(1 << 40, 1 << 30, B.F32) == B.SIZE_MAX
     assert B.argreduce_scratch_bytes(1, 5, 9) == B.SIZE_MAX
 
 
@@ -171,7 +172,7 @@ def test_forced_paths(mi355x):
     assert B.argreduce_debug_force_path(B.PATH_SUBWAVE) == 0
     p = B.argreduce_plan(1, 202048, B.F32)
     assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 64
-    assert B.argreduce_debug_force_path(5) == -1
+    assert B.argreduce_debug_force_path(6) == -1 and B.argreduce_debug_force_path(B.PATH_AXIS) == -1
     assert B.argreduce_debug_set_capacity(-5) == -1
 
 
@@ -287,3 +288,40 @@ def test_scan_scratch_too_small(mi355x):
                                      need - 1, 0) == -4
     assert B.argreduce_scan_lastaxis(FAKE, B.I64, 1, 65536, B.MAX, FAKE * 4, FAKE * 8, 0,
                                      need, 0) == -4
+
+
+# rows wider than INT32_MAX: windows
+
+
+def test_wide_rows_plan(mi355x):
+    p = B.argreduce_plan(1, INT32_MAX + 1, B.F16)
+    assert p["path"] == B.PATH_WIDE and p["dispatches"] == 2
+    w = p["window"]
+    assert 0 < w <= 1 << 30 and w % 4096 == 0
+    assert p["blocks_per_row"] == -(-(INT32_MAX + 1) // w) and p["grid_blocks"] == p["blocks_per_row"]
+    assert p["blocks_per_row"] >= MI355X_THREADS // 256  # about one window per resident workgroup
+    assert p["scratch_bytes"] == 15 + p["blocks_per_row"] * 16
+    assert B.argreduce_scratch_bytes(1, INT32_MAX + 1, B.F16) == p["scratch_bytes"]
+    p = B.argreduce_plan(3, 5 * 2 ** 31, B.F64)
+    assert p["path"] == B.PATH_WIDE and p["window"] <= 1 << 30 and p["grid_blocks"] == 3 * p["blocks_per_row"]
+    assert p["scratch_bytes"] == 15 + 3 * p["blocks_per_row"] * 16
+    # the last ordinary width keeps its path
+    assert B.argreduce_plan(1, INT32_MAX, B.F16)["path"] == B.PATH_SPLIT
+    # wide rows are refused by the middle-axis and scan entry points only
+    assert B.argreduce_axis(FAKE, B.F32, 2, INT32_MAX + 1, 3, B.MAX, FAKE, 0, 0, 0) == -3
+    assert B.argreduce_scan_lastaxis(FAKE, B.F32, 1, INT32_MAX + 1, B.MAX, FAKE * 4, FAKE * 8,
+                                     0, 0, 0) == -3
+    assert B.argreduce_lastaxis(FAKE, B.F16, 1, INT32_MAX + 1, B.MAX, FAKE, FAKE, 100, 0) == -4
+
+
+def test_forced_window(mi355x):
+    assert B.argreduce_debug_set_window(-1) == -1 and B.argreduce_debug_set_window((1 << 30) + 1) == -1
+    assert B.argreduce_debug_force_path(B.PATH_AXIS) == -1 and B.argreduce_debug_force_path(B.PATH_SCAN) == -1
+    assert B.argreduce_debug_force_path(B.PATH_WIDE) == 0
+    assert B.argreduce_debug_set_window(1000) == 0
+    p = B.argreduce_plan(5, 2500, B.F32)
+    assert p["path"] == B.PATH_WIDE and p["window"] == 1000 and p["blocks_per_row"] == 3
+    assert p["grid_blocks"] == 15 and p["unroll"] == 2 and p["scratch_bytes"] == 15 + 15 * 16
+    B.argreduce_debug_set_window(0)
+    p = B.argreduce_plan(1, 202048, B.F32)  # forced, automatic window
+    assert p["path"] == B.PATH_WIDE and p["window"] == 4096

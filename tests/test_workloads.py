@@ -70,3 +70,14 @@ def test_axis_workloads_shapes(oracle_lib):
         got = oracle_lib.argreduce_axis(w.data.reshape(outer, length, inner), "f32", "max")
         want = np.argmax(w.data.reshape(outer, length, inner), axis=1)  # NaN-free: first occurrence
         assert np.array_equal(got, want)
+
+
+def test_wide_workload_is_tiled():
+    w = W.wide_row_f16()
+    (rows, cols), plants = w.tiled
+    assert (w.rows, w.cols) == (rows, cols) == (1, 2 ** 31 + 4096)
+    assert w.nbytes == cols * 2 and w.data.shape == (1, 1 << 20)
+    # the planted extremes lie beyond every repeated draw, and the expectations follow
+    assert np.abs(w.data.astype(np.float32)).max() < 8.0
+    assert w.planted["max"][0] == min(k for k, v in plants.items() if v == 8.0) > 2 ** 31
+    assert w.planted["min"][0] == min(k for k, v in plants.items() if v == -8.0) == 5
