@@ -38,7 +38,8 @@ EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events",
            "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
            "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
-           "argreduce_debug_set_window")
+           "argreduce_debug_set_window", "argreduce_debug_launch_store",
+           "argreduce_debug_set_spin_limit")
 
 
 class ArgreduceError(RuntimeError):
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_scan_lastaxis.restype = c_int
                 h.argreduce_scan_plan.argtypes = [i64, i64, c_int, ctypes.POINTER(argreduce_plan_t)]
                 h.argreduce_scan_plan.restype = c_int
+                h.argreduce_debug_launch_store.argtypes = [vp, vp]
+                h.argreduce_debug_launch_store.restype = c_int
+                h.argreduce_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+                h.argreduce_debug_set_spin_limit.restype = c_int
                 h.argreduce_debug_set_window.argtypes = [i64]
                 h.argreduce_debug_set_window.restype = c_int
                 h.argreduce_debug_launch_empty.argtypes = [vp]
@@ -186,6 +191,14 @@ def argreduce_scan_plan(rows: int, cols: int, dtype) -> dict:
 
 def argreduce_debug_set_capacity(threads: int) -> int:
     return lib().argreduce_debug_set_capacity(threads)
+
+
+def argreduce_debug_launch_store(out_ptr: int, stream: int) -> int:
+    return lib().argreduce_debug_launch_store(out_ptr, stream)
+
+
+def argreduce_debug_set_spin_limit(polls: int) -> int:
+    return lib().argreduce_debug_set_spin_limit(polls)
 
 
 def argreduce_debug_set_window(elements: int) -> int:

@@ -415,6 +415,18 @@ ARGREDUCE_EXPORT int argreduce_debug_force_path(int path) {
     return ARGREDUCE_OK;
 }
 
+ARGREDUCE_EXPORT int argreduce_debug_launch_store(int64_t* out, void* stream) {
+    if (out == nullptr || reinterpret_cast<uintptr_t>(out) % 8 != 0) return ARGREDUCE_ERR_INVALID_ARG;
+    return argreduce::launch_store_floor(out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ARGREDUCE_OK
+               : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_set_spin_limit(uint32_t polls) {
+    argreduce::set_spin_limit(polls);
+    return ARGREDUCE_OK;
+}
+
 ARGREDUCE_EXPORT int argreduce_debug_launch_empty(void* stream) {
     return argreduce::launch_empty(static_cast<hipStream_t>(stream)) == hipSuccess
                ? ARGREDUCE_OK

@@ -78,6 +78,8 @@ hipError_t launch(const Plan& plan, const void* x, int dtype, int op, int64_t ro
 
 // Launches one empty kernel (the launch floor of the measurement hooks).
 hipError_t launch_empty(hipStream_t stream);
+hipError_t launch_store_floor(int64_t* out, hipStream_t stream);
+void set_spin_limit(uint32_t polls);
 
 // Events recorded around the row-scanning kernel of every launch when both are set.
 void set_kernel_events(hipEvent_t start, hipEvent_t stop);

@@ -47,7 +47,6 @@
 
 namespace argreduce {
 
-constexpr uint32_t kSpinLimit = 1u << 20;  // polls of one slot before giving up (~1 s)
 
 template <typename Fmt, int OP, int G, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
@@ -71,7 +70,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
                                                           uint32_t B, int64_t grid_rows,
                                                           int64_t* __restrict__ out,
                                                           uint64_t* __restrict__ slots,
-                                                          uint32_t nonce) {
+                                                          uint32_t nonce, uint32_t spin_limit) {
     using C = typename Fmt::C;
     __shared__ int s_timeout;
     const uint32_t b = blockIdx.x % B;
@@ -128,7 +127,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
                 }
                 ok = ok && Cand<C, OP>::valid_index(pay[0], cols);
                 if (!ok) {
-                    if (++spins > kSpinLimit) {
+                    if (++spins > spin_limit) {
                         s_timeout = 1;
                         break;
                     }
@@ -463,6 +462,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_wide_merge(const Wide<typenam
 
 __global__ void k_empty() {}
 
+// The floor of any call that delivers a result: one workgroup, one argument, one store.
+__global__ void k_store_floor(int64_t* __restrict__ out) {
+    if (threadIdx.x == 0) out[0] = 0;
+}
+
 std::atomic<uint32_t> g_nonce{0};
 
 uint32_t next_nonce() {
@@ -471,6 +475,14 @@ uint32_t next_nonce() {
         n = g_nonce.fetch_add(1u, std::memory_order_relaxed) + 1u;
     } while (n == 0u || n == 0xffffffffu);
     return n;
+}
+
+std::atomic<uint32_t> g_spin_limit{1u << 20};
+
+uint32_t spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+void set_spin_limit(uint32_t polls) {
+    g_spin_limit.store(polls == 0 ? (1u << 20) : polls, std::memory_order_relaxed);
 }
 
 std::atomic<hipEvent_t> g_ev_start{nullptr};
@@ -490,7 +502,7 @@ void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows,
                    uint64_t* slots, hipStream_t s) {
     launch_scan(k_blocks<Fmt, OP, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, cols,
                 rows, static_cast<uint32_t>(p.blocks_per_row), p.grid_rows, out, slots,
-                p.blocks_per_row > 1 ? next_nonce() : 0u);
+                p.blocks_per_row > 1 ? next_nonce() : 0u, spin_limit());
 }
 
 template <typename Fmt, int OP>
@@ -647,6 +659,11 @@ hipError_t launch_axis(const AxisPlan& p, const void* x, int dtype, int op, int6
 
 hipError_t launch_empty(hipStream_t s) {
     hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_store_floor(int64_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_store_floor, dim3(1), dim3(64), 0, s, out);
     return hipGetLastError();
 }
 

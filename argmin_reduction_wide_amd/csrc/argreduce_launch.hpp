@@ -15,6 +15,11 @@ namespace argreduce {
 // reset to) nor 0xffffffff.
 uint32_t next_nonce();
 
+// Polls of one published word before a bounded wait gives up (argreduce_debug_set_spin_limit;
+// default 2^20, about a second).
+uint32_t spin_limit();
+void set_spin_limit(uint32_t polls);  // 0 restores the default
+
 // Measurement events (argreduce_debug_set_kernel_events); null when unset.
 extern std::atomic<hipEvent_t> g_ev_start;
 extern std::atomic<hipEvent_t> g_ev_stop;

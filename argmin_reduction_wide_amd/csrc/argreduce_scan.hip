@@ -57,7 +57,6 @@ namespace {
 constexpr uint32_t kEmpty = 0xffffffffu;  // index of the empty piece
 constexpr uint32_t kNaN0 = 0x7fffffffu;   // index of a leading NaN (reported as 0)
 constexpr uint32_t kFail = 0xfffffffeu;   // published by a tile whose look-back timed out
-constexpr uint32_t kScanSpinLimit = 1u << 20;
 constexpr int kLookBackTiles = 1;  // tiles per lane of the look-back window
 
 // Storage bits of an output value, per format.
@@ -243,7 +242,7 @@ __device__ inline bool read_state(const uint64_t* w, uint32_t nonce, C& v, uint3
 // published its aggregate. The uniform result is in every lane of the calling wave.
 template <typename C, int OP, int K>
 __device__ inline bool look_back(const uint64_t* row_states, uint32_t t, uint32_t nonce, C& accv,
-                                 uint32_t& acci) {
+                                 uint32_t& acci, uint32_t spin_limit) {
     using Op = ScanOp<C, OP>;
     using SW = StateWords<C>;
     const uint32_t lane = threadIdx.x % kWave;
@@ -296,7 +295,7 @@ __device__ inline bool look_back(const uint64_t* row_states, uint32_t t, uint32_
             const uint64_t mask = __ballot(fk < K);
             lp = mask ? __ffsll(static_cast<unsigned long long>(mask)) - 1 : kWave;
             if (__ballot(static_cast<int>(lane) <= lp && !ready) == 0) break;
-            if (++spins > kScanSpinLimit) return false;
+            if (++spins > spin_limit) return false;
             __builtin_amdgcn_s_sleep(2);
         }
         // a predecessor that failed makes this tile fail too, rather than use its state
@@ -352,7 +351,8 @@ template <typename Fmt, int OP, int U, bool VECIO>
 __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict__ x, uint32_t cols,
                                                        uint32_t T, uint8_t* __restrict__ out_val,
                                                        int64_t* __restrict__ out_idx,
-                                                       uint64_t* __restrict__ states, uint32_t nonce) {
+                                                       uint64_t* __restrict__ states, uint32_t nonce,
+                                                       uint32_t spin_limit) {
     using C = typename Fmt::C;
     using Op = ScanOp<C, OP>;
     using S = typename Out<Fmt>::S;
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
         bool ok = true;
         if (t > 0) {
             if (lane == 0) publish(mine, nonce, av, ai);  // aggregate
-            ok = look_back<C, OP, kLookBackTiles>(row_states, t, nonce, pv, pi);
+            ok = look_back<C, OP, kLookBackTiles>(row_states, t, nonce, pv, pi, spin_limit);
         }
         if (lane == 0) {
             C incv = pv;
@@ -592,13 +592,13 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
     constexpr int US = kScanUnrollShort, UL = kScanUnrollLong;
     if (p.unroll == US && p.vecio)
-        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == US)
-        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.vecio)
-        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else
-        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce);
+        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     return hipGetLastError();
 }
 

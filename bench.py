@@ -185,13 +185,20 @@ class Case:
         return self.out.cpu().numpy()
 
 
-def launch_floor_us(steps: int) -> float:
+def launch_floor_us(steps: int, store: bool = False) -> float:
+    """Per-call time of an empty kernel (no arguments), or, with `store`, of a kernel that
+    takes one pointer argument and stores one int64: the floor of any call that returns a
+    result (the kernel-argument path costs most of the difference)."""
     import torch
 
     import argmin_reduction_wide_amd.binding as B
 
     stream = torch.cuda.current_stream().cuda_stream
-    f = B.lib().argreduce_debug_launch_empty
+    if store:
+        out = torch.zeros(1, dtype=torch.int64, device="cuda")
+        f = lambda st: B.lib().argreduce_debug_launch_store(out.data_ptr(), st)
+    else:
+        f = B.lib().argreduce_debug_launch_empty
     for _ in range(50):
         f(stream)
     torch.cuda.synchronize()
@@ -345,7 +352,9 @@ def main() -> int:
     sec_w = W.c4_square_f32_f64("f32")
     sec = measure(sec_w, "max", args.steps, args.warmup)
     floor = launch_floor_us(args.steps)
-    log(f"[bench] launch floor (empty kernel) {floor:.3f} us")
+    store_floor = launch_floor_us(args.steps, store=True)
+    log(f"[bench] launch floor (empty kernel) {floor:.3f} us; one-argument store kernel "
+        f"{store_floor:.3f} us")
 
     extra = []
     if args.all:
@@ -388,6 +397,7 @@ def main() -> int:
         "graph_us_per_call": prim["graph_us_per_call"],
         "kernel_event_us": prim["kernel_event_us"],
         "launch_floor_us": round(floor, 3),
+        "store_floor_us": round(store_floor, 3),
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -258,6 +258,19 @@ int argreduce_scan_plan(int64_t rows, int64_t cols, argreduce_dtype_t dtype,
  * launch). Returns ARGREDUCE_OK or ARGREDUCE_ERR_HIP. */
 int argreduce_debug_launch_empty(void *stream);
 
+/* Measurement hook: the floor of a call that delivers a result. Enqueues one workgroup of
+ * a kernel that takes one pointer argument and stores one int64 (0) at `out` (8-byte
+ * aligned device memory) — the same launch and kernel-argument cost as every entry point,
+ * with no data read. Returns ARGREDUCE_OK, ARGREDUCE_ERR_INVALID_ARG or ARGREDUCE_ERR_HIP. */
+int argreduce_debug_launch_store(int64_t *out, void *stream);
+
+/* Test hook for the bounded waits (the split ArgMax path's finalizing workgroup, the scan's
+ * look-back): polls of one published word before the wait gives up and the affected
+ * outputs become -1 (0 restores the default, 2^20 polls). Process-wide. With a tiny limit
+ * a wait can give up although nothing is wrong; this lets tests drive the time-out path
+ * from the host while every kernel still ends normally. */
+int argreduce_debug_set_spin_limit(uint32_t polls);
+
 /* Measurement hook: when both are non-NULL, every later call launches its main kernel
  * (not a merge or clear kernel) with `start` recorded just before and
  * `stop` just after it on the same stream (hipEvent_t values created by the caller with

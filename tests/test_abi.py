@@ -325,3 +325,9 @@ def test_forced_window(mi355x):
     B.argreduce_debug_set_window(0)
     p = B.argreduce_plan(1, 202048, B.F32)  # forced, automatic window
     assert p["path"] == B.PATH_WIDE and p["window"] == 4096
+
+
+def test_debug_hooks_validate(lib):
+    assert B.argreduce_debug_launch_store(0, 0) == -1
+    assert B.argreduce_debug_launch_store(FAKE + 4, 0) == -1
+    assert B.argreduce_debug_set_spin_limit(0) == 0

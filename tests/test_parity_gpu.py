@@ -345,3 +345,32 @@ def test_axis_workloads_full_size(oracle_lib):
         arr = w.data.reshape(outer, length, inner)
         for op in w.ops + tuple(o + "_last" for o in w.ops):
             check_axis(oracle_lib, arr, w.dtype, op, f"axis workload {w.name}")
+
+
+def test_bounded_wait_gives_up_cleanly(oracle_lib):
+    """The split path's bounded wait, driven from the host with a one-poll limit: every
+    output is the oracle's index or -1 (a wait that gave up), every kernel ends; with the
+    default limit restored the same scratch gives exact results again."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    cases = [(1, 202048, "f32"), (32, 202048, "f16"), (3, 500000, "f64")]
+    try:
+        B.argreduce_debug_set_spin_limit(1)
+        for rows, cols, dtype in cases:
+            arr = W.random_rows(rng, rows, cols, dtype, "ties")
+            want = oracle_lib.argreduce_lastaxis(arr, dtype, "max")
+            t = to_device(arr, dtype)
+            need = B.argreduce_scratch_bytes(rows, cols, dtype)
+            scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+            for rep in range(5):
+                announce(f"one-poll limit rows={rows} cols={cols} dtype={dtype} rep={rep}")
+                rc, got = run(t, dtype, "max", scratch=scratch)
+                assert rc == 0
+                assert np.all((got == want) | (got == -1)), (rows, cols, dtype, got)
+            B.argreduce_debug_set_spin_limit(0)
+            rc, got = run(t, dtype, "max", scratch=scratch)
+            assert rc == 0 and np.array_equal(got, want)
+            B.argreduce_debug_set_spin_limit(1)
+    finally:
+        B.argreduce_debug_set_spin_limit(0)

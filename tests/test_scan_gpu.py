@@ -203,3 +203,27 @@ def test_scan_torch_wrapper(oracle_lib):
     ti = torch.arange(65536, device="cuda", dtype=torch.int64)
     v, i = ar.cummax(ti)
     assert torch.equal(v, ti) and torch.equal(i, ti)
+
+
+def test_scan_bounded_look_back_gives_up_cleanly(oracle_lib):
+    """The look-back's bounded wait with a one-poll limit: each index is the oracle's or -1
+    (a tile that gave up, and the tiles after it); with the default limit restored the same
+    scratch gives exact results."""
+    import torch
+
+    rng = np.random.default_rng(904)
+    arr = inputs(rng, 1, 3 << 20, "f32", "ties")
+    want_v, want_i = oracle_lib.cumulative(arr, "f32", "max")
+    need = B.argreduce_scan_scratch_bytes(1, 3 << 20, "f32")
+    scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+    try:
+        B.argreduce_debug_set_spin_limit(1)
+        for rep in range(3):
+            announce(f"scan one-poll limit rep={rep}")
+            rc, _, got_i = run_scan(arr, "f32", "max", scratch=scratch)
+            assert rc == 0
+            assert np.all((got_i == want_i) | (got_i == -1))
+    finally:
+        B.argreduce_debug_set_spin_limit(0)
+    rc, got_v, got_i = run_scan(arr, "f32", "max", scratch=scratch)
+    assert rc == 0 and np.array_equal(got_i, want_i) and np.array_equal(bits(got_v), bits(want_v))
