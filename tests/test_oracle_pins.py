@@ -50,7 +50,7 @@ def test_rejects_empty_rows(oracle_lib):
 
 
 def test_closed_form_itself_on_hand_rows():
-    """The checker's closed form on rows small enough to verify by eye."""
+    """The independent closed form on rows small enough to verify by eye."""
     nan, inf = float("nan"), float("inf")
     rows = np.array([[1, 3, 3, 2], [nan, 5, 6, 7], [-inf, -inf, nan, -inf],
                      [2, nan, 9, 9], [-0.0, 0.0, -1, 0.0]])
