@@ -39,7 +39,7 @@ EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
            "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
            "argreduce_debug_set_window", "argreduce_debug_launch_store",
-           "argreduce_debug_set_spin_limit")
+           "argreduce_debug_set_spin_limit", "argreduce_debug_launch_read")
 
 
 class ArgreduceError(RuntimeError):
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_scan_plan.restype = c_int
                 h.argreduce_debug_launch_store.argtypes = [vp, vp]
                 h.argreduce_debug_launch_store.restype = c_int
+                h.argreduce_debug_launch_read.argtypes = [vp, sz, vp, i64, vp]
+                h.argreduce_debug_launch_read.restype = c_int
                 h.argreduce_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
                 h.argreduce_debug_set_spin_limit.restype = c_int
                 h.argreduce_debug_set_window.argtypes = [i64]
@@ -195,6 +197,11 @@ def argreduce_debug_set_capacity(threads: int) -> int:
 
 def argreduce_debug_launch_store(out_ptr: int, stream: int) -> int:
     return lib().argreduce_debug_launch_store(out_ptr, stream)
+
+
+def argreduce_debug_launch_read(x_ptr: int, nbytes: int, out_ptr: int, grid: int,
+                                stream: int) -> int:
+    return lib().argreduce_debug_launch_read(x_ptr, nbytes, out_ptr, grid, stream)
 
 
 def argreduce_debug_set_spin_limit(polls: int) -> int:

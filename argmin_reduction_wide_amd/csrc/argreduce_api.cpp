@@ -30,13 +30,11 @@ constexpr int64_t kWaveRowMaxVec = 256;
 // Middle axis: at most one wavefront of lanes along `inner` per tile.
 constexpr int64_t kAxisMaxLanes = 64;
 constexpr int64_t kBlockRowMaxVec = 2048;
-// A split row gives each lane about this many 16-byte vectors (all in flight at once).
-constexpr int64_t kSplitVecPerLane = 2;
-// Split rows use at most 1/kSplitFillDiv of one device wave of workgroups: with several
-// rows, fewer workgroups per row (more vectors per lane, fewer partials to merge) measured
-// faster than filling the device.
-constexpr int64_t kSplitFillDiv = 4;
 constexpr int64_t kMaxBlocksPerRow = 1024;
+// Rows too wide for one step of loads (or too many to split in one device wave) use at most
+// 1/kSplitFillDiv of a device wave of workgroups: there the call is bandwidth-bound, and
+// fewer workgroups per row (fewer partials to merge) measured faster than filling the device.
+constexpr int64_t kSplitFillDiv = 4;
 // Grids hold at most this many device-fulls of workgroups; further rows are looped over.
 // Many-row shapes run fastest with every row's team launched at once (the dispatcher keeps
 // the CUs fed), so the cap only bounds pathological row counts.
@@ -52,6 +50,8 @@ std::atomic<int64_t> g_capacity_override{0};
 std::atomic<int> g_force_path{ARGREDUCE_PATH_AUTO};
 std::atomic<int64_t> g_window{0};
 constexpr int64_t kMaxWindow = int64_t{1} << 30;
+// Workgroups of the streaming-read measurement kernel.
+constexpr int64_t kMaxReadGrid = 65536;
 
 int64_t elem_size(int dtype) {
     switch (dtype) {
@@ -154,10 +154,24 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     const int64_t vec_row = ceil_div(cols * elem_size(dtype), 16);  // 16-byte vectors per row
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
     const int64_t rows1 = rows > 0 ? rows : 1;
-    const int64_t fill_b = cap_blocks / kSplitFillDiv / rows1;  // workgroups per row allowed
-    const int64_t want_b = ceil_div(vec_row, kBlock * kSplitVecPerLane);
-    int64_t split_b = fill_b < want_b ? fill_b : want_b;
-    split_b = split_b < kMaxBlocksPerRow ? split_b : kMaxBlocksPerRow;
+    // Split rows: the fewest 16-byte loads per lane (U) for which one step of
+    // B = ceil(vec_row / (256 U)) workgroups per row covers the row while the workgroups of
+    // every row fit in one device wave. A call of a few rows is latency-bound: the time after
+    // the last load arrives (the lane's compares, then the merges) grows with U, and more
+    // workgroups cost little. Failing that, 8 loads per lane and a share of the device's
+    // workgroups per row; the row then takes several steps.
+    int64_t split_b = 0;
+    for (int64_t u = 1; u <= kMaxUnrollBlocks; u *= 2) {
+        const int64_t b = ceil_div(vec_row, kBlock * u);
+        if (b <= kMaxBlocksPerRow && b * rows1 <= cap_blocks) {
+            split_b = b;
+            break;
+        }
+    }
+    if (split_b == 0) {
+        split_b = cap_blocks / kSplitFillDiv / rows1;
+        split_b = split_b < kMaxBlocksPerRow ? split_b : kMaxBlocksPerRow;
+    }
 
     int path = g_force_path.load(std::memory_order_relaxed);
     int64_t group = 64, blocks_per_row = 1;
@@ -418,6 +432,18 @@ ARGREDUCE_EXPORT int argreduce_debug_force_path(int path) {
 ARGREDUCE_EXPORT int argreduce_debug_launch_store(int64_t* out, void* stream) {
     if (out == nullptr || reinterpret_cast<uintptr_t>(out) % 8 != 0) return ARGREDUCE_ERR_INVALID_ARG;
     return argreduce::launch_store_floor(out, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? ARGREDUCE_OK
+               : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_launch_read(const void* x, size_t bytes, uint32_t* out,
+                                                 int64_t grid, void* stream) {
+    if (x == nullptr || out == nullptr || bytes == 0 || bytes % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0 ||
+        grid < 1 || grid > argreduce::kMaxReadGrid)
+        return ARGREDUCE_ERR_INVALID_ARG;
+    return argreduce::launch_read_floor(x, bytes, out, static_cast<uint32_t>(grid),
+                                        static_cast<hipStream_t>(stream)) == hipSuccess
                ? ARGREDUCE_OK
                : ARGREDUCE_ERR_HIP;
 }

@@ -210,15 +210,18 @@ struct Cand {
     }
     // Update for positions visited in increasing order by one lane: strict comparison, or
     // non-strict for the last-index ops (false for NaN either way).
+    // (Bitwise, not short-circuit, operators here and in merge: each comparison becomes a
+    // lane mask combined on the scalar unit, with no branches.)
     __device__ void update(C e, uint32_t pos) {
-        const bool t = kLast ? (better(e, v) || e == v) : better(e, v);
+        const bool t = kLast ? (better(e, v) | (e == v)) : better(e, v);
         v = t ? e : v;
         i = t ? pos : i;
     }
     // Merge with another lane's candidate: better value wins, equal values -> tie rule;
     // under the last-index ops a leading NaN (index INT32_MAX) wins outright.
     __device__ void merge(C ov, uint32_t oi) {
-        const bool t = (kLast && oi == kNaN0Last) || better(ov, v) || (ov == v && tie_wins(oi, i));
+        const bool nan0 = kLast ? (oi == kNaN0Last) : false;
+        const bool t = nan0 | better(ov, v) | ((ov == v) & tie_wins(oi, i));
         v = t ? ov : v;
         i = t ? oi : i;
     }
@@ -429,9 +432,13 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
     for (uint32_t k = tail0 + lane; k < cols; k += team)
         c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
 
+    // slot k's index is the position of its vector's first element; an empty slot stays
+    // empty (its index must not be offset)
 #pragma unroll
-    for (int k = 0; k < Fmt::VW; ++k)
-        if (s[k].i != Cand<C, OP>::kNone) c.merge(s[k].v, s[k].i + k);
+    for (int k = 0; k < Fmt::VW; ++k) {
+        const uint32_t idx = s[k].i == Cand<C, OP>::kNone ? Cand<C, OP>::kNone : s[k].i + k;
+        c.merge(s[k].v, idx);
+    }
 }
 
 }  // namespace argreduce

@@ -79,6 +79,10 @@ hipError_t launch(const Plan& plan, const void* x, int dtype, int op, int64_t ro
 // Launches one empty kernel (the launch floor of the measurement hooks).
 hipError_t launch_empty(hipStream_t stream);
 hipError_t launch_store_floor(int64_t* out, hipStream_t stream);
+// A plain streaming read of `bytes` (a multiple of 16) at `x` (16-byte aligned) with `grid`
+// workgroups; `out` holds `grid` words (written only for one improbable XOR of the data).
+hipError_t launch_read_floor(const void* x, size_t bytes, uint32_t* out, uint32_t grid,
+                             hipStream_t stream);
 void set_spin_limit(uint32_t polls);
 
 // Events recorded around the row-scanning kernel of every launch when both are set.

@@ -393,9 +393,10 @@ template <typename C, int OP>
 __device__ inline void wide_merge(C& av, int64_t& ai, C bv, int64_t bi) {
     using K = Cand<C, OP>;
     constexpr bool kLast = op_is_last(OP);
-    const bool a_nan0 = kLast && ai == kWideNaN0;
-    const bool b_nan0 = kLast && bi == kWideNaN0;
-    const bool t = b_nan0 || (!a_nan0 && (K::better(bv, av) || (bv == av && (kLast ? bi > ai : bi < ai))));
+    const bool a_nan0 = kLast ? (ai == kWideNaN0) : false;
+    const bool b_nan0 = kLast ? (bi == kWideNaN0) : false;
+    const bool tie = kLast ? (bi > ai) : (bi < ai);
+    const bool t = b_nan0 | (!a_nan0 & (K::better(bv, av) | ((bv == av) & tie)));
     av = t ? bv : av;
     ai = t ? bi : ai;
 }
@@ -465,6 +466,29 @@ __global__ void k_empty() {}
 // The floor of any call that delivers a result: one workgroup, one argument, one store.
 __global__ void k_store_floor(int64_t* __restrict__ out) {
     if (threadIdx.x == 0) out[0] = 0;
+}
+
+// The practical read roofline: a plain grid-stride stream of 16-byte nontemporal loads
+// (four in flight per lane) folded with XOR. The store is taken only for one bit pattern,
+// so the loads cannot be removed and nothing is written in practice.
+__global__ __launch_bounds__(kBlockThreads) void k_read_floor(const u32x4* __restrict__ x, size_t nvec,
+                                                       uint32_t* __restrict__ out) {
+    constexpr int U = 4;
+    const size_t stride = static_cast<size_t>(gridDim.x) * kBlockThreads;
+    size_t i = static_cast<size_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (U - 1) * stride < nvec; i += U * stride) {
+        u32x4 q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) q[u] = __builtin_nontemporal_load(x + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= q[u].x ^ q[u].y ^ q[u].z ^ q[u].w;
+    }
+    for (; i < nvec; i += stride) {
+        const u32x4 q = __builtin_nontemporal_load(x + i);
+        acc ^= q.x ^ q.y ^ q.z ^ q.w;
+    }
+    if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
 }
 
 std::atomic<uint32_t> g_nonce{0};
@@ -664,6 +688,13 @@ hipError_t launch_empty(hipStream_t s) {
 
 hipError_t launch_store_floor(int64_t* out, hipStream_t s) {
     hipLaunchKernelGGL(k_store_floor, dim3(1), dim3(64), 0, s, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_floor(const void* x, size_t bytes, uint32_t* out, uint32_t grid,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(k_read_floor, dim3(grid), dim3(kBlockThreads), 0, s,
+                       static_cast<const u32x4*>(x), bytes / 16, out);
     return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ struct ScanOp {
     __device__ static bool better(C a, C b) { return kMaxOp ? (a > b) : (a < b); }
     // (av, ai) := (av, ai) then (bv, bi): the later piece wins only when strictly better.
     __device__ static void combine(C& av, uint32_t& ai, C bv, uint32_t bi) {
-        const bool t = (ai == kEmpty) || better(bv, av);
+        const bool t = (ai == kEmpty) | better(bv, av);  // bitwise: no branch
         av = t ? bv : av;
         ai = t ? bi : ai;
     }
@@ -125,7 +125,7 @@ struct ScanOp {
         const bool nan = is_nan(e);
         if constexpr (std::is_floating_point<C>::value) {
             v = p == 0 ? (nan ? absorbing() : e) : (nan ? identity() : e);
-            i = (p == 0 && nan) ? kNaN0 : p;
+            i = ((p == 0) & nan) ? kNaN0 : p;
         } else {
             v = e;
             i = p;

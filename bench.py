@@ -14,7 +14,8 @@ buffer and is reported beside it). The timed region divided by K is the per-call
 (`value`). HIP events recorded around the main kernel of each call (the library's
 measurement hook) give that kernel's own per-launch duration, `kernel_event_us`, which the
 roofline divides into the algorithmic bytes. The launch floor is an empty kernel launched the same
-way. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this host
+way; the read floor (`read_floor`, read-only workloads) is a plain streaming-read kernel over
+the same rotated inputs and byte count, the practical read roofline in the same harness. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this host
 on a bounded sample of calls of the same workload.
 
 `--pmc-pass` runs a fixed sequence for hardware-counter collection instead (a 256 MiB
@@ -178,6 +179,35 @@ class Case:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs) * 1000.0 / steps
 
+    def read_floor(self, steps: int, grids=(512, 1024, 2048, 4096)) -> dict:
+        """The practical read roofline for this workload: a plain streaming-read kernel over
+        the same rotated inputs and byte count (no reduction work), fastest of a few grids."""
+        import torch
+
+        nbytes = self.w.nbytes // 16 * 16
+        sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
+        best = None
+        for grid in grids:
+            def go(i):
+                rc = self.B.argreduce_debug_launch_read(self.ptrs[i % self.n_rot], nbytes,
+                                                        sink.data_ptr(), grid, self.stream)
+                if rc != 0:
+                    raise RuntimeError(f"streaming read failed with status {rc}")
+            for i in range(20):
+                go(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                go(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / steps
+            if best is None or us < best[0]:
+                best = (us, grid)
+        return {"us_per_call": round(best[0], 3), "grid": best[1], "bytes": nbytes,
+                "gbps": round(nbytes / (best[0] * 1e-6) / 1e9, 1)}
+
     def result(self):
         import torch
 
@@ -250,6 +280,8 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     hot = c.timed(steps, warmup // 4 + 1, rotate=False)
     kus = c.kernel_timed(min(steps, 1000))
     gus = c.graph_timed(min(steps, 200), max(1, steps // 200)) if graph else None
+    # the read roofline in the same harness (read-only workloads: a scan also writes)
+    rf = c.read_floor(min(steps, 500)) if c.vals is None else None
     rec = {
         "workload": w.name, "op": op, "dtype": w.dtype, "shape": list(c.shape),
         "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
@@ -258,6 +290,8 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
         "gbps_per_call": round(c.bytes / (us * 1e-6) / 1e9, 1),
         "pct_hbm_peak_per_call": round(100 * c.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes": c.bytes, "rotated_copies": c.n_rot, "plan": c.plan,
+        "read_floor": rf,
+        "pct_of_read_floor": None if rf is None else round(100 * rf["us_per_call"] / us, 1),
         # per-launch duration of the scanning kernel itself (HIP events recorded around each
         # launch on its stream), the figure rocprofv3's kernel trace reports as well
         "roofline": roofline(c.bytes, kus, w.name if op == "max" else ""),
@@ -398,6 +432,8 @@ def main() -> int:
         "kernel_event_us": prim["kernel_event_us"],
         "launch_floor_us": round(floor, 3),
         "store_floor_us": round(store_floor, 3),
+        "read_floor": prim["read_floor"],
+        "pct_of_read_floor": prim["pct_of_read_floor"],
         "roofline": prim["roofline"],
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -264,6 +264,16 @@ int argreduce_debug_launch_empty(void *stream);
  * with no data read. Returns ARGREDUCE_OK, ARGREDUCE_ERR_INVALID_ARG or ARGREDUCE_ERR_HIP. */
 int argreduce_debug_launch_store(int64_t *out, void *stream);
 
+/* Measurement hook: the practical read roofline. Enqueues on `stream` a plain streaming
+ * read of `bytes` (a non-zero multiple of 16) at `x` (16-byte aligned device memory) by
+ * `grid` workgroups of 256 threads (1 .. 65536): grid-stride 16-byte nontemporal loads, four
+ * in flight per lane, folded with XOR. `out` (device memory of `grid` uint32 words, 4-byte
+ * aligned) is written only when a workgroup's XOR equals one fixed 32-bit pattern, so in
+ * practice nothing is written; the kernel does none of the reduction's work. Returns
+ * ARGREDUCE_OK, ARGREDUCE_ERR_INVALID_ARG or ARGREDUCE_ERR_HIP. */
+int argreduce_debug_launch_read(const void *x, size_t bytes, uint32_t *out, int64_t grid,
+                                void *stream);
+
 /* Test hook for the bounded waits (the split ArgMax path's finalizing workgroup, the scan's
  * look-back): polls of one published word before the wait gives up and the affected
  * outputs become -1 (0 restores the default, 2^20 polls). Process-wide. With a tiny limit

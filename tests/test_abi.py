@@ -124,34 +124,39 @@ def test_plan_paths_for_the_measured_shapes(mi355x):
 
 
 def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
-    """Split rows give each lane at least one 16-byte vector, cover the row in one step of
-    in-flight loads, and fill at most one wave of the device."""
+    """Split rows take the fewest 16-byte loads per lane (U) for which one step of
+    ceil(vectors / (256 U)) workgroups per row covers the row with all rows' workgroups in
+    one device wave (so no workgroup is idle), else 8 loads per lane and several steps."""
+    cap_blocks = MI355X_THREADS // 256
     for rows, cols, dtype in [(1, 32000, B.F32), (1, 202048, B.F32), (8, 202048, B.F32),
-                              (32, 202048, B.F16), (1, 2 ** 24, B.F64), (100, 50000, B.BF16)]:
+                              (32, 202048, B.F16), (64, 202048, B.BF16), (1, 2 ** 24, B.F64),
+                              (100, 50000, B.BF16), (300, 40000, B.F32), (256, 202048, B.F16)]:
         p = B.argreduce_plan(rows, cols, dtype)
-        if p["path"] != B.PATH_SPLIT:
-            continue
+        assert p["path"] == B.PATH_SPLIT, (rows, cols, p)
         esize = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}[dtype]
         vec = -(-cols * esize // 16)
-        assert p["blocks_per_row"] * 256 <= vec
-        if p["blocks_per_row"] * 256 * 8 >= vec:
-            assert p["blocks_per_row"] * 256 * p["unroll"] >= vec  # one step of loads
+        b, u = p["blocks_per_row"], p["unroll"]
+        assert p["grid_blocks"] == rows * b <= cap_blocks and p["grid_rows"] == rows
+        fits = [uu for uu in (1, 2, 4, 8) if rows * -(-vec // (256 * uu)) <= cap_blocks]
+        if fits:
+            assert u == fits[0] and b == -(-vec // (256 * u))  # one step, fewest loads
+            assert b * 256 * u >= vec > (b - 1) * 256 * u
         else:
-            assert p["unroll"] == 8  # very wide rows loop over steps of 8 vectors per lane
-        assert p["grid_blocks"] <= MI355X_THREADS // 256
-        assert p["grid_rows"] == rows
+            assert u == 8 and b == cap_blocks // 4 // rows  # several steps of 8 loads
 
 
 def test_split_is_bounded_by_capacity(lib):
-    """About two 16-byte vectors per lane, and never more workgroups than a quarter of one
-    device wave: at an H200-sized capacity (1056 workgroups of 256 threads) [1, 202048] fp32
-    uses 99 workgroups, and [32, 202048] fp32 is limited to 1056 // 4 // 32 = 8 per row."""
+    """At an H200-sized capacity (1056 workgroups of 256 threads) [1, 202048] fp32 takes one
+    vector per lane (198 workgroups), and [32, 202048] fp32 needs 8 per lane for its 32 rows
+    to fit: 25 workgroups per row, 800 in all."""
     B.argreduce_debug_set_capacity(H200_THREADS)
     p = B.argreduce_plan(1, 202048, B.F32)
-    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 99 and p["unroll"] == 2
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 198 and p["unroll"] == 1
     p = B.argreduce_plan(32, 202048, B.F32)
-    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 8 and p["unroll"] == 8
-    assert p["grid_blocks"] <= H200_THREADS // 256 // 4
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 25 and p["unroll"] == 8
+    assert p["grid_blocks"] == 800 <= H200_THREADS // 256
+    p = B.argreduce_plan(512, 202048, B.F32)  # no one-step split fits: a quarter device wave
+    assert p["path"] == B.PATH_BLOCK and p["unroll"] == 8
 
 
 def test_small_capacity_forces_row_loops(lib):
@@ -330,4 +335,13 @@ def test_forced_window(mi355x):
 def test_debug_hooks_validate(lib):
     assert B.argreduce_debug_launch_store(0, 0) == -1
     assert B.argreduce_debug_launch_store(FAKE + 4, 0) == -1
+    # the streaming-read hook: null, unaligned, ragged or empty sizes, grid out of range
+    assert B.argreduce_debug_launch_read(0, 4096, FAKE, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 4096, 0, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE + 8, 4096, FAKE, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 4100, FAKE, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 0, FAKE, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 4096, FAKE + 2, 1, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 4096, FAKE, 0, 0) == -1
+    assert B.argreduce_debug_launch_read(FAKE, 4096, FAKE, 65537, 0) == -1
     assert B.argreduce_debug_set_spin_limit(0) == 0

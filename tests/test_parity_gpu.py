@@ -374,3 +374,26 @@ def test_bounded_wait_gives_up_cleanly(oracle_lib):
             B.argreduce_debug_set_spin_limit(1)
     finally:
         B.argreduce_debug_set_spin_limit(0)
+
+
+def test_streaming_read_hook_covers_every_vector():
+    """The read-roofline kernel reads every 16-byte vector exactly where the grid-stride walk
+    says: a single word set to the kernel's store pattern is reported by the one workgroup
+    whose lanes cover it (unrolled body and ragged tail alike), and by no other."""
+    import torch
+
+    pattern = 0x9E3779B9
+    for nvec, grid, pos in ((1, 1, 0), (1000, 3, 999), (4096, 4, 1234), (1 << 20, 512, 777777),
+                            (1 << 20, 512, (1 << 20) - 1), (5 * 2048 + 17, 2, 5 * 2048 + 3)):
+        announce(f"streaming read nvec={nvec} grid={grid} pos={pos}")
+        x = torch.zeros(nvec * 4, dtype=torch.int32, device="cuda")
+        x[pos * 4 + 2] = pattern - (1 << 32)  # the 32-bit pattern as a signed int32
+        sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        assert B.argreduce_debug_launch_read(x.data_ptr(), nvec * 16, sink.data_ptr(), grid, st) == 0
+        torch.cuda.synchronize()
+        got = sink.cpu().numpy().view(np.uint32)
+        block = (pos % (grid * 256)) // 256
+        want = np.zeros(grid, dtype=np.uint32)
+        want[block] = pattern
+        assert np.array_equal(got, want), (nvec, grid, pos, got)
