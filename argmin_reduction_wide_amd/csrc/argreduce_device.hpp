@@ -340,61 +340,79 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
 // once), then tail elements; its positions therefore increase, and position 0 is the
 // first position of whichever lane visits it.
 //
-// Body vectors feed VW candidates per lane, one per element slot k of a vector, each
-// holding the position of its vector (element k is that position + k): a strict update
-// costs one compare and two selects per element. The slots and the head/tail candidate are
-// merged with the tie rule at the end. Positions are 32-bit and formed only after the
-// bounds check: the remaining count (nvec - base) is compared, never a sum that could pass
-// INT32_MAX. Byte offsets are 64-bit.
+// Per step, each lane keeps one running candidate for the step's U·VW elements, as a value
+// and the element's step slot u·VW + k (a compile-time constant, so the index select takes
+// an inline constant): one compare and two selects per element, no per-slot candidates to
+// merge afterwards. The slot becomes a position once per step and the step's candidate is
+// merged into the lane's candidate with the tie rule (every position of a step is greater
+// than those visited before it). In the last, partial step a lane past the end loads the
+// last vector again (a load under a lane condition would be a branch that makes the step's
+// loads wait on each other) and replaces it with all-ones bits, a NaN in every format,
+// which no comparison takes. Positions are 32-bit and formed only after the bounds check:
+// the remaining count (nvec - base) is compared, never a sum that could pass INT32_MAX.
+// Byte offsets are 64-bit.
 
 template <typename Fmt, int OP, int U, bool kGuard>
 __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base, uint32_t rem,
                                  uint32_t lane, uint32_t team, uint32_t head,
-                                 Cand<typename Fmt::C, OP> (&s)[Fmt::VW], bool origin) {
+                                 Cand<typename Fmt::C, OP>& c, bool origin) {
     using C = typename Fmt::C;
     using Vec = typename Fmt::Vec;
-    // In the last, partial step (kGuard) a lane past the end re-reads the last vector
-    // instead of skipping its load: a load under a lane condition becomes a branch, and the
-    // loads of a step then wait on each other. Visiting a real element again, with its own
-    // position and after every smaller position of the lane, changes no result.
-    uint32_t dd[U];
+    using K = Cand<C, OP>;
+    static_assert(U * Fmt::VW <= 64, "step slots must be inline constants");
+    constexpr uint32_t kNoSlot = 0xffffffffu;
+    Vec q[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t d = lane + static_cast<uint32_t>(u) * team;
-        dd[u] = (!kGuard || d < rem) ? d : rem - 1;
-    }
-    Vec q[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+        const uint32_t dd = (!kGuard || d < rem) ? d : rem - 1;
         q[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const Vec*>(body + static_cast<size_t>(base + dd[u]) * 16u));
+            reinterpret_cast<const Vec*>(body + static_cast<size_t>(base + dd) * 16u));
+    }
     // Issue every load of the step before any arithmetic: the scheduler would otherwise
     // interleave (and, under register pressure, wait on) loads one by one.
     __builtin_amdgcn_sched_barrier(0);
+    C lv = K::identity();
+    uint32_t ls = kNoSlot;
+    bool nan0 = false;  // last-index ops: a NaN at position 0 (taken as (NaN, slot 0))
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t d = dd[u];
-        {
-            C e[Fmt::VW];
-            Fmt::unpack(q[u], e);
-            const uint32_t pos = head + (base + d) * Fmt::VW;
-            if (u == 0) {
-                // Only the first vector of lane 0 can start at position 0 (head == 0); it is
-                // slot 0's first visit, so position 0 is taken unconditionally.
-                Cand<C, OP> t0 = s[0];
-                t0.update(e[0], pos);
-                Cand<C, OP> f0;
-                f0.take_first(e[0]);
-                const bool first = (pos == 0) && origin;
-                s[0].v = first ? f0.v : t0.v;
-                s[0].i = first ? f0.i : t0.i;
-            } else {
-                s[0].update(e[0], pos);
-            }
+        Vec qu = q[u];
+        if constexpr (kGuard) {
+            const bool past = lane + static_cast<uint32_t>(u) * team >= rem;
+            u32x4 w = __builtin_bit_cast(u32x4, qu);
+            w.x = past ? 0xffffffffu : w.x;
+            w.y = past ? 0xffffffffu : w.y;
+            w.z = past ? 0xffffffffu : w.z;
+            w.w = past ? 0xffffffffu : w.w;
+            qu = __builtin_bit_cast(Vec, w);
+        }
+        C e[Fmt::VW];
+        Fmt::unpack(qu, e);
 #pragma unroll
-            for (int k = 1; k < Fmt::VW; ++k) s[k].update(e[k], pos);
+        for (int k = 0; k < Fmt::VW; ++k) {
+            const uint32_t slot = static_cast<uint32_t>(u * Fmt::VW + k);
+            const bool t = K::kLast ? (K::better(e[k], lv) | (e[k] == lv)) : K::better(e[k], lv);
+            if (u == 0 && k == 0) {
+                // Position 0 (lane 0 of the row's first step when the row starts aligned) is
+                // the lane's first visit: taken unconditionally, as (fix(x0), 0).
+                const bool first = ((base | lane | head) == 0) & origin;
+                K f;
+                f.take_first(e[0]);
+                nan0 = K::kLast ? (first & (f.i == kNaN0Last)) : false;
+                lv = first ? f.v : (t ? e[0] : lv);
+                ls = (first | t) ? slot : ls;
+            } else {
+                lv = t ? e[k] : lv;
+                ls = t ? slot : ls;
+            }
         }
     }
+    constexpr uint32_t kShift = Fmt::VW == 8 ? 3 : (Fmt::VW == 4 ? 2 : 1);
+    const uint32_t pos = head + (base + lane + (ls >> kShift) * team) * Fmt::VW +
+                         (ls & (Fmt::VW - 1));
+    const uint32_t idx = ls == kNoSlot ? K::kNone : (nan0 ? kNaN0Last : pos);
+    c.merge(lv, idx);
 }
 
 // `origin`: false when `row` is a window of a longer row that does not start at the row's
@@ -402,11 +420,7 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
 template <typename Fmt, int OP, int U>
 __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, uint32_t lane,
                                 uint32_t team, Cand<typename Fmt::C, OP>& c, bool origin = true) {
-    using C = typename Fmt::C;
     c.init();
-    Cand<C, OP> s[Fmt::VW];
-#pragma unroll
-    for (int k = 0; k < Fmt::VW; ++k) s[k].init();
     const uint32_t misalign = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
     uint32_t head = ((16u - misalign) & 15u) / Fmt::kSize;
     head = head < cols ? head : cols;
@@ -421,9 +435,9 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
     for (uint32_t base = 0; base < nvec; base += step) {
         const uint32_t rem = nvec - base;
         if (rem >= step) {
-            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, s, origin);
+            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, c, origin);
         } else {
-            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, s, origin);
+            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, c, origin);
             break;
         }
         if (rem == step) break;
@@ -431,14 +445,6 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
 
     for (uint32_t k = tail0 + lane; k < cols; k += team)
         c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
-
-    // slot k's index is the position of its vector's first element; an empty slot stays
-    // empty (its index must not be offset)
-#pragma unroll
-    for (int k = 0; k < Fmt::VW; ++k) {
-        const uint32_t idx = s[k].i == Cand<C, OP>::kNone ? Cand<C, OP>::kNone : s[k].i + k;
-        c.merge(s[k].v, idx);
-    }
 }
 
 }  // namespace argreduce

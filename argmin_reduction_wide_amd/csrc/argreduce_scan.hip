@@ -375,6 +375,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
     uint8_t* vrow = out_val + row_off * sizeof(S);
     int64_t* irow = out_idx + row_off;
     const uint32_t tile0 = t * kTile;
+    // x[0] of the row, for positions that report a leading NaN: loaded with the tile's
+    // loads, so that it is not a dependent load after the look-back
+    S x0 = 0;
+    if constexpr (std::is_floating_point<C>::value) x0 = *reinterpret_cast<const S*>(row);
     // first position of chunk u of this lane
     auto chunk_pos = [&](int u) -> uint32_t {
         return tile0 + ((wave * U + static_cast<uint32_t>(u)) * kWave + lane) * VW;
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
 #pragma unroll
             for (int k = 1; k < VW; ++k) {
                 // strict update: NaN never wins; the padding past the row end is skipped
-                const bool b = (p0 + k < cols) && Op::better(e[k], av);
+                const bool b = (p0 + k < cols) & Op::better(e[k], av);
                 av = b ? e[k] : av;
                 ai = b ? p0 + k : ai;
             }
@@ -485,9 +489,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
     }
     Op::combine(tv, ti, wv, wi);
     const bool fail = s_fail != 0;
-    // x[0] of the row, for positions that report a leading NaN
-    S x0 = 0;
-    if constexpr (std::is_floating_point<C>::value) x0 = *reinterpret_cast<const S*>(row);
 
     // outputs
 #pragma unroll
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
 #pragma unroll
         for (int k = 0; k < VW; ++k) {
             if (k > 0) {
-                const bool b = (VECIO || p0 + k < cols) && Op::better(e[k], rv);
+                const bool b = (VECIO || p0 + k < cols) & Op::better(e[k], rv);
                 rv = b ? e[k] : rv;
                 ri = b ? p0 + k : ri;
             }
