@@ -155,15 +155,17 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
     const int64_t rows1 = rows > 0 ? rows : 1;
     // Split rows: the fewest 16-byte loads per lane (U) for which one step of
-    // B = ceil(vec_row / (256 U)) workgroups per row covers the row while the workgroups of
-    // every row fit in one device wave. A call of a few rows is latency-bound: the time after
-    // the last load arrives (the lane's compares, then the merges) grows with U, and more
-    // workgroups cost little. Failing that, 8 loads per lane and a share of the device's
-    // workgroups per row; the row then takes several steps.
+    // B = ceil(vec_row / (256 U)) workgroups per row covers the row, while the workgroups of
+    // every row fit in one device wave and the row's finalizing workgroup polls at most one
+    // published word per thread (B <= 256; a second word per thread costs a second round
+    // trip). A call of a few rows is latency-bound: the time after the last load arrives
+    // (the lane's compares, then the merges) grows with U, and more workgroups cost little.
+    // Failing that, 8 loads per lane and a share of the device's workgroups per row; the row
+    // then takes several steps.
     int64_t split_b = 0;
     for (int64_t u = 1; u <= kMaxUnrollBlocks; u *= 2) {
         const int64_t b = ceil_div(vec_row, kBlock * u);
-        if (b <= kMaxBlocksPerRow && b * rows1 <= cap_blocks) {
+        if (b <= kBlock && b * rows1 <= cap_blocks) {
             split_b = b;
             break;
         }

@@ -125,19 +125,22 @@ def test_plan_paths_for_the_measured_shapes(mi355x):
 
 def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
     """Split rows take the fewest 16-byte loads per lane (U) for which one step of
-    ceil(vectors / (256 U)) workgroups per row covers the row with all rows' workgroups in
-    one device wave (so no workgroup is idle), else 8 loads per lane and several steps."""
+    ceil(vectors / (256 U)) <= 256 workgroups per row covers the row with all rows'
+    workgroups in one device wave (so no workgroup is idle), else 8 loads per lane and
+    several steps."""
     cap_blocks = MI355X_THREADS // 256
     for rows, cols, dtype in [(1, 32000, B.F32), (1, 202048, B.F32), (8, 202048, B.F32),
                               (32, 202048, B.F16), (64, 202048, B.BF16), (1, 2 ** 24, B.F64),
-                              (100, 50000, B.BF16), (300, 40000, B.F32), (256, 202048, B.F16)]:
+                              (100, 50000, B.BF16), (300, 40000, B.F32), (256, 202048, B.F16),
+                              (1, 1 << 20, B.F32), (1, 1 << 21, B.F32)]:
         p = B.argreduce_plan(rows, cols, dtype)
         assert p["path"] == B.PATH_SPLIT, (rows, cols, p)
         esize = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}[dtype]
         vec = -(-cols * esize // 16)
         b, u = p["blocks_per_row"], p["unroll"]
         assert p["grid_blocks"] == rows * b <= cap_blocks and p["grid_rows"] == rows
-        fits = [uu for uu in (1, 2, 4, 8) if rows * -(-vec // (256 * uu)) <= cap_blocks]
+        fits = [uu for uu in (1, 2, 4, 8)
+                if -(-vec // (256 * uu)) <= 256 and rows * -(-vec // (256 * uu)) <= cap_blocks]
         if fits:
             assert u == fits[0] and b == -(-vec // (256 * u))  # one step, fewest loads
             assert b * 256 * u >= vec > (b - 1) * 256 * u
