@@ -124,6 +124,29 @@ def test_special_value_fuzz(oracle_lib, hooks, cap):
             check(oracle_lib, arr, dtype, op, f"fuzz trial={trial} cap={cap} kind={kind}")
 
 
+@pytest.mark.parametrize("dtype", ("f32", "f16"))
+def test_split_plan_boundaries(oracle_lib, hooks, dtype):
+    """Rows at the edges of the split plan's one-step rule: for U = 1, 2, 4, 8 loads per lane,
+    the widest row that B <= min(256, device wave / rows) workgroups cover in one step, and
+    one element more (the next U, or several steps), for 1 and 32 rows."""
+    rng = np.random.default_rng(66)
+    cap_blocks = B.argreduce_plan(1, 1, dtype)["device_threads"] // 256
+    for rows in (1, 32):
+        bmax = min(256, cap_blocks // rows)
+        for u in (1, 2, 4, 8):
+            edge = bmax * 256 * u * VW[dtype]
+            for cols in (edge, edge + 1):
+                p = B.argreduce_plan(rows, cols, dtype)
+                # quarter steps in [-25, 25): many ties, exact in every format
+                arr = W.to_storage(rng.integers(-100, 100, (rows, cols)) / 4.0, dtype)
+                for op in ("max", "min_last"):
+                    check(oracle_lib, arr, dtype, op,
+                          f"split edge rows={rows} u={u} cols={cols} B={p['blocks_per_row']} "
+                          f"U={p['unroll']}")
+                if cols == edge:
+                    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] * 256 * p["unroll"] * VW[dtype] >= cols
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_widths_straddling_widest_scan_step(oracle_lib, hooks, dtype):
     """cols = S-1, S, S+1 where S is the elements one scan step of a row covers."""
