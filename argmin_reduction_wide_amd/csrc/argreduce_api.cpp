@@ -280,9 +280,11 @@ int make_axis_plan(int64_t outer, int64_t len, int64_t inner, int dtype, uintptr
     p->tiles = outer * p->tiles_per_o;
     const int64_t tiles1 = p->tiles > 0 ? p->tiles : 1;
     p->unroll = (p->vec && vw == 2) ? 4 : 8;
-    // Split the axis over workgroups while the tiles leave the device's resident workgroups
-    // unfilled, but not beyond one step (unroll positions) per thread.
-    const int64_t fill = cap_blocks / tiles1;
+    // Split the axis over workgroups while the tiles leave a quarter of a device wave of
+    // workgroups unfilled, but not beyond one step (unroll positions) per thread. Filling the
+    // whole wave measured 2-22% slower (more partials, and the 100-register kernel runs only
+    // four workgroups per CU): [1,1048576,32] fp32 29.5 -> 27.7 us, [1,4096,4096] 20.3 -> 15.9.
+    const int64_t fill = cap_blocks / kSplitFillDiv / tiles1;
     const int64_t want = ceil_div(len, rows_per_tile * p->unroll);
     int64_t b = fill < want ? fill : want;
     b = b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
