@@ -1,19 +1,22 @@
 // gfx950 kernels of the last-axis ArgMax / ArgMin library and their launchers.
 //
-// Three launch shapes, after the dispatch paths of "[CUDA] Parallelize ArgMax/ArgMin over
-// wide last axes" (Description / Approach and Testing: narrow rows, one block per row,
-// several blocks per row, more rows than grid rows), re-cut for 64-lane wavefronts:
+// The last-axis launch shapes follow the dispatch paths of "[CUDA] Parallelize
+// ArgMax/ArgMin over wide last axes" (Description / Approach and Testing: narrow rows, one
+// block per row, several blocks per row, more rows than grid rows), re-cut for 64-lane
+// wavefronts:
 //
 //   k_subwave  a group of G lanes (G = 1..64, a power of two) of one wavefront per row;
 //              G = 64 is a wavefront per row. Rows beyond the grid are looped over.
 //              Narrow rows use the group idea of TVM's shared-memory reduction page
 //              ("reduction -> shared", Algorithm: group size from the reduction length,
-//              xor-shuffle tree within the group).
+//              a tree within the group; here on the DPP crossbar).
 //   k_blocks   B workgroups of 256 threads per row; B == 1 is a workgroup per row.
+//   k_wide     rows wider than INT32_MAX: one workgroup per window of at most 2^30
+//              elements (32-bit positions inside it), k_wide_merge as a second dispatch.
 //
-// and, for a reduction over a middle axis, k_axis (a tile of outputs per workgroup, the
-// axis split over B workgroups when tiles are few) with k_axis_merge as its second
-// dispatch when B > 1.
+// A reduction over a middle axis uses k_axis (a tile of outputs per workgroup, the axis
+// split over B workgroups when tiles are few) with k_axis_merge as its second dispatch when
+// B > 1. k_empty, k_store_floor and k_read_floor are the measurement hooks' kernels.
 //
 // Merging a row split over B > 1 workgroups. The page merges partials through a small
 // global buffer reduced by the last block to arrive, ordered as partial write, device-wide
@@ -46,7 +49,6 @@
 #include "argreduce_launch.hpp"
 
 namespace argreduce {
-
 
 template <typename Fmt, int OP, int G, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
@@ -148,7 +150,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
         if (threadIdx.x == 0) out[r] = s_timeout ? int64_t{-1} : Cand<C, OP>::result(m.i);
     }
 }
-
 
 // Tree merge of the TR = 256 / TL thread rows of a workgroup (TL lanes each, EPL candidates
 // per lane) through LDS: the result lands in thread row 0. Ends with a barrier, so the
@@ -471,8 +472,9 @@ __global__ void k_store_floor(int64_t* __restrict__ out) {
 // The practical read roofline: a plain grid-stride stream of 16-byte nontemporal loads
 // (four in flight per lane) folded with XOR. The store is taken only for one bit pattern,
 // so the loads cannot be removed and nothing is written in practice.
-__global__ __launch_bounds__(kBlockThreads) void k_read_floor(const u32x4* __restrict__ x, size_t nvec,
-                                                       uint32_t* __restrict__ out) {
+__global__ __launch_bounds__(kBlockThreads) void k_read_floor(const u32x4* __restrict__ x,
+                                                              size_t nvec,
+                                                              uint32_t* __restrict__ out) {
     constexpr int U = 4;
     const size_t stride = static_cast<size_t>(gridDim.x) * kBlockThreads;
     size_t i = static_cast<size_t>(blockIdx.x) * kBlockThreads + threadIdx.x;

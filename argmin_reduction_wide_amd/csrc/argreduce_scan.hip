@@ -31,8 +31,10 @@
 // published its inclusive prefix ends the walk, the aggregates of the tiles after it are
 // folded in), then publishes its inclusive prefix. Inclusive prefixes travel back one
 // window per round of polls, so the window (and the tile size) sets the rate of a long
-// row's first tiles. Wider windows (several tiles per lane) measured slower: every poll
-// round then reads several times more state words. The states are the same self-checking
+// row's first tiles. Wider windows measured slower: several tiles per lane (every poll
+// round reads several times more state words, and the registers cost occupancy), and all
+// four wavefronts polling a 256-tile window with a barrier per round. The states are the
+// same self-checking
 // words as the split ArgMax path: 64-bit agent-scope atomic stores of (nonce << 32) |
 // payload, one word per 32 bits of (index, value), each word validated on its own, so no
 // fence orders them. A fresh nonce per call makes earlier calls' words invalid; a call
