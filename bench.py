@@ -241,14 +241,25 @@ def launch_floor_us(steps: int, store: bool = False) -> float:
     return e0.elapsed_time(e1) * 1000.0 / steps
 
 
+def code_text(src: str) -> str:
+    """Source text without comments and with whitespace collapsed: what the compiler sees
+    (the sources hold no string literals with comment markers)."""
+    import re
+
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the library sources: counter figures are valid only for this build."""
+    """sha256 over the library sources' code (comments and layout excluded): counter figures
+    are valid only for this build."""
     import hashlib
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
