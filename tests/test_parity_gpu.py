@@ -201,8 +201,10 @@ def test_undersized_scratch_leaves_output_untouched():
 
 
 def test_graph_capture_and_replay(oracle_lib):
-    """Capture one call per path into a HIP graph; replay with new inputs; every replay
-    must match the oracle (the counter reset is a kernel, so it replays correctly)."""
+    """Capture one call per path into a HIP graph; replay with new inputs, with an eager call
+    on the same scratch between replays; every replay and every eager call must match the
+    oracle (the split path's finalizer clears its published words itself, so a replay, whose
+    nonce is the captured one, starts from clean words)."""
     import torch
 
     rng = np.random.default_rng(31)
@@ -237,6 +239,46 @@ def test_graph_capture_and_replay(oracle_lib):
             torch.cuda.synchronize()
             want = oracle_lib.argreduce_lastaxis(arr, dtype, "max")
             assert np.array_equal(out.cpu().numpy(), want), (rows, cols, dtype, rep)
+            # eager work between replays, on the same scratch
+            rc, got = run(x, dtype, "min_last", scratch=scratch if need else None)
+            assert rc == 0
+            assert np.array_equal(got, oracle_lib.argreduce_lastaxis(arr, dtype, "min_last")), rep
+        del g
+
+
+def test_axis_graph_capture_and_replay(oracle_lib):
+    """The middle-axis reduction captured into a HIP graph, split (two dispatches) and not,
+    replayed on new inputs with eager calls in between; every result matches the oracle."""
+    import torch
+
+    rng = np.random.default_rng(32)
+    for outer, length, inner, dtype in [(1, 1 << 16, 32, "f32"), (256, 16, 256, "f16")]:
+        tdt = {"f32": torch.float32, "f16": torch.float16}[dtype]
+        x = torch.empty((outer, length * inner), dtype=tdt, device="cuda")
+        out = torch.empty(outer * inner, dtype=torch.int64, device="cuda")
+        need = B.argreduce_axis_scratch_bytes(outer, length, inner, dtype)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        plan = B.argreduce_axis_plan(outer, length, inner, dtype)
+        announce(f"axis graph capture shape=({outer},{length},{inner}) {dtype} plan={plan}")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                rc = B.argreduce_axis(x.data_ptr(), dtype, outer, length, inner, "max",
+                                      out.data_ptr(), scratch.data_ptr(), need, s.cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        for rep in range(6):
+            arr = W.random_rows(rng, outer * length, inner, dtype, "ties").reshape(outer, length, inner)
+            x.copy_(to_device(arr.reshape(outer, length * inner), dtype))
+            torch.cuda.synchronize()
+            announce(f"axis graph replay {rep}")
+            g.replay()
+            torch.cuda.synchronize()
+            want = oracle_lib.argreduce_axis(arr, dtype, "max").reshape(-1)
+            assert np.array_equal(out.cpu().numpy(), want), (outer, length, inner, dtype, rep)
+            check_axis(oracle_lib, arr, dtype, "min", f"axis eager between replays {rep}")
         del g
 
 
@@ -308,7 +350,7 @@ def check_axis(oracle_lib, arr, dtype, op, what, **kw):
 
 # inner spans the 4 / 16 / 64-lane tiles of element loads and the 8 / 32 / 64-lane tiles of
 # 16-byte loads (an inner row of 16, 32, 48 ... bytes), ragged last tiles, and, with a long
-# axis and few outputs, both the one-dispatch (polled) and the two-dispatch split.
+# axis and few outputs, the split over several workgroups with its merge dispatch.
 AXIS_SHAPES = [(1, 1, 2), (3, 7, 3), (2, 300, 5), (4, 33, 16), (2, 1000, 17), (5, 64, 64),
                (2, 129, 100), (1, 20000, 32), (3, 5000, 4), (1, 70001, 2), (8, 512, 257),
                (2, 700, 256), (1, 3000, 520), (1, 300000, 8)]
