@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace argreduce {
 
 constexpr int kBlockThreads = 256;  // threads per workgroup of every kernel
@@ -269,8 +271,14 @@ struct Words<double> {
 
 template <int CTRL, int ROW_MASK>
 __device__ inline uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-        static_cast<int>(v), static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+    // With every row enabled each pattern used here gives every lane a source, so no
+    // "old" value (and no copy of it) is needed.
+    if constexpr (ROW_MASK == 0xf)
+        return static_cast<uint32_t>(
+            __builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+    else
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+            static_cast<int>(v), static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
 }
 template <int CTRL, int ROW_MASK>
 __device__ inline float dpp_val(float v) {
@@ -290,19 +298,72 @@ __device__ inline void dpp_merge(Cand<C, OP>& c) {
     c.merge(ov, oi);
 }
 
+// A 32-bit candidate as one 64-bit key whose unsigned order is the merge rule: the value,
+// mapped to an unsigned integer in its order (sign-magnitude to offset binary; reversed for
+// the min ops; -0 first made +0, since the two compare equal), above the index arranged so
+// that the preferred index of a tie is the larger (its complement for the first-index ops,
+// index + 1 for the last-index ones, whose empty index -1 then loses every tie). A
+// last-index leading NaN, which wins outright, is the all-ones key (no other key reaches
+// it: the largest value key is that of +inf). A merge step is then one 64-bit compare and
+// two selects. Only the value's order survives the round trip (-0 returns as +0), which is
+// all a merge or a result uses.
+template <int OP>
+struct Key32 {
+    static constexpr bool kMaxOp = op_is_max(OP);
+    static constexpr bool kLast = op_is_last(OP);
+    __device__ static uint64_t make(float v, uint32_t i) {
+        const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0 (never folded: no fast-math)
+        uint32_t hi = (u >> 31) ? ~u : (u | 0x80000000u);
+        hi = kMaxOp ? hi : ~hi;
+        const uint32_t lo = kLast ? i + 1u : ~i;
+        const uint64_t k = (static_cast<uint64_t>(hi) << 32) | lo;
+        return (kLast && i == kNaN0Last) ? ~uint64_t{0} : k;
+    }
+    __device__ static void split(uint64_t k, float& v, uint32_t& i) {
+        uint32_t hi = static_cast<uint32_t>(k >> 32);
+        const uint32_t lo = static_cast<uint32_t>(k);
+        hi = kMaxOp ? hi : ~hi;
+        v = __uint_as_float((hi >> 31) ? (hi & 0x7fffffffu) : ~hi);
+        i = kLast ? lo - 1u : ~lo;
+        if (kLast && k == ~uint64_t{0}) {
+            v = __builtin_nanf("");
+            i = kNaN0Last;
+        }
+    }
+};
+
+template <int CTRL, int ROW_MASK>
+__device__ inline uint64_t dpp_max_key(uint64_t k) {
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(k));
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(k >> 32));
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    return o > k ? o : k;
+}
+
 // Merge over aligned groups of G lanes (G a power of two <= 64). Afterwards the group's
 // last lane (lane % G == G - 1) holds the group's merged candidate; for G <= 16 every lane
 // of the group does. Steps: swap neighbours, swap pairs (quad permutes), mirror within 8,
 // mirror within 16, broadcast lane 15 of each 16-lane row into the next row (rows 1, 3),
-// broadcast lane 31 into rows 2 and 3.
+// broadcast lane 31 into rows 2 and 3. 32-bit values merge as 64-bit keys (Key32).
 template <int G, typename C, int OP>
 __device__ inline void group_merge(Cand<C, OP>& c) {
-    if constexpr (G >= 2) dpp_merge<0xB1, 0xf>(c);   // quad_perm [1,0,3,2]
-    if constexpr (G >= 4) dpp_merge<0x4E, 0xf>(c);   // quad_perm [2,3,0,1]
-    if constexpr (G >= 8) dpp_merge<0x141, 0xf>(c);  // row_half_mirror
-    if constexpr (G >= 16) dpp_merge<0x140, 0xf>(c); // row_mirror
-    if constexpr (G >= 32) dpp_merge<0x142, 0xa>(c); // row_bcast:15
-    if constexpr (G >= 64) dpp_merge<0x143, 0xc>(c); // row_bcast:31
+    if constexpr (std::is_same<C, float>::value) {
+        uint64_t k = Key32<OP>::make(c.v, c.i);
+        if constexpr (G >= 2) k = dpp_max_key<0xB1, 0xf>(k);   // quad_perm [1,0,3,2]
+        if constexpr (G >= 4) k = dpp_max_key<0x4E, 0xf>(k);   // quad_perm [2,3,0,1]
+        if constexpr (G >= 8) k = dpp_max_key<0x141, 0xf>(k);  // row_half_mirror
+        if constexpr (G >= 16) k = dpp_max_key<0x140, 0xf>(k); // row_mirror
+        if constexpr (G >= 32) k = dpp_max_key<0x142, 0xa>(k); // row_bcast:15
+        if constexpr (G >= 64) k = dpp_max_key<0x143, 0xc>(k); // row_bcast:31
+        Key32<OP>::split(k, c.v, c.i);
+    } else {
+        if constexpr (G >= 2) dpp_merge<0xB1, 0xf>(c);
+        if constexpr (G >= 4) dpp_merge<0x4E, 0xf>(c);
+        if constexpr (G >= 8) dpp_merge<0x141, 0xf>(c);
+        if constexpr (G >= 16) dpp_merge<0x140, 0xf>(c);
+        if constexpr (G >= 32) dpp_merge<0x142, 0xa>(c);
+        if constexpr (G >= 64) dpp_merge<0x143, 0xc>(c);
+    }
 }
 
 // Merge over the whole workgroup; the result is valid in thread 0. Uses LDS and two
