@@ -462,3 +462,67 @@ def test_streaming_read_hook_covers_every_vector():
         want = np.zeros(grid, dtype=np.uint32)
         want[block] = pattern
         assert np.array_equal(got, want), (nvec, grid, pos, got)
+
+
+def test_concurrent_streams_and_host_threads(oracle_lib):
+    """Split-path calls on two streams at once (separate scratch), then from four host
+    threads with a stream each: every result matches the oracle (per-call nonces keep the
+    published words of concurrent calls apart)."""
+    import threading
+
+    import torch
+
+    rng = np.random.default_rng(88)
+    cases = [(4, 202048, "f32"), (2, 300000, "bf16"), (1, 500000, "f16"), (8, 100000, "f32")]
+    arrs = [W.random_rows(rng, r, c, d, "ties") for r, c, d in cases]
+    wants = [oracle_lib.argreduce_lastaxis(a, d, "max") for a, (_, _, d) in zip(arrs, cases)]
+    xs = [to_device(a, d) for a, (_, _, d) in zip(arrs, cases)]
+    for (r, c, d) in cases:
+        assert B.argreduce_plan(r, c, d)["path"] == B.PATH_SPLIT
+
+    def call(k, stream, reps):
+        r, c, d = cases[k]
+        need = B.argreduce_scratch_bytes(r, c, d)
+        scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+        outs = []
+        for _ in range(reps):
+            out = torch.full((r,), -7, dtype=torch.int64, device="cuda")
+            rc = B.argreduce_lastaxis(xs[k].data_ptr(), d, r, c, "max", out.data_ptr(),
+                                      scratch.data_ptr(), need, stream.cuda_stream)
+            assert rc == 0
+            outs.append(out)
+        return outs
+
+    announce("two streams, interleaved split calls")
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    o0 = call(0, s0, 20)
+    o1 = call(1, s1, 20)
+    torch.cuda.synchronize()
+    for o in o0:
+        assert np.array_equal(o.cpu().numpy(), wants[0])
+    for o in o1:
+        assert np.array_equal(o.cpu().numpy(), wants[1])
+
+    announce("four host threads, a stream each")
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                results[k] = call(k, s, 10)
+            s.synchronize()
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k in range(len(cases)):
+        for o in results[k]:
+            assert np.array_equal(o.cpu().numpy(), wants[k]), k
