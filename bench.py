@@ -13,10 +13,12 @@ together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeat
 buffer and is reported beside it). The timed region divided by K is the per-call time
 (`value`). HIP events recorded around the main kernel of each call (the library's
 measurement hook) give that kernel's own per-launch duration, `kernel_event_us`, which the
-roofline divides into the algorithmic bytes. The launch floor is an empty kernel launched the same
-way; the read floor (`read_floor`, read-only workloads) is a plain streaming-read kernel over
-the same rotated inputs and byte count, the practical read roofline in the same harness. The CPU baseline is the oracle (a single-threaded sequential scan) timed on this host
-on a bounded sample of calls of the same workload.
+roofline divides into the algorithmic bytes. Ten further trials of 200 calls give the
+spread of the per-call figure (`trials_us_per_call`). The launch floor is an empty kernel
+launched the same way; the read floor (`read_floor`, read-only workloads) is a plain
+streaming-read kernel over the same rotated inputs and byte count, the practical read
+roofline in the same harness. The CPU baseline is the oracle (a single-threaded sequential
+scan) timed on this host on a bounded sample of calls of the same workload.
 
 `--pmc-pass` runs a fixed sequence for hardware-counter collection instead (a 256 MiB
 device copy, whose known bytes calibrate FETCH_SIZE / WRITE_SIZE, then 100 calls of each
@@ -117,17 +119,17 @@ class Case:
         if rc != 0:
             raise RuntimeError(f"argreduce call failed with status {rc}")
 
-    def timed(self, steps: int, warmup: int, rotate: bool = True) -> float:
-        """Microseconds per call over exactly `steps` calls."""
+    def timed(self, steps: int, warmup: int, rotate: bool = True, start: int = 0) -> float:
+        """Microseconds per call over exactly `steps` calls (rotating from copy `start`)."""
         import torch
 
         for i in range(warmup):
-            self.call(i if rotate else 0)
+            self.call(start + i if rotate else 0)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
-            self.call(i if rotate else 0)
+            self.call(start + warmup + i if rotate else 0)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / steps
@@ -288,6 +290,11 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     c = Case(w, op)
     log(f"[bench] {w.name} {op}: plan {c.plan}, {c.n_rot} rotated copies")
     us = c.timed(steps, warmup, rotate=True)
+    # ten further trials of 200 rotated calls, each continuing the rotation where the last
+    # one stopped (no copy is read again while it can still sit in the Infinity Cache):
+    # the spread of the per-call figure
+    trials = sorted(c.timed(200, 0, rotate=True, start=warmup + steps + 200 * k)
+                    for k in range(10))
     hot = c.timed(steps, warmup // 4 + 1, rotate=False)
     kus = c.kernel_timed(min(steps, 1000))
     gus = c.graph_timed(min(steps, 200), max(1, steps // 200)) if graph else None
@@ -296,6 +303,9 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     rec = {
         "workload": w.name, "op": op, "dtype": w.dtype, "shape": list(c.shape),
         "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
+        "trials_us_per_call": {"n": 10, "calls": 200, "min": round(trials[0], 3),
+                               "median": round((trials[4] + trials[5]) / 2, 3),
+                               "max": round(trials[-1], 3)},
         "graph_us_per_call": None if gus is None else round(gus, 3),
         "kernel_event_us": round(kus, 3),
         "gbps_per_call": round(c.bytes / (us * 1e-6) / 1e9, 1),
@@ -439,6 +449,7 @@ def main() -> int:
         "gbps_per_call": prim["gbps_per_call"],
         "pct_hbm_peak_per_call": prim["pct_hbm_peak_per_call"],
         "hot_us_per_call": prim["hot_us_per_call"],
+        "trials_us_per_call": prim["trials_us_per_call"],
         "graph_us_per_call": prim["graph_us_per_call"],
         "kernel_event_us": prim["kernel_event_us"],
         "launch_floor_us": round(floor, 3),
