@@ -11,8 +11,9 @@
 //     for ArgMin, index SENTINEL > any position): the identity the page prescribes;
 //   * candidates of different lanes, waves and workgroups are merged with a commutative,
 //     associative rule: the better value wins, equal values go to the lower index;
-//   * position 0 is taken unconditionally by the lane that visits it (always that lane's
-//     first visit), as the candidate (fix(x[0]), 0), where fix(NaN) is the op's absorbing
+//   * position 0 also enters as a candidate of its own, (fix(x[0]), 0), merged like any
+//     other (the merge is commutative, so this equals seeding the scan with it), where
+//     fix(NaN) is the op's absorbing
 //     value (+inf for ArgMax, -inf for ArgMin) and fix(v) = v otherwise. A NaN at
 //     position 0 then beats every other candidate, which gives the page's "leading NaN
 //     yields index 0"; a -inf (ArgMax) at position 0 is kept as a real candidate, which
@@ -64,6 +65,8 @@ struct F32 {
     using Vec = f32x4;
     static constexpr int kSize = 4;
     static constexpr int VW = 4;
+    using Bits = uint32_t;
+    __device__ static C from_bits(Bits b) { return __uint_as_float(b); }
     __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
     __device__ static void unpack(const Vec q, C (&e)[VW]) {
         e[0] = q.x;
@@ -78,6 +81,8 @@ struct F16 {
     using Vec = f16x8;
     static constexpr int kSize = 2;
     static constexpr int VW = 8;
+    using Bits = uint16_t;
+    __device__ static C from_bits(Bits b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
     __device__ static C load1(const uint8_t* p) {
         return static_cast<float>(*reinterpret_cast<const _Float16*>(p));
     }
@@ -95,8 +100,10 @@ struct BF16 {
     // bfloat16 is the upper half of a binary32: widening is a shift (exact).
     __device__ static C lo(uint32_t w) { return __uint_as_float(w << 16); }
     __device__ static C hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    using Bits = uint16_t;
+    __device__ static C from_bits(Bits b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
     __device__ static C load1(const uint8_t* p) {
-        return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+        return from_bits(*reinterpret_cast<const uint16_t*>(p));
     }
     __device__ static void unpack(const Vec q, C (&e)[VW]) {
         e[0] = lo(q.x); e[1] = hi(q.x);
@@ -111,6 +118,8 @@ struct F64 {
     using Vec = f64x2;
     static constexpr int kSize = 8;
     static constexpr int VW = 2;
+    using Bits = uint64_t;
+    __device__ static C from_bits(Bits b) { return __longlong_as_double(static_cast<long long>(b)); }
     __device__ static C load1(const uint8_t* p) { return *reinterpret_cast<const double*>(p); }
     __device__ static void unpack(const Vec q, C (&e)[VW]) {
         e[0] = q.x;
@@ -187,9 +196,9 @@ struct Cand {
     }
     // Value under which position 0 enters: NaN becomes the absorbing value.
     __device__ static C fix(C x0) { return (x0 != x0) ? absorbing() : x0; }
-    // Position 0, always the first element its lane visits: taken unconditionally, as
-    // (fix(e), 0); under the last-index ops a NaN there enters as (NaN, INT32_MAX), which
-    // no later element can replace (every comparison with NaN is false).
+    // The candidate of position 0: (fix(e), 0); under the last-index ops a NaN there
+    // enters as (NaN, INT32_MAX), which no element can replace (every comparison with NaN
+    // is false) and merges give priority.
     __device__ void take_first(C e) {
         const bool nan = (e != e);
         if constexpr (kLast) {
@@ -198,16 +207,6 @@ struct Cand {
         } else {
             v = nan ? absorbing() : e;
             i = 0u;
-        }
-    }
-    // Visit of one element by a lane, positions increasing.
-    // `origin`: position 0 of this scan is position 0 of the row (false for the windows
-    // after the first of a row wider than INT32_MAX, whose first element is ordinary).
-    __device__ void visit(C e, uint32_t pos, bool origin = true) {
-        if (pos == 0 && origin) {
-            take_first(e);
-        } else {
-            update(e, pos);
         }
     }
     // Update for positions visited in increasing order by one lane: strict comparison, or
@@ -398,8 +397,7 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
 // 16-byte boundary, a body of nvec 16-byte vectors, and a tail of up to VW-1 elements.
 // Lane `lane` takes head elements lane, lane+team, ..., then body vectors lane,
 // lane+team, ... (U vectors in flight per step, loaded nontemporally: each byte is read
-// once), then tail elements; its positions therefore increase, and position 0 is the
-// first position of whichever lane visits it.
+// once), then tail elements; its positions therefore increase.
 //
 // Per step, each lane keeps one running candidate for the step's U·VW elements, as a value
 // and the element's step slot u·VW + k (a compile-time constant, so the index select takes
@@ -416,7 +414,7 @@ __device__ inline void block_merge(Cand<C, OP>& c) {
 template <typename Fmt, int OP, int U, bool kGuard>
 __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base, uint32_t rem,
                                  uint32_t lane, uint32_t team, uint32_t head,
-                                 Cand<typename Fmt::C, OP>& c, bool origin) {
+                                 Cand<typename Fmt::C, OP>& c) {
     using C = typename Fmt::C;
     using Vec = typename Fmt::Vec;
     using K = Cand<C, OP>;
@@ -435,7 +433,6 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
     __builtin_amdgcn_sched_barrier(0);
     C lv = K::identity();
     uint32_t ls = kNoSlot;
-    bool nan0 = false;  // last-index ops: a NaN at position 0 (taken as (NaN, slot 0))
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         Vec qu = q[u];
@@ -454,34 +451,34 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
         for (int k = 0; k < Fmt::VW; ++k) {
             const uint32_t slot = static_cast<uint32_t>(u * Fmt::VW + k);
             const bool t = K::kLast ? (K::better(e[k], lv) | (e[k] == lv)) : K::better(e[k], lv);
-            if (u == 0 && k == 0) {
-                // Position 0 (lane 0 of the row's first step when the row starts aligned) is
-                // the lane's first visit: taken unconditionally, as (fix(x0), 0).
-                const bool first = ((base | lane | head) == 0) & origin;
-                K f;
-                f.take_first(e[0]);
-                nan0 = K::kLast ? (first & (f.i == kNaN0Last)) : false;
-                lv = first ? f.v : (t ? e[0] : lv);
-                ls = (first | t) ? slot : ls;
-            } else {
-                lv = t ? e[k] : lv;
-                ls = t ? slot : ls;
-            }
+            lv = t ? e[k] : lv;
+            ls = t ? slot : ls;
         }
     }
     constexpr uint32_t kShift = Fmt::VW == 8 ? 3 : (Fmt::VW == 4 ? 2 : 1);
     const uint32_t pos = head + (base + lane + (ls >> kShift) * team) * Fmt::VW +
                          (ls & (Fmt::VW - 1));
-    const uint32_t idx = ls == kNoSlot ? K::kNone : (nan0 ? kNaN0Last : pos);
-    c.merge(lv, idx);
+    c.merge(lv, ls == kNoSlot ? K::kNone : pos);
 }
 
 // `origin`: false when `row` is a window of a longer row that does not start at the row's
 // position 0 (its first element is then an ordinary element).
+//
+// Position 0 enters as its own candidate (fix(x0), 0) (for the last-index ops a NaN there
+// as (NaN, INT32_MAX)), merged into lane 0's result after the scan: the merge is
+// commutative, so this equals taking it first, and the scan's ordinary visit of position 0
+// is harmless (a NaN is never taken; any other value gives the same or a tie-losing
+// candidate). The other lanes, and every step, carry no position-0 test. Lane 0 issues
+// the seed's load (raw bits: a conversion right after it would wait for it) before the
+// scan and converts it after.
 template <typename Fmt, int OP, int U>
 __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, uint32_t lane,
                                 uint32_t team, Cand<typename Fmt::C, OP>& c, bool origin = true) {
+    using C = typename Fmt::C;
     c.init();
+    const bool seeded = origin & (lane == 0);
+    typename Fmt::Bits x0 = 0;
+    if (seeded) x0 = *reinterpret_cast<const typename Fmt::Bits*>(row);
     const uint32_t misalign = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
     uint32_t head = ((16u - misalign) & 15u) / Fmt::kSize;
     head = head < cols ? head : cols;
@@ -489,23 +486,30 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
     const uint32_t tail0 = head + nvec * Fmt::VW;
 
     for (uint32_t k = lane; k < head; k += team)
-        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
+        c.update(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
 
     const uint8_t* body = row + static_cast<size_t>(head) * Fmt::kSize;  // 16-byte aligned
     const uint32_t step = team * U;
     for (uint32_t base = 0; base < nvec; base += step) {
         const uint32_t rem = nvec - base;
         if (rem >= step) {
-            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, c, origin);
+            scan_step<Fmt, OP, U, false>(body, base, rem, lane, team, head, c);
         } else {
-            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, c, origin);
+            scan_step<Fmt, OP, U, true>(body, base, rem, lane, team, head, c);
             break;
         }
         if (rem == step) break;
     }
 
     for (uint32_t k = tail0 + lane; k < cols; k += team)
-        c.visit(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k, origin);
+        c.update(Fmt::load1(row + static_cast<size_t>(k) * Fmt::kSize), k);
+
+    if (seeded) {
+        Cand<C, OP> f;
+        asm volatile("" : "+v"(x0));  // keeps the conversion (and its wait) here
+        f.take_first(Fmt::from_bits(x0));
+        c.merge(f.v, f.i);
+    }
 }
 
 }  // namespace argreduce
