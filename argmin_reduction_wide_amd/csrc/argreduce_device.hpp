@@ -331,6 +331,39 @@ struct Key32 {
     }
 };
 
+// One step of an unsigned 32-bit maximum over the DPP pattern CTRL: a lane without a
+// source (bound_ctrl) or outside ROW_MASK takes 0, the identity, so the compiler folds the
+// move into one v_max_u32 with a DPP operand.
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp_max_u32(uint32_t h) {
+    const uint32_t o = static_cast<uint32_t>(
+        ROW_MASK == 0xf
+            ? __builtin_amdgcn_mov_dpp(static_cast<int>(h), CTRL, ROW_MASK, 0xf, true)
+            : __builtin_amdgcn_update_dpp(0, static_cast<int>(h), CTRL, ROW_MASK, 0xf, false));
+    return o > h ? o : h;
+}
+// Unsigned maximum over the 64 lanes of a wavefront, in lane 63 (the six patterns of
+// group_merge), then read out as a wave-uniform value.
+__device__ inline uint32_t wave_max_u32(uint32_t h) {
+    h = dpp_max_u32<0xB1, 0xf>(h);
+    h = dpp_max_u32<0x4E, 0xf>(h);
+    h = dpp_max_u32<0x141, 0xf>(h);
+    h = dpp_max_u32<0x140, 0xf>(h);
+    h = dpp_max_u32<0x142, 0xa>(h);
+    h = dpp_max_u32<0x143, 0xc>(h);
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(h), 63));
+}
+// The largest 64-bit key of a wavefront, in two 32-bit passes: the largest upper half,
+// then the largest lower half among the lanes that hold it. Each pass is six single
+// instructions (v_max_u32 with a DPP operand) instead of six 64-bit compare-and-select
+// steps, and the result is uniform across the wavefront.
+__device__ inline uint64_t wave_max_key(uint64_t k) {
+    const uint32_t hi = static_cast<uint32_t>(k >> 32);
+    const uint32_t top = wave_max_u32(hi);
+    const uint32_t lo = wave_max_u32(hi == top ? static_cast<uint32_t>(k) : 0u);
+    return (static_cast<uint64_t>(top) << 32) | lo;
+}
+
 template <int CTRL, int ROW_MASK>
 __device__ inline uint64_t dpp_max_key(uint64_t k) {
     const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(static_cast<uint32_t>(k));
@@ -343,10 +376,14 @@ __device__ inline uint64_t dpp_max_key(uint64_t k) {
 // last lane (lane % G == G - 1) holds the group's merged candidate; for G <= 16 every lane
 // of the group does. Steps: swap neighbours, swap pairs (quad permutes), mirror within 8,
 // mirror within 16, broadcast lane 15 of each 16-lane row into the next row (rows 1, 3),
-// broadcast lane 31 into rows 2 and 3. 32-bit values merge as 64-bit keys (Key32).
+// broadcast lane 31 into rows 2 and 3. 32-bit values merge as 64-bit keys (Key32); a whole
+// wavefront of them in two 32-bit passes (wave_max_key), which leaves the result in every
+// lane.
 template <int G, typename C, int OP>
 __device__ inline void group_merge(Cand<C, OP>& c) {
-    if constexpr (std::is_same<C, float>::value) {
+    if constexpr (std::is_same<C, float>::value && G == 64) {
+        Key32<OP>::split(wave_max_key(Key32<OP>::make(c.v, c.i)), c.v, c.i);
+    } else if constexpr (std::is_same<C, float>::value) {
         uint64_t k = Key32<OP>::make(c.v, c.i);
         if constexpr (G >= 2) k = dpp_max_key<0xB1, 0xf>(k);   // quad_perm [1,0,3,2]
         if constexpr (G >= 4) k = dpp_max_key<0x4E, 0xf>(k);   // quad_perm [2,3,0,1]
@@ -370,23 +407,37 @@ __device__ inline void group_merge(Cand<C, OP>& c) {
 template <typename C, int OP>
 __device__ inline void block_merge(Cand<C, OP>& c) {
     constexpr int kWaves = kBlockThreads / kWave;
-    __shared__ C s_v[kWaves];
-    __shared__ uint32_t s_i[kWaves];
-    group_merge<kWave>(c);
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    if (lane == kWave - 1) {
-        s_v[wave] = c.v;
-        s_i[wave] = c.i;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        c.v = s_v[0];
-        c.i = s_i[0];
+    if constexpr (std::is_same<C, float>::value) {
+        // the wavefronts' keys through LDS, merged by thread 0 as three 64-bit maxima
+        __shared__ uint64_t s_k[kWaves];
+        const uint64_t k = wave_max_key(Key32<OP>::make(c.v, c.i));
+        if (lane == 0) s_k[wave] = k;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t m = s_k[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) c.merge(s_v[w], s_i[w]);
+            for (int w = 1; w < kWaves; ++w) m = s_k[w] > m ? s_k[w] : m;
+            Key32<OP>::split(m, c.v, c.i);
+        }
+    } else {
+        __shared__ C s_v[kWaves];
+        __shared__ uint32_t s_i[kWaves];
+        group_merge<kWave>(c);
+        if (lane == kWave - 1) {
+            s_v[wave] = c.v;
+            s_i[wave] = c.i;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            c.v = s_v[0];
+            c.i = s_i[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) c.merge(s_v[w], s_i[w]);
+        }
     }
-    __syncthreads();  // s_v / s_i may be reused by the caller's next call
+    __syncthreads();  // the LDS words may be reused by the caller's next call
 }
 
 // ---------------------------------------------------------------------------------------
