@@ -36,6 +36,9 @@ def flags() -> list[str]:
         "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
         # no packed-fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # kernel arguments preloaded into SGPRs at wave launch (gfx950 supports it; the
+        # code object keeps a loading prologue for firmware that does not)
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", INCLUDE, "-I", CSRC,
     ]
 
