@@ -68,10 +68,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
 
 template <typename Fmt, int OP, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restrict__ x,
-                                                          uint32_t cols, int64_t rows,
-                                                          uint32_t B, int64_t grid_rows,
+                                                          int64_t rows, int64_t grid_rows,
                                                           int64_t* __restrict__ out,
                                                           uint64_t* __restrict__ slots,
+                                                          uint32_t cols, uint32_t B,
                                                           uint32_t nonce, uint32_t spin_limit) {
     using C = typename Fmt::C;
     __shared__ int s_timeout;
@@ -183,8 +183,8 @@ __device__ void merge_rows(Cand (&c)[EPL], C (*s_v)[kBlockThreads], uint32_t (*s
 // Workgroup id with the 8 XCDs in mind: workgroups are handed to the XCDs round-robin
 // (XCD = blockIdx % 8); this maps the ones XCD k receives onto one contiguous range of ids,
 // so that each XCD streams its own contiguous part of the tensor.
-__device__ inline uint32_t xcd_contiguous_id() {
-    const uint32_t g = gridDim.x, q = g / 8, r = g % 8, k = blockIdx.x % 8;
+__device__ inline uint32_t xcd_contiguous_id(uint32_t g) {
+    const uint32_t q = g / 8, r = g % 8, k = blockIdx.x % 8;
     return k * q + (k < r ? k : r) + blockIdx.x / 8;
 }
 
@@ -208,11 +208,10 @@ struct Partial {
 // dispatch, merges them; the kernel boundary orders the two, so nothing waits.
 template <typename Fmt, int OP, int TL, bool VEC, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restrict__ x,
-                                                        uint32_t len, int64_t inner,
-                                                        int64_t tiles_per_o, int64_t tiles,
-                                                        uint32_t B, int64_t grid_tiles,
+                                                        int64_t inner, int64_t tiles,
                                                         int64_t* __restrict__ out,
-                                                        Partial<typename Fmt::C>* __restrict__ part) {
+                                                        Partial<typename Fmt::C>* __restrict__ part,
+                                                        uint32_t len, uint32_t B, uint32_t grid) {
     using C = typename Fmt::C;
     using L = typename std::conditional<VEC, typename Fmt::Vec, C>::type;
     constexpr int TR = kBlockThreads / TL;
@@ -222,7 +221,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
     __shared__ uint32_t s_i[EPL][kBlockThreads];
     const uint32_t tl = threadIdx.x % TL;
     const uint32_t tr = threadIdx.x / TL;
-    const uint32_t id = xcd_contiguous_id();
+    const int64_t tiles_per_o = (inner + TO - 1) / TO;
+    const int64_t grid_tiles = grid / B;
+    const uint32_t id = xcd_contiguous_id(grid);
     const uint32_t b = id % B;
     const int64_t slot = id / B;
     const uint32_t rteam = B * TR;  // thread rows sharing one tile
@@ -331,8 +332,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
 // workgroup are contiguous), then the thread rows tree-merge through LDS.
 template <typename Fmt, int OP, int ML>
 __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
-    const Partial<typename Fmt::C>* __restrict__ part, uint32_t B, int64_t inner,
-    int64_t tiles_per_o, int to, int64_t tiles, int64_t* __restrict__ out) {
+    const Partial<typename Fmt::C>* __restrict__ part, int64_t* __restrict__ out, int64_t inner,
+    int64_t tiles_per_o, int64_t tiles, uint32_t B, int to, uint32_t grid) {
     using C = typename Fmt::C;
     constexpr int MR = kBlockThreads / ML;
     constexpr int kBatch = 8;
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
     const uint32_t ml = threadIdx.x % ML;
     const uint32_t mr = threadIdx.x / ML;
     const int64_t groups = (to + ML - 1) / ML;
-    for (int64_t g = blockIdx.x; g < tiles * groups; g += gridDim.x) {
+    for (int64_t g = blockIdx.x; g < tiles * groups; g += grid) {
         const int64_t t = g / groups;
         const int64_t j = (g - t * groups) * ML + ml;  // output within the tile
         const int64_t o = t / tiles_per_o;
@@ -526,8 +527,8 @@ void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                    uint64_t* slots, hipStream_t s) {
-    launch_scan(k_blocks<Fmt, OP, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, cols,
-                rows, static_cast<uint32_t>(p.blocks_per_row), p.grid_rows, out, slots,
+    launch_scan(k_blocks<Fmt, OP, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, rows,
+                p.grid_rows, out, slots, cols, static_cast<uint32_t>(p.blocks_per_row),
                 p.blocks_per_row > 1 ? next_nonce() : 0u, spin_limit());
 }
 
@@ -588,8 +589,8 @@ void launch_axis_tl(const AxisPlan& p, const uint8_t* x, int64_t* out, uint8_t* 
     P* part = reinterpret_cast<P*>(scratch16);
     const uint32_t B = static_cast<uint32_t>(p.blocks_per_tile);
     launch_scan(k_axis<Fmt, OP, TL, VEC, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
-                static_cast<uint32_t>(p.len), p.inner, p.tiles_per_o, p.tiles, B, p.grid_tiles,
-                out, B > 1 ? part : nullptr);
+                p.inner, p.tiles, out, B > 1 ? part : nullptr, static_cast<uint32_t>(p.len), B,
+                static_cast<uint32_t>(p.grid_blocks));
     if (B == 1) return;
     // lanes per output group: fewer (more thread rows) as B grows, so that every thread
     // loads at most 8 partials
@@ -599,14 +600,14 @@ void launch_axis_tl(const AxisPlan& p, const uint8_t* x, int64_t* out, uint8_t* 
     const dim3 grid(static_cast<uint32_t>(work < (int64_t{1} << 20) ? work : (int64_t{1} << 20)));
     const P* cpart = part;
     if (ml == 64)
-        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 64>), grid, dim3(kBlockThreads), 0, s, cpart, B,
-                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 64>), grid, dim3(kBlockThreads), 0, s, cpart, out,
+                           p.inner, p.tiles_per_o, p.tiles, B, static_cast<int>(p.tile), grid.x);
     else if (ml == 8)
-        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 8>), grid, dim3(kBlockThreads), 0, s, cpart, B,
-                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 8>), grid, dim3(kBlockThreads), 0, s, cpart, out,
+                           p.inner, p.tiles_per_o, p.tiles, B, static_cast<int>(p.tile), grid.x);
     else
-        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 1>), grid, dim3(kBlockThreads), 0, s, cpart, B,
-                           p.inner, p.tiles_per_o, p.tile, p.tiles, out);
+        hipLaunchKernelGGL((k_axis_merge<Fmt, OP, 1>), grid, dim3(kBlockThreads), 0, s, cpart, out,
+                           p.inner, p.tiles_per_o, p.tiles, B, static_cast<int>(p.tile), grid.x);
 }
 
 template <typename Fmt, int OP>
