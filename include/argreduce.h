@@ -109,11 +109,13 @@ size_t argreduce_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dty
  *                 success; each value lies in [0, cols).
  *   scratch       device pointer to at least argreduce_scratch_bytes(rows, cols, dtype)
  *                 bytes, at any byte alignment, with any contents on entry: a row split
- *                 over several workgroups publishes one 8-byte word per workgroup, tagged
- *                 with a per-call nonce, and the call ignores words that do not carry its
- *                 own nonce and an in-range index (arbitrary contents pass that filter with
- *                 probability below 2^-32 per word). May be NULL when that figure is 0.
- *                 The call leaves the words it used zeroed.
+ *                 over several workgroups publishes two 8-byte words per workgroup (three
+ *                 for F64), each tagged with a per-call nonce, and the call ignores words
+ *                 that do not carry its own nonce and an in-range index (arbitrary
+ *                 contents pass that filter with probability below 2^-32 per word). May be
+ *                 NULL when that figure is 0. The call leaves the words it used zeroed.
+ *                 Calls that can run at the same time (on different streams) need
+ *                 separate scratch buffers.
  *   scratch_bytes size of the scratch buffer in bytes.
  *   stream        hipStream_t on which all work is enqueued (NULL = default stream).
  *
@@ -238,7 +240,8 @@ int argreduce_axis_plan(int64_t outer, int64_t len, int64_t inner, argreduce_dty
  *   argreduce_scan_scratch_bytes gives the size (0 when every row fits in one tile;
  *   SIZE_MAX for invalid arguments). One dispatch per call; when `stream` is being
  *   captured into a HIP graph, a small kernel that clears the state words is enqueued
- *   before it, so that graph replays stay correct. Status codes as argreduce_lastaxis;
+ *   before it, so that graph replays stay correct. Calls that can run at the same time
+ *   need separate scratch buffers. Status codes as argreduce_lastaxis;
  *   ARGREDUCE_ERR_TOO_WIDE also when rows * tiles per row exceeds 2^32 - 1.
  */
 size_t argreduce_scan_scratch_bytes(int64_t rows, int64_t cols, argreduce_dtype_t dtype);
