@@ -14,7 +14,9 @@ buffer and is reported beside it). The timed region divided by K is the per-call
 (`value`). HIP events recorded around the main kernel of each call (the library's
 measurement hook) give that kernel's own per-launch duration, `kernel_event_us`, which the
 roofline divides into the algorithmic bytes. Ten further trials of 200 calls give the
-spread of the per-call figure (`trials_us_per_call`). The launch floor is an empty kernel
+spread of the per-call figure (`trials_us_per_call`); `host_enqueue_us_per_call` is the host's
+time to enqueue one call, which at these sizes is close to the GPU's time per call (the host
+launch path, not only the kernel, sets the rate). The launch floor is an empty kernel
 launched the same way; the read floor (`read_floor`, read-only workloads) is a plain
 streaming-read kernel over the same rotated inputs and byte count, the practical read
 roofline in the same harness. The CPU baseline is the oracle (a single-threaded sequential
@@ -128,8 +130,12 @@ class Case:
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
+        t0 = time.perf_counter()
         for i in range(steps):
             self.call(start + warmup + i if rotate else 0)
+        # host time to enqueue the calls: when it matches the GPU time per call, the host's
+        # launch path, not the kernel, sets the rate
+        self.host_us = (time.perf_counter() - t0) * 1e6 / steps
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / steps
@@ -220,7 +226,9 @@ class Case:
 def launch_floor_us(steps: int, store: bool = False) -> float:
     """Per-call time of an empty kernel (no arguments), or, with `store`, of a kernel that
     takes one pointer argument and stores one int64: the floor of any call that returns a
-    result (the kernel-argument path costs most of the difference)."""
+    result. The difference is the host's launch path for a kernel with arguments: the host
+    needs as long to enqueue such a launch as the GPU needs per call, and how long depends
+    on the CPU core the launching thread runs on."""
     import torch
 
     import argmin_reduction_wide_amd.binding as B
@@ -290,6 +298,7 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     c = Case(w, op)
     log(f"[bench] {w.name} {op}: plan {c.plan}, {c.n_rot} rotated copies")
     us = c.timed(steps, warmup, rotate=True)
+    host_us = c.host_us
     # ten further trials of 200 rotated calls, each continuing the rotation where the last
     # one stopped (no copy is read again while it can still sit in the Infinity Cache):
     # the spread of the per-call figure
@@ -302,7 +311,8 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     rf = c.read_floor(min(steps, 500)) if c.vals is None else None
     rec = {
         "workload": w.name, "op": op, "dtype": w.dtype, "shape": list(c.shape),
-        "us_per_call": round(us, 3), "hot_us_per_call": round(hot, 3),
+        "us_per_call": round(us, 3), "host_enqueue_us_per_call": round(host_us, 3),
+        "hot_us_per_call": round(hot, 3),
         "trials_us_per_call": {"n": 10, "calls": 200, "min": round(trials[0], 3),
                                "median": round((trials[4] + trials[5]) / 2, 3),
                                "max": round(trials[-1], 3)},
@@ -448,6 +458,7 @@ def main() -> int:
                    "rows": 1, "cols": 202048, "op": "max", "plan": prim["plan"]},
         "gbps_per_call": prim["gbps_per_call"],
         "pct_hbm_peak_per_call": prim["pct_hbm_peak_per_call"],
+        "host_enqueue_us_per_call": prim["host_enqueue_us_per_call"],
         "hot_us_per_call": prim["hot_us_per_call"],
         "trials_us_per_call": prim["trials_us_per_call"],
         "graph_us_per_call": prim["graph_us_per_call"],
