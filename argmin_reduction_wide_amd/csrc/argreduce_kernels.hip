@@ -29,7 +29,7 @@
 //     words (nonce << 32) | payload, where the nonce is a per-call value and the payloads
 //     are the index and the 32-bit halves of the value: 2 words for f32/f16/bf16 (value
 //     widened to f32), 3 for f64;
-//   * the row's workgroup with the highest id (dispatched after the others) polls the
+//   * the row's workgroup with the highest id polls the
 //     words of the other B-1 workgroups with agent-scope atomic loads until every word
 //     carries this call's nonce, merges, writes out[r], and resets the words to 0 so that
 //     a replayed HIP graph, whose nonce is fixed, starts from clean words.
@@ -37,8 +37,10 @@
 // Every word is written once and validated on its own, so no cross-location ordering (and
 // no release fence) is needed; stale or arbitrary scratch contents are ignored unless a
 // word equals this call's nonce in its upper half (and, for the index word, holds an
-// in-range index). The poll is bounded: should a word never arrive, out[r] = -1 (never
-// expected: the other workgroups of the row wait on nothing, and have lower ids).
+// in-range index). Only finalizers wait, and only on lower-numbered workgroups, which wait
+// on nothing; each XCD starts the workgroups it is given in id order, so by induction on
+// the id every wait ends, also when the grid is larger than the device. The poll is
+// bounded all the same: should a word never arrive, out[r] = -1 (never observed).
 #include <hip/hip_ext.h>
 
 #include <atomic>
