@@ -38,9 +38,11 @@
 // no release fence) is needed; stale or arbitrary scratch contents are ignored unless a
 // word equals this call's nonce in its upper half (and, for the index word, holds an
 // in-range index). Only finalizers wait, and only on lower-numbered workgroups, which wait
-// on nothing; each XCD starts the workgroups it is given in id order, so by induction on
-// the id every wait ends, also when the grid is larger than the device. The poll is
-// bounded all the same: should a word never arrive, out[r] = -1 (never observed).
+// on nothing. The automatic plans keep the grid within one device wave, so every
+// workgroup is resident at once; larger grids (forced plans) rely on each XCD starting
+// the workgroups it is given in id order, which makes every wait end by induction on the
+// id. The poll is bounded all the same: should a word never arrive, out[r] = -1 (never
+// observed).
 #include <hip/hip_ext.h>
 
 #include <atomic>

@@ -40,9 +40,11 @@
 // fence orders them. A fresh nonce per call makes earlier calls' words invalid; a call
 // captured into a HIP graph, whose nonce is fixed across replays, first clears its words
 // with a small kernel (a graph node, not a memset). Forward progress: a tile waits only
-// on tiles of lower workgroup id, which publish their aggregate without waiting; each XCD
-// starts the workgroups it is given in id order, so by induction on the id every wait
-// ends. The wait is bounded all the same (indices -1 on a timeout, never observed).
+// on tiles of lower workgroup id, which publish their aggregate without waiting. With
+// more tiles than fit on the device at once this relies on each XCD starting the
+// workgroups it is given in id order (then every wait ends, by induction on the id), the
+// assumption of any look-back scan whose tile ids are workgroup ids. The wait is bounded
+// all the same (indices -1 on a timeout, never observed).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
