@@ -1,4 +1,9 @@
-"""ctypes binding of the HIP library ``libargreduce.so`` (argument marshalling only).
+"""Python binding of the HIP library ``libargreduce.so`` (argument marshalling only).
+
+ctypes loads the library and serves every entry point; the three reduction calls go
+through a small CPython fast-call module (``_argreduce_fast``, built beside the library)
+when it is present, because a ctypes call with nine converted arguments costs about as
+much host time as the GPU spends on a small reduction.
 
 The functions carry the names of the C ABI in include/argreduce.h and take the same
 arguments (device pointers as Python ints). ``argmax`` / ``argmin`` are conveniences for
@@ -119,8 +124,41 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_debug_launch_empty.restype = c_int
                 h.argreduce_debug_set_kernel_events.argtypes = [vp, vp]
                 h.argreduce_debug_set_kernel_events.restype = c_int
+                _bind_fast(h)
                 _lib = h
     return _lib
+
+
+_fast = None
+
+
+def _bind_fast(h: ctypes.CDLL) -> None:
+    """Hand the library's reduction entry points (and launch-floor hooks) to the CPython
+    fast-call module, when it has been built: it marshals the same arguments with far less
+    host time per call than ctypes. Without it the ctypes functions serve."""
+    global _fast
+    try:
+        from . import _argreduce_fast as m
+    except ImportError:
+        return
+    addr = lambda f: ctypes.cast(f, ctypes.c_void_p).value
+    m.bind(addr(h.argreduce_lastaxis), addr(h.argreduce_axis), addr(h.argreduce_scan_lastaxis),
+           addr(h.argreduce_debug_launch_empty), addr(h.argreduce_debug_launch_store),
+           addr(h.argreduce_debug_launch_read))
+    _fast = m
+
+
+def fast():
+    """The fast-call module bound to the loaded library, or None when it is not built. Its
+    functions take the C ABI's arguments as ints (enum codes, not names)."""
+    lib()
+    return _fast
+
+
+def _entry(name: str):
+    """A reduction entry point: the fast-call one when built, else the ctypes one."""
+    h = lib()
+    return getattr(_fast, name) if _fast is not None else getattr(h, name)
 
 
 def _dtype_code(dtype) -> int:
@@ -143,8 +181,8 @@ def argreduce_scratch_bytes(rows: int, cols: int, dtype) -> int:
 def argreduce_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, out_ptr: int,
                        scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
     """Enqueue the reduction; returns the library's status code (0 = success)."""
-    return lib().argreduce_lastaxis(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
-                                    out_ptr, scratch_ptr, scratch_bytes, stream)
+    return _entry("argreduce_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
+                                        out_ptr, scratch_ptr, scratch_bytes, stream)
 
 
 def argreduce_plan(rows: int, cols: int, dtype) -> dict:
@@ -161,8 +199,8 @@ def argreduce_axis_scratch_bytes(outer: int, length: int, inner: int, dtype) -> 
 
 def argreduce_axis(x_ptr: int, dtype, outer: int, length: int, inner: int, op, out_ptr: int,
                    scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
-    return lib().argreduce_axis(x_ptr, _dtype_code(dtype), outer, length, inner, _op_code(op),
-                                out_ptr, scratch_ptr, scratch_bytes, stream)
+    return _entry("argreduce_axis")(x_ptr, _dtype_code(dtype), outer, length, inner,
+                                    _op_code(op), out_ptr, scratch_ptr, scratch_bytes, stream)
 
 
 def argreduce_axis_plan(outer: int, length: int, inner: int, dtype) -> dict:
@@ -179,8 +217,9 @@ def argreduce_scan_scratch_bytes(rows: int, cols: int, dtype) -> int:
 
 def argreduce_scan_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, values_ptr: int,
                             idx_ptr: int, scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
-    return lib().argreduce_scan_lastaxis(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
-                                         values_ptr, idx_ptr, scratch_ptr, scratch_bytes, stream)
+    return _entry("argreduce_scan_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols,
+                                             _op_code(op), values_ptr, idx_ptr, scratch_ptr,
+                                             scratch_bytes, stream)
 
 
 def argreduce_scan_plan(rows: int, cols: int, dtype) -> dict:
@@ -196,12 +235,12 @@ def argreduce_debug_set_capacity(threads: int) -> int:
 
 
 def argreduce_debug_launch_store(out_ptr: int, stream: int) -> int:
-    return lib().argreduce_debug_launch_store(out_ptr, stream)
+    return _entry("argreduce_debug_launch_store")(out_ptr, stream)
 
 
 def argreduce_debug_launch_read(x_ptr: int, nbytes: int, out_ptr: int, grid: int,
                                 stream: int) -> int:
-    return lib().argreduce_debug_launch_read(x_ptr, nbytes, out_ptr, grid, stream)
+    return _entry("argreduce_debug_launch_read")(x_ptr, nbytes, out_ptr, grid, stream)
 
 
 def argreduce_debug_set_spin_limit(polls: int) -> int:
@@ -217,7 +256,7 @@ def argreduce_debug_force_path(path: int) -> int:
 
 
 def argreduce_debug_launch_empty(stream: int) -> int:
-    return lib().argreduce_debug_launch_empty(stream)
+    return _entry("argreduce_debug_launch_empty")(stream)
 
 
 def argreduce_debug_set_kernel_events(start: int, stop: int) -> int:

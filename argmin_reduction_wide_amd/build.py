@@ -43,6 +43,33 @@ def flags() -> list[str]:
     ]
 
 
+def fast_binding_path() -> str:
+    import sysconfig
+
+    return os.path.join(PKG, "_argreduce_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
+
+
+def build_fast_binding(verbose: bool = False) -> str:
+    """Compile the CPython fast-call marshalling module (host C, no device code) next to the
+    library; it links against the Python runtime only."""
+    import sysconfig
+
+    out = fast_binding_path()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the fast-call binding")
+    cmd = [cc, "-O2", "-std=c11", "-fPIC", "-shared", "-fvisibility=hidden",
+           "-I", sysconfig.get_paths()["include"], "-I", INCLUDE,
+           os.path.join(CSRC, "argreduce_pyfast.c"), "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"fast-call binding failed ({proc.returncode}):\n{proc.stderr[-4000:]}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every source to an object (in parallel), then link the shared library."""
     objdir = os.path.join(os.path.dirname(out), "_build")
@@ -77,3 +104,4 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_fast_binding(verbose="-v" in sys.argv))

@@ -89,35 +89,40 @@ class Case:
             n_out = self.rows * self.cols
             self.shape = (self.rows, self.cols)
             self.need = B.argreduce_scan_scratch_bytes(self.rows, self.cols, w.dtype)
-            self.fn = B.lib().argreduce_scan_lastaxis
+            self.fn = B._entry("argreduce_scan_lastaxis")
             self.plan = B.argreduce_scan_plan(self.rows, self.cols, w.dtype)
             self.vals = torch.empty((self.rows, self.cols), dtype=tdt, device="cuda")
         elif w.axis_shape is None:
             n_out = self.rows
             self.shape = (self.rows, self.cols)
             self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
-            self.fn = B.lib().argreduce_lastaxis
+            self.fn = B._entry("argreduce_lastaxis")
             self.plan = B.argreduce_plan(self.rows, self.cols, w.dtype)
         else:
             outer, length, inner = w.axis_shape
             n_out = outer * inner
             self.shape = (outer, length, inner)
             self.need = B.argreduce_axis_scratch_bytes(outer, length, inner, w.dtype)
-            self.fn = B.lib().argreduce_axis
+            self.fn = B._entry("argreduce_axis")
             self.plan = B.argreduce_axis_plan(outer, length, inner, w.dtype)
         self.out = torch.empty(n_out, dtype=torch.int64, device="cuda")
         self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
+        self.binding = "cpython-fastcall" if B.fast() is not None else "ctypes"
+        self._argv_cache = None
         # input read once, one int64 per output (and, for a scan, one value per element)
         self.bytes = w.nbytes + n_out * 8 + (w.nbytes if self.vals is not None else 0)
 
+    def argv(self, k: int) -> tuple:
+        """The C call's arguments for rotated copy k (built once per copy and stream)."""
+        if self._argv_cache is None or self._argv_cache[0] != self.stream:
+            tail = ((self.vals.data_ptr(),) if self.vals is not None else ()) + (
+                self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
+            self._argv_cache = (self.stream, [(p, self.dt, *self.shape, self.opc, *tail)
+                                              for p in self.ptrs])
+        return self._argv_cache[1][k]
+
     def call(self, i: int) -> None:
-        if self.vals is not None:
-            rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
-                         self.vals.data_ptr(), self.out.data_ptr(), self.scratch.data_ptr(),
-                         self.need, self.stream)
-        else:
-            rc = self.fn(self.ptrs[i % self.n_rot], self.dt, *self.shape, self.opc,
-                         self.out.data_ptr(), self.scratch.data_ptr(), self.need, self.stream)
+        rc = self.fn(*self.argv(i % self.n_rot))
         if rc != 0:
             raise RuntimeError(f"argreduce call failed with status {rc}")
 
@@ -196,9 +201,11 @@ class Case:
         sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
         best = None
         for grid in grids:
+            read = self.B._entry("argreduce_debug_launch_read")
+            sink_ptr = sink.data_ptr()
+
             def go(i):
-                rc = self.B.argreduce_debug_launch_read(self.ptrs[i % self.n_rot], nbytes,
-                                                        sink.data_ptr(), grid, self.stream)
+                rc = read(self.ptrs[i % self.n_rot], nbytes, sink_ptr, grid, self.stream)
                 if rc != 0:
                     raise RuntimeError(f"streaming read failed with status {rc}")
             for i in range(20):
@@ -236,9 +243,11 @@ def launch_floor_us(steps: int, store: bool = False) -> float:
     stream = torch.cuda.current_stream().cuda_stream
     if store:
         out = torch.zeros(1, dtype=torch.int64, device="cuda")
-        f = lambda st: B.lib().argreduce_debug_launch_store(out.data_ptr(), st)
+        out_ptr = out.data_ptr()
+        g = B._entry("argreduce_debug_launch_store")
+        f = lambda st: g(out_ptr, st)
     else:
-        f = B.lib().argreduce_debug_launch_empty
+        f = B._entry("argreduce_debug_launch_empty")
     for _ in range(50):
         f(stream)
     torch.cuda.synchronize()
@@ -312,6 +321,7 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     rec = {
         "workload": w.name, "op": op, "dtype": w.dtype, "shape": list(c.shape),
         "us_per_call": round(us, 3), "host_enqueue_us_per_call": round(host_us, 3),
+        "binding": c.binding,
         "hot_us_per_call": round(hot, 3),
         "trials_us_per_call": {"n": 10, "calls": 200, "min": round(trials[0], 3),
                                "median": round((trials[4] + trials[5]) / 2, 3),
@@ -459,6 +469,7 @@ def main() -> int:
         "gbps_per_call": prim["gbps_per_call"],
         "pct_hbm_peak_per_call": prim["pct_hbm_peak_per_call"],
         "host_enqueue_us_per_call": prim["host_enqueue_us_per_call"],
+        "binding": prim["binding"],
         "hot_us_per_call": prim["hot_us_per_call"],
         "trials_us_per_call": prim["trials_us_per_call"],
         "graph_us_per_call": prim["graph_us_per_call"],
