@@ -9,6 +9,9 @@
  * with nine converted arguments takes about 2 us of host time, which is as long as the
  * GPU needs for a small reduction; a METH_FASTCALL function takes a small fraction of it.
  *
+ * The reduction calls release the GIL while the library enqueues (as ctypes does), so host
+ * threads can launch side by side.
+ *
  * Return value: the library's status code as a Python int. A Python argument that is not
  * an int in range raises TypeError / OverflowError before the library is called; calling
  * before bind() raises RuntimeError.
@@ -71,8 +74,12 @@ static PyObject *fast_lastaxis(PyObject *self, PyObject *const *a, Py_ssize_t n)
     const size_t sbytes = PyLong_AsSize_t(a[7]);
     void *stream = arg_ptr(a[8]);
     if (PyErr_Occurred()) return NULL;
-    return PyLong_FromLong(g_lastaxis(x, (argreduce_dtype_t)dtype, (int64_t)rows, (int64_t)cols,
-                                      (argreduce_op_t)op, out, scratch, sbytes, stream));
+    int rc;
+    Py_BEGIN_ALLOW_THREADS
+    rc = g_lastaxis(x, (argreduce_dtype_t)dtype, (int64_t)rows, (int64_t)cols,
+                    (argreduce_op_t)op, out, scratch, sbytes, stream);
+    Py_END_ALLOW_THREADS
+    return PyLong_FromLong(rc);
 }
 
 /* argreduce_axis(x, dtype, outer, len, inner, op, out_idx, scratch, scratch_bytes, stream) */
@@ -90,9 +97,12 @@ static PyObject *fast_axis(PyObject *self, PyObject *const *a, Py_ssize_t n) {
     const size_t sbytes = PyLong_AsSize_t(a[8]);
     void *stream = arg_ptr(a[9]);
     if (PyErr_Occurred()) return NULL;
-    return PyLong_FromLong(g_axis(x, (argreduce_dtype_t)dtype, (int64_t)outer, (int64_t)len,
-                                  (int64_t)inner, (argreduce_op_t)op, out, scratch, sbytes,
-                                  stream));
+    int rc;
+    Py_BEGIN_ALLOW_THREADS
+    rc = g_axis(x, (argreduce_dtype_t)dtype, (int64_t)outer, (int64_t)len, (int64_t)inner,
+                (argreduce_op_t)op, out, scratch, sbytes, stream);
+    Py_END_ALLOW_THREADS
+    return PyLong_FromLong(rc);
 }
 
 /* argreduce_scan_lastaxis(x, dtype, rows, cols, op, out_values, out_idx, scratch,
@@ -112,8 +122,12 @@ static PyObject *fast_scan(PyObject *self, PyObject *const *a, Py_ssize_t n) {
     const size_t sbytes = PyLong_AsSize_t(a[8]);
     void *stream = arg_ptr(a[9]);
     if (PyErr_Occurred()) return NULL;
-    return PyLong_FromLong(g_scan(x, (argreduce_dtype_t)dtype, (int64_t)rows, (int64_t)cols,
-                                  (argreduce_op_t)op, values, out, scratch, sbytes, stream));
+    int rc;
+    Py_BEGIN_ALLOW_THREADS
+    rc = g_scan(x, (argreduce_dtype_t)dtype, (int64_t)rows, (int64_t)cols, (argreduce_op_t)op,
+                values, out, scratch, sbytes, stream);
+    Py_END_ALLOW_THREADS
+    return PyLong_FromLong(rc);
 }
 
 /* The measurement hooks, marshalled the same way so that their floors carry the same

@@ -526,3 +526,58 @@ def test_concurrent_streams_and_host_threads(oracle_lib):
     for k in range(len(cases)):
         for o in results[k]:
             assert np.array_equal(o.cpu().numpy(), wants[k]), k
+
+
+def test_fast_call_and_ctypes_marshalling_agree(oracle_lib):
+    """The same calls through the CPython fast-call module and through ctypes give the
+    oracle's results on every path kind (split, workgroup, lane group, middle axis, scan)."""
+    import torch
+
+    fast = B.fast()
+    assert fast is not None, "the fast-call module is built with the library"
+    h = B.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(91)
+    for rows, cols, dtype, op in [(3, 202048, "f32", "max"), (64, 4096, "f16", "min_last"),
+                                  (1000, 64, "bf16", "max"), (2, 300000, "f64", "min")]:
+        announce(f"marshalling lastaxis [{rows},{cols}] {dtype} {op}")
+        arr = W.random_rows(rng, rows, cols, dtype, "ties")
+        x = to_device(arr, dtype)
+        need = B.argreduce_scratch_bytes(rows, cols, dtype)
+        scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        want = oracle_lib.argreduce_lastaxis(arr, dtype, op)
+        for fn in (fast.argreduce_lastaxis, h.argreduce_lastaxis):
+            out = torch.full((rows,), -7, dtype=torch.int64, device="cuda")
+            rc = fn(x.data_ptr(), B.DTYPE_NAMES[dtype], rows, cols, B.OP_NAMES[op],
+                    out.data_ptr(), scratch.data_ptr(), need, stream)
+            torch.cuda.synchronize()
+            assert rc == 0 and np.array_equal(out.cpu().numpy(), want), fn
+
+    announce("marshalling axis [4,3000,40] f32 max")
+    arr = W.random_rows(rng, 4 * 3000, 40, "f32", "ties").reshape(4, 3000, 40)
+    x = to_device(arr, "f32")
+    need = B.argreduce_axis_scratch_bytes(4, 3000, 40, "f32")
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    want = oracle_lib.argreduce_axis(arr, "f32", "max").reshape(-1)
+    for fn in (fast.argreduce_axis, h.argreduce_axis):
+        out = torch.full((4 * 40,), -7, dtype=torch.int64, device="cuda")
+        rc = fn(x.data_ptr(), B.F32, 4, 3000, 40, B.MAX, out.data_ptr(), scratch.data_ptr(),
+                need, stream)
+        torch.cuda.synchronize()
+        assert rc == 0 and np.array_equal(out.cpu().numpy(), want), fn
+
+    announce("marshalling scan [2,50000] i64 cummax")
+    arr = rng.integers(-1000, 1000, size=(2, 50000), dtype=np.int64)
+    x = torch.from_numpy(arr.copy()).cuda()
+    need = B.argreduce_scan_scratch_bytes(2, 50000, "i64")
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    want_v, want_i = oracle_lib.cumulative(arr, "i64", "max")
+    for fn in (fast.argreduce_scan_lastaxis, h.argreduce_scan_lastaxis):
+        vals = torch.empty_like(x)
+        idx = torch.full((2, 50000), -7, dtype=torch.int64, device="cuda")
+        rc = fn(x.data_ptr(), B.I64, 2, 50000, B.MAX, vals.data_ptr(), idx.data_ptr(),
+                scratch.data_ptr(), need, stream)
+        torch.cuda.synchronize()
+        assert rc == 0, fn
+        assert np.array_equal(idx.cpu().numpy(), want_i.reshape(2, 50000)), fn
+        assert np.array_equal(vals.cpu().numpy(), want_v.reshape(2, 50000)), fn
