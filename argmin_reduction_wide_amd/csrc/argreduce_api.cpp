@@ -343,9 +343,27 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
     *p = ScanPlan{};
     p->rows = rows;
     p->cols = cols;
-    // U = 8 only for rows of many U = 4 tiles (there the look-back's depth matters; with a
-    // few tiles per row, the smaller tile keeps more workgroups in flight)
-    p->unroll = cols <= 64 * kBlock * kScanUnrollShort * (16 / es) ? kScanUnrollShort : kScanUnrollLong;
+    // Tile size (U 16-byte chunks per lane). A row that fits one tile of U <= 2 takes the
+    // smallest tile that holds it whole (no look-back: a second tile costs a handoff). A
+    // longer row takes U = 1 while it needs at most 64 such tiles and the grid stays within
+    // two device waves of workgroups (more, smaller tiles: more loads in flight, the
+    // look-back still one round), else U = 2 under the same 64-tile bound, else U = 8 (the
+    // look-back's depth matters). Measured against U = 4 for every short row: [1,65536]
+    // int64 5.9 -> 5.35 us, fp32 6.0 -> 4.1, [64,1024] int64 4.0 -> 3.2, [1024,64] int64
+    // 4.4 -> 3.0, [4096,1024] fp32 15.5 -> 12.7, [4096,4096] fp32 48.9 -> 45.5 (U = 2, two
+    // tiles per row; U = 1 with four: 52.7).
+    const int64_t vec_elems = 16 / es;
+    const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
+    const auto tiles_of = [&](int64_t u) { return ceil_div(cols, kBlock * u * vec_elems); };
+    const int64_t t1 = tiles_of(kScanUnrollTiny), t2 = tiles_of(kScanUnrollShort);
+    if (t2 == 1)
+        p->unroll = t1 == 1 ? kScanUnrollTiny : kScanUnrollShort;
+    else if (t1 <= 64 && rows <= 2 * cap_blocks / t1)
+        p->unroll = kScanUnrollTiny;
+    else if (t2 <= 64)
+        p->unroll = kScanUnrollShort;
+    else
+        p->unroll = kScanUnrollLong;
     p->tile_elems = kBlock * p->unroll * (16 / es);
     p->tiles_per_row = ceil_div(cols, p->tile_elems);
     if (rows > 0 && rows > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / p->tiles_per_row)

@@ -42,9 +42,11 @@ struct AxisPlan {
 };
 
 // Cumulative extremum with indices (cummax / cummin) along the last axis.
-// 16-byte chunks per lane per tile: 4, or 8 for rows of more than 64 such tiles (bigger
-// tiles: fewer tiles for the look-back to walk through).
-constexpr int kScanUnrollShort = 4;
+// 16-byte chunks per lane per tile: 1 or 2 while a row needs at most 64 tiles of that size,
+// 8 for longer rows (bigger tiles: fewer tiles for the look-back to walk through). The
+// choice between them is the scan plan's.
+constexpr int kScanUnrollTiny = 1;
+constexpr int kScanUnrollShort = 2;
 constexpr int kScanUnrollLong = 8;
 
 struct ScanPlan {

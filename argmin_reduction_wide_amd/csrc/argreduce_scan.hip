@@ -595,8 +595,12 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     uint8_t* vb = static_cast<uint8_t*>(out_val);
     const uint32_t cols = static_cast<uint32_t>(p.cols);
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
-    constexpr int US = kScanUnrollShort, UL = kScanUnrollLong;
-    if (p.unroll == US && p.vecio)
+    constexpr int UT = kScanUnrollTiny, US = kScanUnrollShort, UL = kScanUnrollLong;
+    if (p.unroll == UT && p.vecio)
+        launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+    else if (p.unroll == UT)
+        launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+    else if (p.unroll == US && p.vecio)
         launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == US)
         launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());

@@ -270,21 +270,31 @@ def test_other_entry_points_refuse_integers(lib):
 
 
 def test_scan_plans_and_scratch(mi355x):
-    # tiles: 256 lanes x U chunks of 16 bytes; U = 8 for rows of more than 64 U = 4 tiles
-    p = B.argreduce_scan_plan(1, 65536, B.I64)
-    assert p["path"] == B.PATH_SCAN and p["unroll"] == 4 and p["outputs_per_block"] == 2048
-    assert p["blocks_per_row"] == 32 and p["grid_blocks"] == 32 and p["load_bytes"] == 16
-    assert p["scratch_bytes"] == 15 + 32 * 2 * 4 * 8  # aggregate + prefix, 4 words each
+    # tiles: 256 lanes x U chunks of 16 bytes. A row that fits one tile of U <= 2 takes the
+    # smallest such tile; else U = 1 while a row needs <= 64 tiles and the grid stays within
+    # two device waves, else U = 2 within 64 tiles, else U = 8.
+    p = B.argreduce_scan_plan(1, 65536, B.I64)  # 128 tiles of U = 1: U = 2
+    assert p["path"] == B.PATH_SCAN and p["unroll"] == 2 and p["outputs_per_block"] == 1024
+    assert p["blocks_per_row"] == 64 and p["grid_blocks"] == 64 and p["load_bytes"] == 16
+    assert p["scratch_bytes"] == 15 + 64 * 2 * 4 * 8  # aggregate + prefix, 4 words each
     assert B.argreduce_scan_scratch_bytes(1, 65536, B.I64) == p["scratch_bytes"]
-    p = B.argreduce_scan_plan(4096, 4096, B.F32)  # one tile per row: no look-back, no scratch
-    assert p["unroll"] == 4 and p["outputs_per_block"] == 4096
-    assert p["blocks_per_row"] == 1 and p["grid_blocks"] == 4096 and p["scratch_bytes"] == 0
+    p = B.argreduce_scan_plan(1, 65536, B.F32)  # 64 tiles of U = 1
+    assert p["unroll"] == 1 and p["outputs_per_block"] == 1024 and p["blocks_per_row"] == 64
+    p = B.argreduce_scan_plan(4096, 1024, B.F32)  # one U = 1 tile per row: no look-back
+    assert p["unroll"] == 1 and p["blocks_per_row"] == 1 and p["scratch_bytes"] == 0
+    p = B.argreduce_scan_plan(64, 1024, B.I64)  # one U = 2 tile rather than two U = 1 tiles
+    assert p["unroll"] == 2 and p["blocks_per_row"] == 1 and p["scratch_bytes"] == 0
+    p = B.argreduce_scan_plan(4096, 4096, B.F32)  # U = 1 would make 16384 workgroups
+    assert p["unroll"] == 2 and p["outputs_per_block"] == 2048
+    assert p["blocks_per_row"] == 2 and p["grid_blocks"] == 8192
+    assert p["scratch_bytes"] == B.argreduce_scan_scratch_bytes(4096, 4096, B.F32) > 0
     p = B.argreduce_scan_plan(3, 8193, B.F16)
-    assert p["outputs_per_block"] == 8192 and p["blocks_per_row"] == 2 and p["load_bytes"] == 2
-    assert p["scratch_bytes"] == 15 + 3 * 2 * 2 * 2 * 8
+    assert p["unroll"] == 1 and p["outputs_per_block"] == 2048 and p["blocks_per_row"] == 5
+    assert p["load_bytes"] == 2 and p["scratch_bytes"] == 15 + 3 * 5 * 2 * 2 * 8
     p = B.argreduce_scan_plan(1, 64 * 4096 + 1, B.F32)
     assert p["unroll"] == 8 and p["outputs_per_block"] == 8192 and p["blocks_per_row"] == 33
-    assert B.argreduce_scan_plan(1, 64 * 4096, B.F32)["unroll"] == 4
+    assert B.argreduce_scan_plan(1, 64 * 2048, B.F32)["unroll"] == 2
+    assert B.argreduce_scan_plan(1, 64 * 2048 + 1, B.F32)["unroll"] == 8
     assert B.argreduce_scan_plan(2, 1 << 24, B.F32)["blocks_per_row"] == 2048
     assert B.argreduce_scan_scratch_bytes(2, 0, B.F32) == B.SIZE_MAX
     assert B.argreduce_scan_scratch_bytes(2, 8, 9) == B.SIZE_MAX

@@ -91,11 +91,12 @@ def check_scan(oracle_lib, arr: np.ndarray, dtype: str, op: str, what: str, **kw
     return got_v, got_i
 
 
-# rows of 1 .. several tiles (a tile is 4096 f32 / 8192 f16 / 2048 64-bit elements, twice
-# that for rows of more than 64 such tiles), row lengths that are not multiples of a
-# 16-byte chunk
-SHAPES = [(1, 1), (1, 7), (3, 5), (2, 100), (4, 2047), (2, 2048), (3, 2049), (1, 4095),
-          (2, 4096), (1, 4097), (2, 8191), (1, 8193), (1, 20000), (3, 65536), (1, 140001)]
+# rows of 1 .. many tiles and across the tile-size choices (a U = 1 tile is 1024 f32 /
+# 2048 f16 / 512 64-bit elements, U = 2 twice that, U = 8 eight times), row lengths that are
+# not multiples of a 16-byte chunk
+SHAPES = [(1, 1), (1, 7), (3, 5), (2, 100), (2, 511), (2, 513), (1, 1023), (1, 1025),
+          (4, 2047), (2, 2048), (3, 2049), (1, 4095), (2, 4096), (1, 4097), (2, 8191),
+          (1, 8193), (1, 20000), (3, 65536), (1, 65537), (1, 131073), (1, 140001)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
