@@ -155,7 +155,7 @@ def fast():
     return _fast
 
 
-def _entry(name: str):
+def entry_point(name: str):
     """A reduction entry point: the fast-call one when built, else the ctypes one."""
     h = lib()
     return getattr(_fast, name) if _fast is not None else getattr(h, name)
@@ -181,7 +181,7 @@ def argreduce_scratch_bytes(rows: int, cols: int, dtype) -> int:
 def argreduce_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, out_ptr: int,
                        scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
     """Enqueue the reduction; returns the library's status code (0 = success)."""
-    return _entry("argreduce_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
+    return entry_point("argreduce_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
                                         out_ptr, scratch_ptr, scratch_bytes, stream)
 
 
@@ -199,7 +199,7 @@ def argreduce_axis_scratch_bytes(outer: int, length: int, inner: int, dtype) -> 
 
 def argreduce_axis(x_ptr: int, dtype, outer: int, length: int, inner: int, op, out_ptr: int,
                    scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
-    return _entry("argreduce_axis")(x_ptr, _dtype_code(dtype), outer, length, inner,
+    return entry_point("argreduce_axis")(x_ptr, _dtype_code(dtype), outer, length, inner,
                                     _op_code(op), out_ptr, scratch_ptr, scratch_bytes, stream)
 
 
@@ -217,7 +217,7 @@ def argreduce_scan_scratch_bytes(rows: int, cols: int, dtype) -> int:
 
 def argreduce_scan_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, values_ptr: int,
                             idx_ptr: int, scratch_ptr: int, scratch_bytes: int, stream: int) -> int:
-    return _entry("argreduce_scan_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols,
+    return entry_point("argreduce_scan_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols,
                                              _op_code(op), values_ptr, idx_ptr, scratch_ptr,
                                              scratch_bytes, stream)
 
@@ -235,12 +235,12 @@ def argreduce_debug_set_capacity(threads: int) -> int:
 
 
 def argreduce_debug_launch_store(out_ptr: int, stream: int) -> int:
-    return _entry("argreduce_debug_launch_store")(out_ptr, stream)
+    return entry_point("argreduce_debug_launch_store")(out_ptr, stream)
 
 
 def argreduce_debug_launch_read(x_ptr: int, nbytes: int, out_ptr: int, grid: int,
                                 stream: int) -> int:
-    return _entry("argreduce_debug_launch_read")(x_ptr, nbytes, out_ptr, grid, stream)
+    return entry_point("argreduce_debug_launch_read")(x_ptr, nbytes, out_ptr, grid, stream)
 
 
 def argreduce_debug_set_spin_limit(polls: int) -> int:
@@ -256,7 +256,7 @@ def argreduce_debug_force_path(path: int) -> int:
 
 
 def argreduce_debug_launch_empty(stream: int) -> int:
-    return _entry("argreduce_debug_launch_empty")(stream)
+    return entry_point("argreduce_debug_launch_empty")(stream)
 
 
 def argreduce_debug_set_kernel_events(start: int, stop: int) -> int:

@@ -89,21 +89,21 @@ class Case:
             n_out = self.rows * self.cols
             self.shape = (self.rows, self.cols)
             self.need = B.argreduce_scan_scratch_bytes(self.rows, self.cols, w.dtype)
-            self.fn = B._entry("argreduce_scan_lastaxis")
+            self.fn = B.entry_point("argreduce_scan_lastaxis")
             self.plan = B.argreduce_scan_plan(self.rows, self.cols, w.dtype)
             self.vals = torch.empty((self.rows, self.cols), dtype=tdt, device="cuda")
         elif w.axis_shape is None:
             n_out = self.rows
             self.shape = (self.rows, self.cols)
             self.need = B.argreduce_scratch_bytes(self.rows, self.cols, w.dtype)
-            self.fn = B._entry("argreduce_lastaxis")
+            self.fn = B.entry_point("argreduce_lastaxis")
             self.plan = B.argreduce_plan(self.rows, self.cols, w.dtype)
         else:
             outer, length, inner = w.axis_shape
             n_out = outer * inner
             self.shape = (outer, length, inner)
             self.need = B.argreduce_axis_scratch_bytes(outer, length, inner, w.dtype)
-            self.fn = B._entry("argreduce_axis")
+            self.fn = B.entry_point("argreduce_axis")
             self.plan = B.argreduce_axis_plan(outer, length, inner, w.dtype)
         self.out = torch.empty(n_out, dtype=torch.int64, device="cuda")
         self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
@@ -201,7 +201,7 @@ class Case:
         sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
         best = None
         for grid in grids:
-            read = self.B._entry("argreduce_debug_launch_read")
+            read = self.B.entry_point("argreduce_debug_launch_read")
             sink_ptr = sink.data_ptr()
 
             def go(i):
@@ -244,10 +244,10 @@ def launch_floor_us(steps: int, store: bool = False) -> float:
     if store:
         out = torch.zeros(1, dtype=torch.int64, device="cuda")
         out_ptr = out.data_ptr()
-        g = B._entry("argreduce_debug_launch_store")
+        g = B.entry_point("argreduce_debug_launch_store")
         f = lambda st: g(out_ptr, st)
     else:
-        f = B._entry("argreduce_debug_launch_empty")
+        f = B.entry_point("argreduce_debug_launch_empty")
     for _ in range(50):
         f(stream)
     torch.cuda.synchronize()

@@ -23,9 +23,9 @@ def fast():
 
 
 def test_reductions_route_through_the_fast_module(fast):
-    assert B._entry("argreduce_lastaxis") is fast.argreduce_lastaxis
-    assert B._entry("argreduce_axis") is fast.argreduce_axis
-    assert B._entry("argreduce_scan_lastaxis") is fast.argreduce_scan_lastaxis
+    assert B.entry_point("argreduce_lastaxis") is fast.argreduce_lastaxis
+    assert B.entry_point("argreduce_axis") is fast.argreduce_axis
+    assert B.entry_point("argreduce_scan_lastaxis") is fast.argreduce_scan_lastaxis
 
 
 LASTAXIS_CASES = [
