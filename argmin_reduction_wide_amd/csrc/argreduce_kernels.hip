@@ -333,7 +333,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
 // Second dispatch of a split middle-axis reduction. Workgroup g takes ML consecutive
 // outputs of one tile (g = tile * groups + group): lane ml owns an output, the 256 / ML
 // thread rows share out its B partials (coalesced: the partials of one first-dispatch
-// workgroup are contiguous), then the thread rows tree-merge through LDS.
+// workgroup are contiguous), then the thread rows tree-merge through LDS (with one output
+// per workgroup, ML = 1, the workgroup merge instead: DPP within each wavefront, then the
+// four wavefronts' keys).
 template <typename Fmt, int OP, int ML>
 __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
     const Partial<typename Fmt::C>* __restrict__ part, int64_t* __restrict__ out, int64_t inner,
@@ -370,7 +372,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis_merge(
                 m[0].merge(e.v, e.i);
             }
         }
-        merge_rows<ML>(m, s_v, s_i);
+        if constexpr (ML == 1) {
+            block_merge(m[0]);  // one output per workgroup: wavefront DPP, then four keys in LDS
+        } else {
+            merge_rows<ML>(m, s_v, s_i);
+        }
         if (mr == 0 && active) out[o * inner + i] = Cand<C, OP>::result(m[0].i);
     }
 }
