@@ -11,9 +11,9 @@ Timing: W untimed warm-up calls, then exactly K calls between two HIP events on 
 the library launches on, synchronised on both sides; the inputs rotate through copies that
 together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeats one
 buffer and is reported beside it). The timed region divided by K is the per-call time
-(`value`). HIP events recorded around the main kernel of each call (the library's
-measurement hook) give that kernel's own per-launch duration, `kernel_event_us`, which the
-roofline divides into the algorithmic bytes. Ten further trials of 200 calls give the
+(`value`); the roofline divides the algorithmic bytes by that per-call time. HIP events
+recorded around the main kernel of single calls (the library's measurement hook) give
+`kernel_event_us`, a cross-check that includes the events' own overhead. Ten further trials of 200 calls give the
 spread of the per-call figure (`trials_us_per_call`); `host_enqueue_us_per_call` is the host's
 time to enqueue one call, which at these sizes is close to the GPU's time per call (the host
 launch path, not only the kernel, sets the rate). The launch floor is an empty kernel
@@ -340,9 +340,12 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
         "algorithmic_bytes": c.bytes, "rotated_copies": c.n_rot, "plan": c.plan,
         "read_floor": rf,
         "pct_of_read_floor": None if rf is None else round(100 * rf["us_per_call"] / us, 1),
-        # per-launch duration of the scanning kernel itself (HIP events recorded around each
-        # launch on its stream), the figure rocprofv3's kernel trace reports as well
-        "roofline": roofline(c.bytes, kus, w.name if op == "max" else ""),
+        # achieved bandwidth over the timed region: the HIP events around the K timed calls on
+        # the launch stream, divided by K. In this GPU-bound loop that is the kernel's
+        # average time per launch, which rocprofv3's kernel trace of the same command agrees
+        # with; events recorded around each single launch (kernel_event_us) carry their own
+        # overhead and serve as a cross-check only.
+        "roofline": roofline(c.bytes, us, w.name if op == "max" else ""),
     }
     log(f"[bench]   {json.dumps(rec)}")
     rec["_case"] = c
