@@ -581,3 +581,25 @@ def test_fast_call_and_ctypes_marshalling_agree(oracle_lib):
         assert rc == 0, fn
         assert np.array_equal(idx.cpu().numpy(), want_i.reshape(2, 50000)), fn
         assert np.array_equal(vals.cpu().numpy(), want_v.reshape(2, 50000)), fn
+
+
+def test_axis_many_partials_planted_columns(oracle_lib, hooks):
+    """A long axis with few outputs, split over more than 256 workgroups per tile (the
+    merge dispatch's one-output workgroups): planted columns with a leading NaN, all -inf,
+    the extremum at the last position, ties at both ends, and NaN everywhere but one
+    position, for every op."""
+    rng = np.random.default_rng(1201)
+    length, inner = 600000, 8
+    for dtype in ("f32", "f16", "bf16"):
+        v = W.quantised_normal(rng, (length, inner))
+        v[0, 0] = np.nan
+        v[:, 1] = -np.inf
+        v[-1, 2] = 1e4
+        v[0, 3] = v[-1, 3] = 1e4
+        v[:, 4] = np.nan
+        v[123456, 4] = -3.0
+        arr = W.to_storage(v, dtype).reshape(1, length, inner)
+        p = B.argreduce_axis_plan(1, length, inner, dtype)
+        assert p["blocks_per_row"] > 256, p
+        for op in OPS:
+            check_axis(oracle_lib, arr, dtype, op, "axis planted columns", dirty=True)
