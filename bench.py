@@ -280,7 +280,7 @@ def code_text(src: str) -> str:
 
 def kernel_source_hash() -> str:
     """sha256 over the library sources' code (comments and layout excluded): counter figures
-    are valid only for this build."""
+    are valid only for the library built from these sources."""
     import hashlib
 
     h = hashlib.sha256()
@@ -415,9 +415,10 @@ def main() -> int:
                     help="run the counter-collection sequence (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the reduction "
-              "has no multi-GPU path in this build (rows or column slices would shard across "
-              "GPUs with one small exchange; see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
+              "has no multi-GPU path (rows, or column slices of one wide row, would shard "
+              "across GPUs, the slices with one all-gather of ~16-byte candidates).",
+              file=sys.stderr)
         return 2
 
     import torch
