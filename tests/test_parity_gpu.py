@@ -590,7 +590,7 @@ def test_axis_many_partials_planted_columns(oracle_lib, hooks):
     position, for every op."""
     rng = np.random.default_rng(1201)
     length, inner = 600000, 8
-    for dtype in ("f32", "f16", "bf16"):
+    for dtype in ("f32", "f16", "bf16", "f64"):
         v = W.quantised_normal(rng, (length, inner))
         v[0, 0] = np.nan
         v[:, 1] = -np.inf
