@@ -286,7 +286,11 @@ int make_axis_plan(int64_t outer, int64_t len, int64_t inner, int dtype, uintptr
     // four workgroups per CU): [1,1048576,32] fp32 29.5 -> 27.7 us, [1,4096,4096] 20.3 -> 15.9.
     const int64_t fill = cap_blocks / kSplitFillDiv / tiles1;
     const int64_t want = ceil_div(len, rows_per_tile * p->unroll);
-    int64_t b = fill < want ? fill : want;
+    // One step per thread when that takes at most 1.5 times the fill: a ragged second step
+    // costs more than the extra partials ([1,600000,8] and [1,150000,32] fp32 10.8 -> 9.7 us,
+    // 512 -> 586 workgroups; [1,1200000,8] bf16 -6%); nearer twice the fill it measured
+    // no faster (977 and 782 workgroups: +0.6-1.1%).
+    int64_t b = 2 * want <= 3 * fill ? want : fill;
     b = b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
     // Two workgroups per tile do not pay for the merge dispatch they need: one per tile,
     // with twice the steps, measured faster ([256,1024,256] fp32 44.8 -> 41.6 us per call).
