@@ -208,6 +208,12 @@ def test_axis_plans(mi355x):
     assert p["path"] == B.PATH_AXIS and p["blocks_per_row"] > 1 and p["dispatches"] == 2
     assert p["scratch_bytes"] == 15 + p["blocks_per_row"] * 32 * 8
     assert p["grid_blocks"] <= MI355X_THREADS // 256
+    # split width: a quarter of the device wave of workgroups (512 for one tile), or up to 1.5
+    # times that when it covers the axis in one step per thread (1024 rows of 8 fp32 each)
+    assert B.argreduce_axis_plan(1, 600000, 8, B.F32)["blocks_per_row"] == 586
+    assert B.argreduce_axis_plan(1, 786432, 8, B.F32)["blocks_per_row"] == 768
+    assert B.argreduce_axis_plan(1, 786433, 8, B.F32)["blocks_per_row"] == 512
+    assert B.argreduce_axis_plan(1, 1000000, 8, B.F32)["blocks_per_row"] == 512
     # lanes: the next power of two of the vectors (16-byte loads) or elements per inner row
     for (inner, dtype), (tile, load) in {
         (3, B.F16): (4, 2), (9, B.F16): (16, 2), (16, B.F16): (16, 16), (8, B.BF16): (8, 16),
