@@ -44,7 +44,8 @@ EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
            "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
            "argreduce_debug_set_window", "argreduce_debug_launch_store",
-           "argreduce_debug_set_spin_limit", "argreduce_debug_launch_read")
+           "argreduce_debug_set_spin_limit", "argreduce_debug_launch_read",
+           "argreduce_wait_timeouts")
 
 
 class ArgreduceError(RuntimeError):
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_debug_launch_read.restype = c_int
                 h.argreduce_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
                 h.argreduce_debug_set_spin_limit.restype = c_int
+                h.argreduce_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+                h.argreduce_wait_timeouts.restype = c_int
                 h.argreduce_debug_set_window.argtypes = [i64]
                 h.argreduce_debug_set_window.restype = c_int
                 h.argreduce_debug_launch_empty.argtypes = [vp]
@@ -245,6 +248,16 @@ def argreduce_debug_launch_read(x_ptr: int, nbytes: int, out_ptr: int, grid: int
 
 def argreduce_debug_set_spin_limit(polls: int) -> int:
     return lib().argreduce_debug_set_spin_limit(polls)
+
+
+def argreduce_wait_timeouts() -> int:
+    """Bounded waits that gave up on the current device since the library was loaded
+    (synchronous read of a device counter); raises ArgreduceError on failure."""
+    c = ctypes.c_uint64(0)
+    rc = lib().argreduce_wait_timeouts(ctypes.byref(c))
+    if rc != 0:
+        raise ArgreduceError(rc, "argreduce_wait_timeouts")
+    return c.value
 
 
 def argreduce_debug_set_window(elements: int) -> int:

@@ -481,6 +481,16 @@ ARGREDUCE_EXPORT int argreduce_debug_set_spin_limit(uint32_t polls) {
     return ARGREDUCE_OK;
 }
 
+ARGREDUCE_EXPORT int argreduce_wait_timeouts(uint64_t* count) {
+    if (count == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ARGREDUCE_ERR_NO_DEVICE;
+    unsigned long long c = 0;
+    if (argreduce::read_wait_timeouts(&c) != hipSuccess) return ARGREDUCE_ERR_HIP;
+    *count = static_cast<uint64_t>(c);
+    return ARGREDUCE_OK;
+}
+
 ARGREDUCE_EXPORT int argreduce_debug_launch_empty(void* stream) {
     return argreduce::launch_empty(static_cast<hipStream_t>(stream)) == hipSuccess
                ? ARGREDUCE_OK

@@ -87,6 +87,9 @@ hipError_t launch_read_floor(const void* x, size_t bytes, uint32_t* out, uint32_
                              hipStream_t stream);
 void set_spin_limit(uint32_t polls);
 
+// Copies the current device's count of bounded waits that gave up to *count (synchronous).
+hipError_t read_wait_timeouts(unsigned long long* count);
+
 // Events recorded around the row-scanning kernel of every launch when both are set.
 void set_kernel_events(hipEvent_t start, hipEvent_t stop);
 

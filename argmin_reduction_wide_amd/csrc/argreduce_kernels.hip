@@ -38,11 +38,13 @@
 // no release fence) is needed; stale or arbitrary scratch contents are ignored unless a
 // word equals this call's nonce in its upper half (and, for the index word, holds an
 // in-range index). Only finalizers wait, and only on lower-numbered workgroups, which wait
-// on nothing. The automatic plans keep the grid within one device wave, so every
-// workgroup is resident at once; larger grids (forced plans) rely on each XCD starting
-// the workgroups it is given in id order, which makes every wait end by induction on the
-// id. The poll is bounded all the same: should a word never arrive, out[r] = -1 (never
-// observed).
+// on nothing. The automatic plans launch at most one device wave of workgroups (CUs * 2048
+// threads / 256), and k_blocks is compiled for eight waves per SIMD, so on an otherwise idle
+// device every workgroup is resident at once. Larger grids (forced plans), or a device
+// shared with other work, rely on each XCD starting the workgroups it is given in id order,
+// which makes every wait end by induction on the id. The poll is bounded all the same:
+// should a word never arrive, out[r] = -1 and the device's timeout counter
+// (argreduce_wait_timeouts) goes up by one (never observed outside tests that force it).
 #include <hip/hip_ext.h>
 
 #include <atomic>
@@ -70,13 +72,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
     }
 }
 
+// Eight waves per SIMD (at most 64 VGPRs): eight workgroups of 256 threads per CU, so a
+// grid of up to (CUs * 2048 / 256) workgroups, the most an automatic split plan launches,
+// is resident at once on an otherwise idle device, whatever the format and unroll.
 template <typename Fmt, int OP, int U>
-__global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restrict__ x,
-                                                          int64_t rows, int64_t grid_rows,
-                                                          int64_t* __restrict__ out,
-                                                          uint64_t* __restrict__ slots,
-                                                          uint32_t cols, uint32_t B,
-                                                          uint32_t nonce, uint32_t spin_limit) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_blocks(const uint8_t* __restrict__ x, int64_t rows, int64_t grid_rows,
+              int64_t* __restrict__ out, uint64_t* __restrict__ slots, uint32_t cols,
+              uint32_t B, uint32_t nonce, uint32_t spin_limit,
+              unsigned long long* __restrict__ timeouts) {
     using C = typename Fmt::C;
     __shared__ int s_timeout;
     const uint32_t b = blockIdx.x % B;
@@ -84,8 +88,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
     const uint32_t team = B * kBlockThreads;
     const uint32_t lane = b * kBlockThreads + threadIdx.x;
     const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
-    if (threadIdx.x == 0) s_timeout = 0;
     for (int64_t r = slot; r < rows; r += grid_rows) {
+        // Thread 0 read the previous row's flag itself, and every other thread's writes to it
+        // came before the barriers of that row's last merge; this row's writes come after
+        // the barriers of the merge below.
+        if (threadIdx.x == 0) s_timeout = 0;
         const uint8_t* row = x + static_cast<size_t>(r) * row_bytes;
         Cand<C, OP> c;
         scan_row<Fmt, OP, U>(row, cols, lane, team, c);
@@ -151,7 +158,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
                 __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         block_merge(m);
-        if (threadIdx.x == 0) out[r] = s_timeout ? int64_t{-1} : Cand<C, OP>::result(m.i);
+        if (threadIdx.x == 0) {
+            out[r] = s_timeout ? int64_t{-1} : Cand<C, OP>::result(m.i);
+            if (s_timeout) __hip_atomic_fetch_add(timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -504,6 +514,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_read_floor(const u32x4* __res
     if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
 }
 
+// Bounded waits that gave up, per device (read by argreduce_wait_timeouts).
+__device__ unsigned long long g_wait_timeouts;
+
 std::atomic<uint32_t> g_nonce{0};
 
 uint32_t next_nonce() {
@@ -526,6 +539,31 @@ std::atomic<hipEvent_t> g_ev_start{nullptr};
 std::atomic<hipEvent_t> g_ev_stop{nullptr};
 
 namespace {
+constexpr int kMaxSymbolDevices = 64;
+std::atomic<unsigned long long*> g_timeouts_addr[kMaxSymbolDevices];
+}  // namespace
+
+unsigned long long* wait_timeouts_counter() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSymbolDevices) return nullptr;
+    unsigned long long* p = g_timeouts_addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    // the device's own copy of the counter: host code never passes the variable's name
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(g_wait_timeouts)) != hipSuccess || addr == nullptr)
+        return nullptr;
+    p = static_cast<unsigned long long*>(addr);
+    g_timeouts_addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+hipError_t read_wait_timeouts(unsigned long long* count) {
+    unsigned long long* p = wait_timeouts_counter();
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    return hipMemcpy(count, p, sizeof(*count), hipMemcpyDeviceToHost);
+}
+
+namespace {
 
 template <typename Fmt, int OP, int G, int U>
 void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
@@ -536,10 +574,10 @@ void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows
 
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
-                   uint64_t* slots, hipStream_t s) {
+                   uint64_t* slots, unsigned long long* timeouts, hipStream_t s) {
     launch_scan(k_blocks<Fmt, OP, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, rows,
                 p.grid_rows, out, slots, cols, static_cast<uint32_t>(p.blocks_per_row),
-                p.blocks_per_row > 1 ? next_nonce() : 0u, spin_limit());
+                p.blocks_per_row > 1 ? next_nonce() : 0u, spin_limit(), timeouts);
 }
 
 template <typename Fmt, int OP>
@@ -582,11 +620,16 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
         return hipGetLastError();
     }
     uint64_t* slots = p.blocks_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
+    unsigned long long* tmo = nullptr;
+    if (p.blocks_per_row > 1) {
+        tmo = wait_timeouts_counter();
+        if (tmo == nullptr) return hipErrorInvalidSymbol;
+    }
     switch (p.unroll) {
-        case 1: launch_blocks<Fmt, OP, 1>(p, x, c32, rows, out, slots, s); break;
-        case 2: launch_blocks<Fmt, OP, 2>(p, x, c32, rows, out, slots, s); break;
-        case 4: launch_blocks<Fmt, OP, 4>(p, x, c32, rows, out, slots, s); break;
-        case 8: launch_blocks<Fmt, OP, 8>(p, x, c32, rows, out, slots, s); break;
+        case 1: launch_blocks<Fmt, OP, 1>(p, x, c32, rows, out, slots, tmo, s); break;
+        case 2: launch_blocks<Fmt, OP, 2>(p, x, c32, rows, out, slots, tmo, s); break;
+        case 4: launch_blocks<Fmt, OP, 4>(p, x, c32, rows, out, slots, tmo, s); break;
+        case 8: launch_blocks<Fmt, OP, 8>(p, x, c32, rows, out, slots, tmo, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -37,14 +37,17 @@
 // same self-checking
 // words as the split ArgMax path: 64-bit agent-scope atomic stores of (nonce << 32) |
 // payload, one word per 32 bits of (index, value), each word validated on its own, so no
-// fence orders them. A fresh nonce per call makes earlier calls' words invalid; a call
-// captured into a HIP graph, whose nonce is fixed across replays, first clears its words
-// with a small kernel (a graph node, not a memset). Forward progress: a tile waits only
-// on tiles of lower workgroup id, which publish their aggregate without waiting. With
+// fence orders them. Every call, eager or captured, takes a nonce of its own from the one
+// process-wide counter (each value is issued once, until the 32-bit counter wraps), so the
+// words an earlier call or graph replay left behind never carry the nonce of a later call.
+// A call captured into a HIP graph keeps its nonce across replays, so it first clears its
+// words with a small kernel (a graph node, not a memset). Forward progress: a tile waits
+// only on tiles of lower workgroup id, which publish their aggregate without waiting. With
 // more tiles than fit on the device at once this relies on each XCD starting the
 // workgroups it is given in id order (then every wait ends, by induction on the id), the
 // assumption of any look-back scan whose tile ids are workgroup ids. The wait is bounded
-// all the same (indices -1 on a timeout, never observed).
+// all the same: on a timeout the tile's indices are -1 and the device's timeout counter
+// goes up by one (never observed outside tests that force it).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -356,7 +359,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
                                                        uint32_t T, uint8_t* __restrict__ out_val,
                                                        int64_t* __restrict__ out_idx,
                                                        uint64_t* __restrict__ states, uint32_t nonce,
-                                                       uint32_t spin_limit) {
+                                                       uint32_t spin_limit,
+                                                       unsigned long long* __restrict__ timeouts) {
     using C = typename Fmt::C;
     using Op = ScanOp<C, OP>;
     using S = typename Out<Fmt>::S;
@@ -481,7 +485,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
             publish(mine + SW::kStride, nonce, incv, ok ? inci : kFail);  // inclusive prefix
             s_v[kWaves] = pv;
             s_i[kWaves] = pi;
-            if (!ok) s_fail = 1;
+            if (!ok) {
+                s_fail = 1;
+                __hip_atomic_fetch_add(timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     __syncthreads();
@@ -576,19 +583,20 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
                          uint8_t* scratch16, hipStream_t s) {
     uint64_t* states = p.tiles_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
     uint32_t nonce = 0;
+    unsigned long long* tmo = nullptr;
     if (states != nullptr) {
+        tmo = wait_timeouts_counter();
+        if (tmo == nullptr) return hipErrorInvalidSymbol;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess) return hipErrorInvalidValue;
         if (cs == hipStreamCaptureStatusActive) {
-            // replays of the graph repeat this nonce: clear the words before each replay
+            // replays of the graph repeat this call's nonce: clear the words before each replay
             const size_t words = p.state_words;
             const size_t blocks = (words + kBlockThreads - 1) / kBlockThreads;
             hipLaunchKernelGGL(k_cum_clear, dim3(static_cast<uint32_t>(blocks < 1024 ? blocks : 1024)),
                                dim3(kBlockThreads), 0, s, states, words);
-            nonce = 1u;
-        } else {
-            nonce = next_nonce();
         }
+        nonce = next_nonce();
     }
     const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
     const uint8_t* xb = static_cast<const uint8_t*>(x);
@@ -597,17 +605,17 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
     constexpr int UT = kScanUnrollTiny, US = kScanUnrollShort, UL = kScanUnrollLong;
     if (p.unroll == UT && p.vecio)
-        launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     else if (p.unroll == UT)
-        launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     else if (p.unroll == US && p.vecio)
-        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     else if (p.unroll == US)
-        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     else if (p.vecio)
-        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     else
-        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
     return hipGetLastError();
 }
 

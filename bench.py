@@ -4,8 +4,11 @@
 Headline workload: ArgMax over fp32 [1, 202048] (vocabulary-sized sampler logits,
 iid N(0, 4), seed 2), the shape the "[CUDA] Parallelize ArgMax/ArgMin over wide last axes"
 page profiles; [4096, 4096] fp32 (iid U(-1,1) with planted inf/NaN rows, seed 4) is timed
-as the second shape of the same metric. A step is one call of the library (every kernel it
-enqueues), on inputs already resident in HBM.
+as the second shape of the same metric, and `all_configs` holds the same figures for every
+configuration of the workload set ([1,32000] fp32, [1,202048] fp32 ArgMax and ArgMin,
+[32,202048] fp16 and bf16 ArgMax and ArgMin, [4096,4096] fp32 and fp64, [65536,1024] fp32
+ArgMin, [65536,64] fp16), each at the same steps and warm-up. A step is one call of the
+library (every kernel it enqueues), on inputs already resident in HBM.
 
 Timing: W untimed warm-up calls, then exactly K calls between two HIP events on the stream
 the library launches on, synchronised on both sides; the inputs rotate through copies that
@@ -20,7 +23,9 @@ launch path, not only the kernel, sets the rate). The launch floor is an empty k
 launched the same way; the read floor (`read_floor`, read-only workloads) is a plain
 streaming-read kernel over the same rotated inputs and byte count, the practical read
 roofline in the same harness. The CPU baseline is the oracle (a single-threaded sequential
-scan) timed on this host on a bounded sample of calls of the same workload.
+scan) timed on this host: the headline workload on one pinned core (median and min of five
+runs), and the [4096,4096] and [65536,1024] fp32 workloads on one pinned core and with their
+rows split across the host's threads (at most 16), with the host's core count and CPU model.
 
 `--pmc-pass` runs a fixed sequence for hardware-counter collection instead (a 256 MiB
 device copy, whose known bytes calibrate FETCH_SIZE / WRITE_SIZE, then 100 calls of each
@@ -385,22 +390,108 @@ def pmc_pass() -> int:
     return 0
 
 
-def cpu_baseline(w, op: str, seconds: float) -> dict:
+# Host threads of the all-cores oracle leg: at most the CPU share one GPU's job gets.
+CPU_THREADS_MAX = 16
+
+
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+
+
+def oracle_leg(o, w, op: str, threads: int, runs: int = 5, min_run_s: float = 0.0) -> dict:
+    """The oracle's time per call of ``arg{op}`` over the whole workload ``w``: one warm-up
+    call, then ``runs`` timed runs (each of as many calls as fill ``min_run_s``, at least
+    one); median and min of the per-call time over the runs. With ``threads`` == 1 the
+    calling thread is pinned to one core for the runs; with more, the rows are split into
+    ``threads`` contiguous slices, each scanned by the oracle on a thread of its own (the
+    scan within a row stays sequential; the ctypes call releases the GIL)."""
+    import threading
+
+    data = w.data
+    rows = data.shape[0]
+    if threads == 1:
+        def call():
+            return o.argreduce_lastaxis(data, w.dtype, op)
+    else:
+        bounds = [rows * k // threads for k in range(threads + 1)]
+        parts = [None] * threads
+
+        def work(k):
+            parts[k] = o.argreduce_lastaxis(data[bounds[k]:bounds[k + 1]], w.dtype, op)
+
+        def call():
+            ts = [threading.Thread(target=work, args=(k,)) for k in range(threads)]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+            import numpy as np
+            return np.concatenate(parts)
+
+    saved = os.sched_getaffinity(0)
+    core = min(saved)
+    if threads == 1:
+        os.sched_setaffinity(0, {core})
+    try:
+        res = call()  # warm-up
+        per_call = []
+        for _ in range(runs):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                call()
+                n += 1
+                el = time.perf_counter() - t0
+                if el >= min_run_s:
+                    break
+            per_call.append(el / n)
+    finally:
+        os.sched_setaffinity(0, saved)
+    per_call.sort()
+    med = per_call[len(per_call) // 2]
+    return {"workload": w.name, "op": op, "shape": [w.rows, w.cols], "dtype": w.dtype,
+            "threads": threads, "pinned_core": core if threads == 1 else None, "runs": runs,
+            "us_per_call_median": round(med * 1e6, 1),
+            "us_per_call_min": round(per_call[0] * 1e6, 1),
+            "gbps_median": round(w.nbytes / med / 1e9, 2), "_result": res}
+
+
+def cpu_baseline(primary, multi: list, seconds: float) -> dict:
+    """The oracle timed on this host: the headline workload on one pinned core (the
+    reported value), and the multi-row workloads on one pinned core and on all host
+    threads (rows split across them), each as the median and min of five runs."""
     import oracle
 
     o = oracle.load()
-    o.argreduce_lastaxis(w.data, w.dtype, op)  # warm
-    n, t0 = 0, time.perf_counter()
-    while True:
-        res = o.argreduce_lastaxis(w.data, w.dtype, op)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds and n >= 3:
-            break
-    return {"value": round(el / n * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"{n} calls of arg{op} {w.dtype} [{w.rows},{w.cols}] (the timed workload's "
-                      f"input) by the single-threaded oracle on one host core, {el:.1f} s",
-            "_result": res}
+    host = host_info()
+    threads = max(1, min(host["affinity_cpus"], CPU_THREADS_MAX))
+    w, op = primary
+    head = oracle_leg(o, w, op, 1, runs=5, min_run_s=seconds / 6)
+    res = head.pop("_result")
+    legs = [head]
+    for mw, mop in multi:
+        for t in (1, threads):
+            leg = oracle_leg(o, mw, mop, t, runs=5)
+            leg.pop("_result")
+            legs.append(leg)
+            log(f"[bench] oracle {mw.name} arg{mop} on {t} thread(s): "
+                f"{leg['us_per_call_median']} us/call (median of 5)")
+    return {"value": head["us_per_call_median"], "unit": "us/call", "cores": 1, "kind": "oracle",
+            "min": head["us_per_call_min"],
+            "sample": f"arg{op} {w.dtype} [{w.rows},{w.cols}] (the timed workload's input) by the "
+                      f"single-threaded oracle pinned to core {head['pinned_core']}: median of 5 "
+                      f"runs of about {seconds / 6:.1f} s each after one warm-up call; the legs "
+                      f"add the multi-row workloads on 1 and on {threads} host threads",
+            "host": host, "legs": legs, "_result": res}
 
 
 def main() -> int:
@@ -410,7 +501,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time every configured workload")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the middle-axis, cumulative-scan and wide-row workloads")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run the counter-collection sequence (for rocprofv3 --pmc) and exit")
     args = ap.parse_args()
@@ -442,10 +534,32 @@ def main() -> int:
     store_floor = launch_floor_us(args.steps, store=True)
     log(f"[bench] launch floor (empty kernel) {floor:.3f} us; one-argument store kernel "
         f"{store_floor:.3f} us")
+    parity_result = prim["_case"].result()
+    prim.pop("_case")
+    sec.pop("_case")
+
+    # Every configuration of the metric's workload set (C1 .. C5b, each op), at the same
+    # steps and warm-up; the two shapes above are not timed twice.
+    all_configs = []
+    multi_rows = {}
+    for name in W.CONFIG_NAMES:
+        for w in W.config_workloads(name):
+            for op in w.ops:
+                if w.name == primary_w.name and op == "max":
+                    r = prim
+                elif w.name == sec_w.name and op == "max":
+                    r = sec
+                else:
+                    r = measure(w, op, args.steps, args.warmup, graph=False)
+                    r.pop("_case")
+                    torch.cuda.empty_cache()
+                all_configs.append(dict(r, config=name))
+            if name in ("c4", "c5a") and w.dtype == "f32":
+                multi_rows[name] = (w, w.ops[0])
 
     extra = []
     if args.all:
-        for name in W.CONFIG_NAMES + ("axis", "scan", "wide"):
+        for name in ("axis", "scan", "wide"):
             for w in W.config_workloads(name):
                 for op in w.ops:
                     r = measure(w, op, max(200, args.steps // 4), args.warmup // 4 + 1, graph=False)
@@ -456,12 +570,10 @@ def main() -> int:
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(primary_w, "max", args.cpu_seconds)
+        cpu = cpu_baseline((primary_w, "max"), [multi_rows["c4"], multi_rows["c5a"]],
+                           args.cpu_seconds)
         res = cpu.pop("_result")
-        parity = bool((prim["_case"].result() == res).all())
-
-    prim.pop("_case")
-    sec.pop("_case")
+        parity = bool((parity_result == res).all())
     rec = {
         "metric": "ArgMax µs/call and achieved HBM GB/s (% of peak) at [1,202048] and [4096,4096]",
         "value": prim["us_per_call"],
@@ -502,10 +614,11 @@ def main() -> int:
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "secondary": sec,
+        "all_configs": all_configs,
         "device": props.name,
     }
     if extra:
-        rec["all_configs"] = extra
+        rec["extra_workloads"] = extra
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -20,7 +20,8 @@
  *
  * Threading, memory and streams (same page, Description / Approach and Testing):
  *   - every pointer argument is a DEVICE pointer owned by the caller; the library never
- *     allocates, frees, synchronises or prints;
+ *     allocates, frees or prints, and only argreduce_wait_timeouts (a diagnostic read of
+ *     a device counter) synchronises;
  *   - all work is enqueued on the caller's HIP stream (`stream` is a hipStream_t, NULL for
  *     the default stream), so a call may be captured into a HIP graph and replayed;
  *   - functions are safe to call from several host threads; calls that share one scratch
@@ -28,9 +29,11 @@
  *
  * Status codes: 0 on success, a negative ARGREDUCE_ERR_* value otherwise. On every error
  * except ARGREDUCE_ERR_HIP nothing has been enqueued and out_idx is untouched. One
- * device-side condition cannot be returned by the call: should a workgroup of a split row
- * never publish its result (not expected: those workgroups wait on nothing), the row's
- * finalizing workgroup gives up after a bounded wait and stores -1 in out_idx[r].
+ * device-side condition cannot be returned by the call, which returns before the kernels
+ * run: should a workgroup of a split row never publish its result (not expected: those
+ * workgroups wait on nothing), the row's finalizing workgroup gives up after a bounded
+ * wait, stores -1 in out_idx[r] and adds one to the device's timeout count, which
+ * argreduce_wait_timeouts reads.
  */
 #ifndef ARGREDUCE_H
 #define ARGREDUCE_H
@@ -278,11 +281,24 @@ int argreduce_debug_launch_read(const void *x, size_t bytes, uint32_t *out, int6
                                 void *stream);
 
 /* Test hook for the bounded waits (the split ArgMax path's finalizing workgroup, the scan's
- * look-back): polls of one published word before the wait gives up and the affected
- * outputs become -1 (0 restores the default, 2^20 polls). Process-wide. With a tiny limit
+ * look-back): polls of one published word before the wait gives up, the affected outputs
+ * become -1 and argreduce_wait_timeouts counts it (0 restores the default, 2^20 polls). Process-wide. With a tiny limit
  * a wait can give up although nothing is wrong; this lets tests drive the time-out path
  * from the host while every kernel still ends normally. */
 int argreduce_debug_set_spin_limit(uint32_t polls);
+
+/* Bounded waits that gave up on the CURRENT device since the library was loaded. Two kinds
+ * of workgroup wait for results that other workgroups of the same launch publish: the
+ * finalizing workgroup of a split row (argreduce_lastaxis, "[CUDA] Parallelize ArgMax/ArgMin
+ * over wide last axes", Description / Approach: the last block merges the partials) and a
+ * tile of a long cumulative-scan row (argreduce_scan_lastaxis). Each stops after a bounded
+ * number of polls (argreduce_debug_set_spin_limit); its outputs then hold -1 and the count
+ * goes up by one per row (split) or per tile (scan). No wait is expected to give up unless a
+ * test forces a tiny limit; a caller that must rule it out compares the count before and
+ * after its calls. Copies the device's counter to *count synchronously, after the work
+ * already enqueued on the default stream (call it off the hot path). Returns ARGREDUCE_OK,
+ * ARGREDUCE_ERR_INVALID_ARG (count NULL), ARGREDUCE_ERR_NO_DEVICE or ARGREDUCE_ERR_HIP. */
+int argreduce_wait_timeouts(uint64_t *count);
 
 /* Measurement hook: when both are non-NULL, every later call launches its main kernel
  * (not a merge or clear kernel) with `start` recorded just before and

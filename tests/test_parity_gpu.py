@@ -124,14 +124,15 @@ def test_special_value_fuzz(oracle_lib, hooks, cap):
             check(oracle_lib, arr, dtype, op, f"fuzz trial={trial} cap={cap} kind={kind}")
 
 
-@pytest.mark.parametrize("dtype", ("f32", "f16"))
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_split_plan_boundaries(oracle_lib, hooks, dtype):
     """Rows at the edges of the split plan's one-step rule: for U = 1, 2, 4, 8 loads per lane,
     the widest row that B <= min(256, device wave / rows) workgroups cover in one step, and
-    one element more (the next U, or several steps), for 1 and 32 rows."""
-    rng = np.random.default_rng(66)
+    one element more (the next U, or several steps), for 1, 8 and 32 rows: on this device
+    [8, 2^20] and [32, 2^18] fp64 are full device waves of the U = 8 kernel."""
+    rng = np.random.default_rng(66 + DTYPES.index(dtype))
     cap_blocks = B.argreduce_plan(1, 1, dtype)["device_threads"] // 256
-    for rows in (1, 32):
+    for rows in (1, 8, 32):
         bmax = min(256, cap_blocks // rows)
         for u in (1, 2, 4, 8):
             edge = bmax * 256 * u * VW[dtype]
@@ -414,12 +415,14 @@ def test_axis_workloads_full_size(oracle_lib):
 
 def test_bounded_wait_gives_up_cleanly(oracle_lib):
     """The split path's bounded wait, driven from the host with a one-poll limit: every
-    output is the oracle's index or -1 (a wait that gave up), every kernel ends; with the
-    default limit restored the same scratch gives exact results again."""
+    output is the oracle's index or -1 (a wait that gave up), every kernel ends, and the
+    device's timeout count goes up by exactly the number of rows that came out -1; with the
+    default limit restored the same scratch gives exact results again and the count stays."""
     import torch
 
     rng = np.random.default_rng(77)
-    cases = [(1, 202048, "f32"), (32, 202048, "f16"), (3, 500000, "f64")]
+    cases = [(1, 202048, "f32"), (32, 202048, "f16"), (3, 500000, "f64"), (40, 65536, "bf16")]
+    gave_up = 0
     try:
         B.argreduce_debug_set_spin_limit(1)
         for rows, cols, dtype in cases:
@@ -430,15 +433,22 @@ def test_bounded_wait_gives_up_cleanly(oracle_lib):
             scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
             for rep in range(5):
                 announce(f"one-poll limit rows={rows} cols={cols} dtype={dtype} rep={rep}")
+                before = B.argreduce_wait_timeouts()
                 rc, got = run(t, dtype, "max", scratch=scratch)
                 assert rc == 0
                 assert np.all((got == want) | (got == -1)), (rows, cols, dtype, got)
+                failed = int(np.count_nonzero(got == -1))
+                assert B.argreduce_wait_timeouts() - before == failed, (rows, cols, dtype, failed)
+                gave_up += failed
             B.argreduce_debug_set_spin_limit(0)
+            before = B.argreduce_wait_timeouts()
             rc, got = run(t, dtype, "max", scratch=scratch)
             assert rc == 0 and np.array_equal(got, want)
+            assert B.argreduce_wait_timeouts() == before
             B.argreduce_debug_set_spin_limit(1)
     finally:
         B.argreduce_debug_set_spin_limit(0)
+    announce(f"one-poll limit: {gave_up} row waits gave up in all")
 
 
 def test_streaming_read_hook_covers_every_vector():

@@ -208,23 +208,52 @@ def test_scan_torch_wrapper(oracle_lib):
 
 def test_scan_bounded_look_back_gives_up_cleanly(oracle_lib):
     """The look-back's bounded wait with a one-poll limit: each index is the oracle's or -1
-    (a tile that gave up, and the tiles after it); with the default limit restored the same
-    scratch gives exact results."""
+    (a tile that gave up, and the tiles after it), every tile with -1 indices is all -1, and
+    the device's timeout count goes up by exactly the number of such tiles; with the default
+    limit restored the same scratch gives exact results and the count stays."""
     import torch
 
     rng = np.random.default_rng(904)
-    arr = inputs(rng, 1, 3 << 20, "f32", "ties")
+    cols = 3 << 20
+    arr = inputs(rng, 1, cols, "f32", "ties")
     want_v, want_i = oracle_lib.cumulative(arr, "f32", "max")
-    need = B.argreduce_scan_scratch_bytes(1, 3 << 20, "f32")
+    need = B.argreduce_scan_scratch_bytes(1, cols, "f32")
+    tile = B.argreduce_scan_plan(1, cols, "f32")["outputs_per_block"]
     scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
     try:
         B.argreduce_debug_set_spin_limit(1)
         for rep in range(3):
             announce(f"scan one-poll limit rep={rep}")
+            before = B.argreduce_wait_timeouts()
             rc, _, got_i = run_scan(arr, "f32", "max", scratch=scratch)
             assert rc == 0
             assert np.all((got_i == want_i) | (got_i == -1))
+            per_tile = (got_i[0] == -1).reshape(-1, tile)  # cols is a multiple of the tile
+            failed = per_tile.any(axis=1)
+            assert np.array_equal(per_tile.all(axis=1), failed)
+            assert B.argreduce_wait_timeouts() - before == int(failed.sum())
     finally:
         B.argreduce_debug_set_spin_limit(0)
+    before = B.argreduce_wait_timeouts()
     rc, got_v, got_i = run_scan(arr, "f32", "max", scratch=scratch)
     assert rc == 0 and np.array_equal(got_i, want_i) and np.array_equal(bits(got_v), bits(want_v))
+    assert B.argreduce_wait_timeouts() == before
+
+
+def test_graph_then_eager_calls_in_a_fresh_process():
+    """In a process of its own (so that its nonce counter starts from the beginning): a
+    captured multi-tile scan replayed, then the first eager scan on the same scratch, then an
+    eager split ArgMax on it, then a replay and an eager scan again; every result bit-exact
+    against the oracle. A capture that reused a value of the eager nonce sequence would let
+    the eager calls accept the replay's stale state words."""
+    import os
+    import subprocess
+    import sys
+
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fresh_process_graph_nonce.py")
+    announce("fresh process: scan graph replay, then eager calls on the same scratch")
+    proc = subprocess.run([sys.executable, "-u", child], capture_output=True, text=True,
+                          timeout=300)
+    print(proc.stdout, flush=True)
+    assert proc.returncode == 0, proc.stdout[-2000:] + proc.stderr[-4000:]
+    assert "fresh-process sequence ok" in proc.stdout
