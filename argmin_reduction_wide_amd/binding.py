@@ -45,7 +45,7 @@ EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
            "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
            "argreduce_debug_set_window", "argreduce_debug_launch_store",
            "argreduce_debug_set_spin_limit", "argreduce_debug_launch_read",
-           "argreduce_wait_timeouts")
+           "argreduce_wait_timeouts", "argreduce_lastaxis_noalloc")
 
 
 class ArgreduceError(RuntimeError):
@@ -119,6 +119,8 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_debug_launch_read.restype = c_int
                 h.argreduce_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
                 h.argreduce_debug_set_spin_limit.restype = c_int
+                h.argreduce_lastaxis_noalloc.argtypes = [vp, c_int, i64, i64, c_int, vp, vp]
+                h.argreduce_lastaxis_noalloc.restype = c_int
                 h.argreduce_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
                 h.argreduce_wait_timeouts.restype = c_int
                 h.argreduce_debug_set_window.argtypes = [i64]
@@ -186,6 +188,18 @@ def argreduce_lastaxis(x_ptr: int, dtype, rows: int, cols: int, op, out_ptr: int
     """Enqueue the reduction; returns the library's status code (0 = success)."""
     return entry_point("argreduce_lastaxis")(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
                                         out_ptr, scratch_ptr, scratch_bytes, stream)
+
+
+# Bytes of the library-held scratch of argreduce_lastaxis_noalloc (include/argreduce.h).
+NOALLOC_SCRATCH_BYTES = 128 * 1024
+
+
+def argreduce_lastaxis_noalloc(x_ptr: int, dtype, rows: int, cols: int, op, out_ptr: int,
+                               stream: int) -> int:
+    """argreduce_lastaxis with the library-held scratch (no scratch argument, nothing
+    allocated); returns the library's status code."""
+    return lib().argreduce_lastaxis_noalloc(x_ptr, _dtype_code(dtype), rows, cols, _op_code(op),
+                                            out_ptr, stream)
 
 
 def argreduce_plan(rows: int, cols: int, dtype) -> dict:

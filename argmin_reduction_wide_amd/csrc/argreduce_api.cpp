@@ -410,28 +410,61 @@ ARGREDUCE_EXPORT int argreduce_plan(int64_t rows, int64_t cols, argreduce_dtype_
     return ARGREDUCE_OK;
 }
 
-ARGREDUCE_EXPORT int argreduce_lastaxis(const void* x, argreduce_dtype_t dtype, int64_t rows,
-                                        int64_t cols, argreduce_op_t op, int64_t* out_idx,
-                                        void* scratch, size_t scratch_bytes, void* stream) {
-    int rc = argreduce::check_shape(rows, cols, dtype);
+namespace argreduce {
+namespace {
+// Argument checks and plan of a last-axis call; *noop is set when there is nothing to do.
+int lastaxis_plan(const void* x, int dtype, int64_t rows, int64_t cols, int op,
+                  const int64_t* out_idx, Plan* p, bool* noop) {
+    *noop = false;
+    int rc = check_shape(rows, cols, dtype);
     if (rc != ARGREDUCE_OK) return rc;
     if (op != ARGREDUCE_MAX && op != ARGREDUCE_MIN && op != ARGREDUCE_MAX_LAST &&
         op != ARGREDUCE_MIN_LAST)
         return ARGREDUCE_ERR_INVALID_ARG;
-    if (rows == 0) return ARGREDUCE_OK;
+    if (rows == 0) {
+        *noop = true;
+        return ARGREDUCE_OK;
+    }
     if (x == nullptr || out_idx == nullptr) return ARGREDUCE_ERR_INVALID_ARG;
-    if (reinterpret_cast<uintptr_t>(x) % argreduce::elem_size(dtype) != 0 ||
+    if (reinterpret_cast<uintptr_t>(x) % elem_size(dtype) != 0 ||
         reinterpret_cast<uintptr_t>(out_idx) % 8 != 0)
         return ARGREDUCE_ERR_INVALID_ARG;
+    return make_plan(rows, cols, dtype, p);
+}
+}  // namespace
+}  // namespace argreduce
+
+ARGREDUCE_EXPORT int argreduce_lastaxis(const void* x, argreduce_dtype_t dtype, int64_t rows,
+                                        int64_t cols, argreduce_op_t op, int64_t* out_idx,
+                                        void* scratch, size_t scratch_bytes, void* stream) {
     Plan p;
-    rc = argreduce::make_plan(rows, cols, dtype, &p);
-    if (rc != ARGREDUCE_OK) return rc;
+    bool noop = false;
+    const int rc = argreduce::lastaxis_plan(x, dtype, rows, cols, op, out_idx, &p, &noop);
+    if (rc != ARGREDUCE_OK || noop) return rc;
     uint8_t* scratch16 = nullptr;
     if (p.scratch_bytes > 0) {
         if (scratch == nullptr || scratch_bytes < p.scratch_bytes)
             return ARGREDUCE_ERR_SCRATCH_TOO_SMALL;
         scratch16 = reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(scratch) + 15u) &
                                                ~static_cast<uintptr_t>(15u));
+    }
+    const hipError_t err = argreduce::launch(p, x, dtype, op, rows, cols, out_idx, scratch16,
+                                             static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? ARGREDUCE_OK : ARGREDUCE_ERR_HIP;
+}
+
+ARGREDUCE_EXPORT int argreduce_lastaxis_noalloc(const void* x, argreduce_dtype_t dtype,
+                                                int64_t rows, int64_t cols, argreduce_op_t op,
+                                                int64_t* out_idx, void* stream) {
+    Plan p;
+    bool noop = false;
+    const int rc = argreduce::lastaxis_plan(x, dtype, rows, cols, op, out_idx, &p, &noop);
+    if (rc != ARGREDUCE_OK || noop) return rc;
+    uint8_t* scratch16 = nullptr;
+    if (p.scratch_bytes > 0) {
+        if (p.scratch_bytes > ARGREDUCE_NOALLOC_SCRATCH_BYTES) return ARGREDUCE_ERR_SCRATCH_TOO_SMALL;
+        scratch16 = argreduce::noalloc_scratch();  // 256-byte aligned
+        if (scratch16 == nullptr) return ARGREDUCE_ERR_HIP;
     }
     const hipError_t err = argreduce::launch(p, x, dtype, op, rows, cols, out_idx, scratch16,
                                              static_cast<hipStream_t>(stream));

@@ -87,6 +87,11 @@ hipError_t launch_read_floor(const void* x, size_t bytes, uint32_t* out, uint32_
                              hipStream_t stream);
 void set_spin_limit(uint32_t polls);
 
+// The current device's copy of the library-held scratch of argreduce_lastaxis_noalloc
+// (ARGREDUCE_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned), located on the first call per
+// device; null when it cannot be located.
+uint8_t* noalloc_scratch();
+
 // Copies the current device's count of bounded waits that gave up to *count (synchronous).
 hipError_t read_wait_timeouts(unsigned long long* count);
 

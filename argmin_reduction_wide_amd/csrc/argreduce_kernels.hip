@@ -543,6 +543,29 @@ constexpr int kMaxSymbolDevices = 64;
 std::atomic<unsigned long long*> g_timeouts_addr[kMaxSymbolDevices];
 }  // namespace
 
+// Scratch of argreduce_lastaxis_noalloc: a file-scope device array, one copy per device,
+// held until the process ends. Host code never passes its name (on the host that is a
+// stand-in, not a device address); noalloc_scratch() returns the device's own address.
+static __device__ __align__(256) uint8_t noalloc_scratch_buf[ARGREDUCE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<uint8_t*> g_noalloc_addr[kMaxSymbolDevices];
+}  // namespace
+
+uint8_t* noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSymbolDevices) return nullptr;
+    uint8_t* p = g_noalloc_addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    // once per device, with that device current
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(noalloc_scratch_buf)) != hipSuccess || addr == nullptr)
+        return nullptr;
+    p = static_cast<uint8_t*>(addr);
+    g_noalloc_addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 unsigned long long* wait_timeouts_counter() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSymbolDevices) return nullptr;

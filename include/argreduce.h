@@ -129,6 +129,29 @@ int argreduce_lastaxis(const void *x, argreduce_dtype_t dtype, int64_t rows, int
                        size_t scratch_bytes, void *stream);
 
 /* ----------------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture that must
+ * not call hipMalloc, tight serving loops, harnesses that forbid allocation.
+ *
+ * argreduce_lastaxis without the scratch arguments: the scratch is a buffer the library
+ * holds, a device array of ARGREDUCE_NOALLOC_SCRATCH_BYTES bytes, one copy per device,
+ * located on the first call on that device and kept until the process ends. Same
+ * arguments otherwise, same results, kernels and status codes; the call allocates and
+ * frees nothing. Returns ARGREDUCE_ERR_SCRATCH_TOO_SMALL, before enqueuing anything, when
+ * argreduce_scratch_bytes(rows, cols, dtype) exceeds ARGREDUCE_NOALLOC_SCRATCH_BYTES (on
+ * MI355X no shape does: the split path needs at most 32 bytes per resident workgroup,
+ * 65,551 bytes in all, and rows wider than INT32_MAX a few tens of KiB at any size that
+ * fits in memory); ARGREDUCE_ERR_HIP when the buffer cannot be located.
+ *
+ * Every call on one device shares that device's buffer, which keeps the last call's
+ * contents (the next call needs nothing cleared: its words carry a per-call nonce). Calls
+ * that can overlap on one device (several streams, several host threads) race on the
+ * buffer and may return wrong indices: the caller must order them, e.g. on one stream.
+ */
+#define ARGREDUCE_NOALLOC_SCRATCH_BYTES (128u * 1024u)
+int argreduce_lastaxis_noalloc(const void *x, argreduce_dtype_t dtype, int64_t rows,
+                               int64_t cols, argreduce_op_t op, int64_t *out_idx, void *stream);
+
+/* ----------------------------------------------------------------------------------------
  * Launch plan and test hooks. The pages' tests force every dispatch path and simulate
  * devices of several thread capacities ("[CUDA] Parallelize ArgMax/ArgMin over wide last
  * axes", Description / Testing); these entry points expose the same controls.

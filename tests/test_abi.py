@@ -74,6 +74,29 @@ def test_null_and_misaligned_pointers(lib):
     assert B.argreduce_lastaxis(FAKE, B.F32, 2, 8, B.MAX, FAKE + 4, 0, 0, 0) == -1
 
 
+def test_noalloc_entry_point_checks_before_any_gpu_call(lib):
+    """argreduce_lastaxis_noalloc validates like argreduce_lastaxis, and refuses a plan
+    whose scratch exceeds the library-held array (ARGREDUCE_NOALLOC_SCRATCH_BYTES, as the
+    header defines it) before touching the device."""
+    text = open(HEADER).read()
+    m = re.search(r"#define ARGREDUCE_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u\)", text)
+    assert m and int(m.group(1)) * int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    f = lib.argreduce_lastaxis_noalloc
+    assert f(FAKE, B.F32, -1, 10, B.MAX, FAKE, 0) == -1
+    assert f(FAKE, B.F32, 4, 0, B.MAX, FAKE, 0) == -1
+    assert f(FAKE, 9, 4, 10, B.MAX, FAKE, 0) == -2
+    assert f(FAKE, B.F32, 4, 10, 7, FAKE, 0) == -1
+    assert f(0, B.F32, 4, 10, B.MAX, FAKE, 0) == -1
+    assert f(FAKE, B.F32, 4, 10, B.MAX, FAKE + 4, 0) == -1
+    assert f(0, B.F32, 0, 10, B.MAX, 0, 0) == 0
+    # the largest split scratch at MI355X capacity fits; a device four times larger does not
+    B.argreduce_debug_set_capacity(MI355X_THREADS)
+    assert B.argreduce_scratch_bytes(8, 1 << 20, B.F64) == 15 + 2048 * 32 <= B.NOALLOC_SCRATCH_BYTES
+    B.argreduce_debug_set_capacity(4 * MI355X_THREADS)
+    assert B.argreduce_scratch_bytes(32, 1 << 20, B.F64) > B.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, B.F64, 32, 1 << 20, B.MAX, FAKE, 0) == -4
+
+
 def test_zero_rows_is_a_no_op(lib):
     assert B.argreduce_lastaxis(0, B.F32, 0, 8, B.MAX, 0, 0, 0, 0) == 0
 
