@@ -227,6 +227,13 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         int64_t grid_rows = max_grid / blocks_per_row;
         grid_rows = grid_rows > 0 ? grid_rows : 1;
         grid_rows = rows1 < grid_rows ? rows1 : grid_rows;
+        if (blocks_per_row > 1) {
+            // a split row's workgroups wait on each other: every row's team is launched at
+            // once (the split kernel has no row loop)
+            if (rows1 > static_cast<int64_t>(std::numeric_limits<uint32_t>::max()) / blocks_per_row)
+                return ARGREDUCE_ERR_TOO_WIDE;
+            grid_rows = rows1;
+        }
         p->lanes_per_row = static_cast<int>(blocks_per_row * kBlock);
         p->blocks_per_row = static_cast<int>(blocks_per_row);
         p->unroll = static_cast<int>(unroll);

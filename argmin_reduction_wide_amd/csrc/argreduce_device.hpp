@@ -521,7 +521,11 @@ __device__ inline void scan_step(const uint8_t* __restrict__ body, uint32_t base
 // is harmless (a NaN is never taken; any other value gives the same or a tie-losing
 // candidate). The other lanes, and every step, carry no position-0 test. Lane 0 issues
 // the seed's load (raw bits: a conversion right after it would wait for it) before the
-// scan and converts it after.
+// scan and converts it after. The load is a relaxed wavefront-scope atomic load, which is
+// always a vector-memory load: with the row address uniform across the wavefront a plain
+// (or nontemporal) load becomes a scalar load, whose value the compiler moves into a vector
+// register at once, so the wavefront would wait one memory latency before issuing any load
+// of the scan.
 template <typename Fmt, int OP, int U>
 __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, uint32_t lane,
                                 uint32_t team, Cand<typename Fmt::C, OP>& c, bool origin = true) {
@@ -529,7 +533,9 @@ __device__ inline void scan_row(const uint8_t* __restrict__ row, uint32_t cols, 
     c.init();
     const bool seeded = origin & (lane == 0);
     typename Fmt::Bits x0 = 0;
-    if (seeded) x0 = *reinterpret_cast<const typename Fmt::Bits*>(row);
+    if (seeded)
+        x0 = __hip_atomic_load(reinterpret_cast<const typename Fmt::Bits*>(row), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
     const uint32_t misalign = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
     uint32_t head = ((16u - misalign) & 15u) / Fmt::kSize;
     head = head < cols ? head : cols;

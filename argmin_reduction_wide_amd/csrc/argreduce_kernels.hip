@@ -5,12 +5,15 @@
 // block per row, several blocks per row, more rows than grid rows), re-cut for 64-lane
 // wavefronts:
 //
-//   k_subwave  a group of G lanes (G = 1..64, a power of two) of one wavefront per row;
-//              G = 64 is a wavefront per row. Rows beyond the grid are looped over.
+//   k_narrow   rows of at most 32 whole 16-byte vectors starting 16-byte aligned: a group
+//              of G lanes (G = 1..32, a power of two) per row, one vector per lane.
+//   k_subwave  a group of G lanes (G = 1..64, a power of two) of one wavefront per row, any
+//              alignment; G = 64 is a wavefront per row. Rows beyond the grid are looped over.
 //              Narrow rows use the group idea of TVM's shared-memory reduction page
 //              ("reduction -> shared", Algorithm: group size from the reduction length,
 //              a tree within the group; here on the DPP crossbar).
-//   k_blocks   B workgroups of 256 threads per row; B == 1 is a workgroup per row.
+//   k_blocks   a workgroup of 256 threads per row; rows beyond the grid are looped over.
+//   k_split    B > 1 workgroups per row, every row's team launched at once.
 //   k_wide     rows wider than INT32_MAX: one workgroup per window of at most 2^30
 //              elements (32-bit positions inside it), k_wide_merge as a second dispatch.
 //
@@ -43,7 +46,7 @@
 // device every workgroup is resident at once. Larger grids (forced plans), or a device
 // shared with other work, rely on each XCD starting the workgroups it is given in id order,
 // which makes every wait end by induction on the id. The poll is bounded all the same:
-// should a word never arrive, out[r] = -1 and the device's timeout counter
+// should a word never arrive, out[r] = -1 and the device's timeout counter g_wait_timeouts
 // (argreduce_wait_timeouts) goes up by one (never observed outside tests that force it).
 #include <hip/hip_ext.h>
 
@@ -55,6 +58,12 @@
 #include "argreduce_launch.hpp"
 
 namespace argreduce {
+
+// Bounded waits of the split kernel that gave up, one copy per device (read by
+// argreduce_wait_timeouts). The kernel names it directly rather than taking its address as
+// an argument: its arguments (14 dwords) then all fit the SGPRs preloaded at wave launch,
+// and a fifteenth would be read from kernel-argument memory, on the host, by every wave.
+__device__ unsigned long long g_wait_timeouts;
 
 template <typename Fmt, int OP, int G, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
@@ -72,96 +81,209 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
     }
 }
 
+// Narrow rows that start 16-byte aligned and are a whole number nvec <= G of 16-byte
+// vectors (the common case of the narrow path, e.g. [65536, 64] fp16: 8 vectors): a group
+// of G lanes per row, one vector per lane, no head or tail, and position 0 taken from lane
+// 0's own vector (no separate seed load). Each lane keeps one candidate for its VW
+// elements with the step-slot trick of scan_step, the group merges on the DPP crossbar,
+// and the group's last lane stores the index. Lanes past nvec hold all-ones bits (NaN in
+// every format), which no comparison takes. One row per group while the grid covers the
+// rows; beyond that the groups loop over rows.
+template <typename Fmt, int OP, int G>
+__global__ __launch_bounds__(kBlockThreads) void k_narrow(const uint8_t* __restrict__ x,
+                                                          uint32_t nvec, int64_t rows,
+                                                          int64_t* __restrict__ out) {
+    using C = typename Fmt::C;
+    using Vec = typename Fmt::Vec;
+    using K = Cand<C, OP>;
+    constexpr int VW = Fmt::VW;
+    constexpr uint32_t kNoSlot = 0xffffffffu;
+    const uint32_t lane = threadIdx.x % G;
+    const int64_t first = (static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x) / G;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * (kBlockThreads / G);
+    const size_t row_bytes = static_cast<size_t>(nvec) * 16u;
+    const bool has = lane < nvec;
+    const uint32_t dl = has ? lane : nvec - 1;  // a lane past the row re-reads its last vector
+    for (int64_t r = first; r < rows; r += stride) {
+        Vec q = __builtin_nontemporal_load(
+            reinterpret_cast<const Vec*>(x + static_cast<size_t>(r) * row_bytes + dl * 16u));
+        u32x4 w = __builtin_bit_cast(u32x4, q);
+        w.x = has ? w.x : 0xffffffffu;
+        w.y = has ? w.y : 0xffffffffu;
+        w.z = has ? w.z : 0xffffffffu;
+        w.w = has ? w.w : 0xffffffffu;
+        C e[VW];
+        Fmt::unpack(__builtin_bit_cast(Vec, w), e);
+        C lv = K::identity();
+        uint32_t ls = kNoSlot;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+            const bool t = K::kLast ? (K::better(e[k], lv) | (e[k] == lv)) : K::better(e[k], lv);
+            lv = t ? e[k] : lv;
+            ls = t ? static_cast<uint32_t>(k) : ls;
+        }
+        K c;
+        c.init();
+        c.merge(lv, ls == kNoSlot ? K::kNone : lane * VW + ls);
+        if (lane == 0) {  // position 0 as its own candidate (fix(x0), 0)
+            K f;
+            f.take_first(e[0]);
+            c.merge(f.v, f.i);
+        }
+        group_merge<G>(c);
+        if (lane == G - 1) out[r] = K::result(c.i);
+    }
+}
+
+// One published candidate of a split row: polls its words (agent-scope atomic loads) until
+// each carries this call's nonce and the index is one a lane's scan can produce, at most
+// about spin_limit polls. The polls are unrolled four at a time with the bound checked once
+// per four: a loop that tested the bound and the words' validity on separate branches every
+// poll measured 0.1-0.15 us slower per call on split rows.
+template <typename C, int OP>
+__device__ inline bool poll_candidate(const uint64_t* e, uint64_t tag, uint32_t cols,
+                                      uint32_t spin_limit, C& v, uint32_t& idx) {
+    constexpr int kW = Words<C>::kWords;
+    for (uint32_t spins = 0;; spins += 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint64_t w[kW];
+#pragma unroll
+            for (int j = 0; j < kW; ++j)
+                w[j] = __hip_atomic_load(&e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t pay[kW];
+            bool tags = true;
+#pragma unroll
+            for (int j = 0; j < kW; ++j) {
+                tags = tags & ((w[j] & 0xffffffff00000000ull) == tag);
+                pay[j] = static_cast<uint32_t>(w[j]);
+            }
+            if (tags & Cand<C, OP>::valid_index(pay[0], cols)) {
+                Words<C>::unpack(pay, v, idx);
+                return true;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (spins >= spin_limit) return false;
+    }
+}
+
+template <typename C>
+__device__ inline void clear_candidate(uint64_t* e) {
+#pragma unroll
+    for (int j = 0; j < Words<C>::kWords; ++j)
+        __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup per row; rows beyond the grid are looped over.
+template <typename Fmt, int OP, int U>
+__global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restrict__ x,
+                                                          int64_t rows,
+                                                          int64_t* __restrict__ out,
+                                                          uint32_t cols) {
+    using K = Cand<typename Fmt::C, OP>;
+    const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        K c;
+        scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, threadIdx.x,
+                             kBlockThreads, c);
+        block_merge(c);
+        if (threadIdx.x == 0) out[r] = K::result(c.i);
+    }
+}
+
+// A row split over B > 1 workgroups: workgroup b of row r = blockIdx / B scans the row's
+// lanes b * 256 .. b * 256 + 255 of a team of B * 256 lanes (one row per team, every row's
+// team launched at once). Workgroups b < B - 1 publish their candidate; workgroup B - 1
+// finalizes the row.
+//
 // Eight waves per SIMD (at most 64 VGPRs): eight workgroups of 256 threads per CU, so a
 // grid of up to (CUs * 2048 / 256) workgroups, the most an automatic split plan launches,
-// is resident at once on an otherwise idle device, whatever the format and unroll.
+// is resident at once on an otherwise idle device, whatever the format and unroll. (A row
+// loop here cost registers: values the compiler hoisted out of it stayed live through the
+// scan and pushed the U = 8 instances past 64 VGPRs.)
 template <typename Fmt, int OP, int U>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
-void k_blocks(const uint8_t* __restrict__ x, int64_t rows, int64_t grid_rows,
-              int64_t* __restrict__ out, uint64_t* __restrict__ slots, uint32_t cols,
-              uint32_t B, uint32_t nonce, uint32_t spin_limit,
-              unsigned long long* __restrict__ timeouts) {
+void k_split(const uint8_t* __restrict__ x, int64_t* __restrict__ out,
+             uint64_t* __restrict__ slots, uint32_t cols, uint32_t B, uint32_t nonce,
+             uint32_t spin_limit) {
     using C = typename Fmt::C;
+    using K = Cand<C, OP>;
     __shared__ int s_timeout;
     const uint32_t b = blockIdx.x % B;
-    const int64_t slot = blockIdx.x / B;
-    const uint32_t team = B * kBlockThreads;
-    const uint32_t lane = b * kBlockThreads + threadIdx.x;
-    const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
-    for (int64_t r = slot; r < rows; r += grid_rows) {
-        // Thread 0 read the previous row's flag itself, and every other thread's writes to it
-        // came before the barriers of that row's last merge; this row's writes come after
-        // the barriers of the merge below.
-        if (threadIdx.x == 0) s_timeout = 0;
-        const uint8_t* row = x + static_cast<size_t>(r) * row_bytes;
-        Cand<C, OP> c;
-        scan_row<Fmt, OP, U>(row, cols, lane, team, c);
-        block_merge(c);
-        if (B == 1) {
-            if (threadIdx.x == 0) out[r] = Cand<C, OP>::result(c.i);
-            continue;
-        }
-        uint64_t* rs = slots + static_cast<size_t>(r) * B * Words<C>::kStride;
-        const uint64_t tag = static_cast<uint64_t>(nonce) << 32;
-        if (b != B - 1) {
-            if (threadIdx.x == 0) {
-                uint64_t* e = rs + static_cast<size_t>(b) * Words<C>::kStride;
-                uint32_t pay[Words<C>::kWords];
-                Words<C>::pack(c.v, c.i, pay);
+    const uint32_t r = blockIdx.x / B;
+    if (threadIdx.x == 0) s_timeout = 0;  // read after the barriers of the last merge
+    K c;
+    scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * cols * Fmt::kSize, cols,
+                         b * kBlockThreads + threadIdx.x, B * kBlockThreads, c);
+    block_merge(c);
+    uint64_t* rs = slots + static_cast<size_t>(r) * B * Words<C>::kStride;
+    const uint64_t tag = static_cast<uint64_t>(nonce) << 32;
+    if (b != B - 1) {
+        if (threadIdx.x == 0) {
+            uint64_t* e = rs + static_cast<size_t>(b) * Words<C>::kStride;
+            uint32_t pay[Words<C>::kWords];
+            Words<C>::pack(c.v, c.i, pay);
 #pragma unroll
-                for (int w = 0; w < Words<C>::kWords; ++w)
-                    __hip_atomic_store(&e[w], tag | pay[w], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-            continue;
+            for (int w = 0; w < Words<C>::kWords; ++w)
+                __hip_atomic_store(&e[w], tag | pay[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        // The row's finalizing workgroup.
-        Cand<C, OP> m;
+        return;
+    }
+    // The row's finalizing workgroup. Its index goes out as an agent-scope store (written
+    // through, like the published words), which measured 0.06 us faster per call on
+    // [32, 202048] than a plain store.
+    if (B - 1 <= static_cast<uint32_t>(kWave)) {
+        // At most one published candidate per lane of wavefront 0: it polls and merges them
+        // alone (no LDS round, no barrier); its lane 0 holds this workgroup's own candidate.
+        if (threadIdx.x >= static_cast<uint32_t>(kWave)) return;
+        K m;
         if (threadIdx.x == 0) {
             m = c;
         } else {
             m.init();
         }
-        for (uint32_t k = threadIdx.x; k + 1 < B; k += kBlockThreads) {
-            uint64_t* e = rs + static_cast<size_t>(k) * Words<C>::kStride;
-            uint32_t pay[Words<C>::kWords];
-            uint32_t spins = 0;
-            bool ok = false;
-            while (!ok) {
-                uint64_t w[Words<C>::kWords];
-#pragma unroll
-                for (int j = 0; j < Words<C>::kWords; ++j)
-                    w[j] = __hip_atomic_load(&e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = true;
-#pragma unroll
-                for (int j = 0; j < Words<C>::kWords; ++j) {
-                    ok = ok && (w[j] & 0xffffffff00000000ull) == tag;
-                    pay[j] = static_cast<uint32_t>(w[j]);
-                }
-                ok = ok && Cand<C, OP>::valid_index(pay[0], cols);
-                if (!ok) {
-                    if (++spins > spin_limit) {
-                        s_timeout = 1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-                }
-            }
-            if (ok) {
-                C v;
-                uint32_t idx;
-                Words<C>::unpack(pay, v, idx);
-                m.merge(v, idx);
-            }
-#pragma unroll
-            for (int j = 0; j < Words<C>::kWords; ++j)
-                __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
+        if (threadIdx.x + 1 < B) {
+            uint64_t* e = rs + static_cast<size_t>(threadIdx.x) * Words<C>::kStride;
+            C v;
+            uint32_t idx;
+            ok = poll_candidate<C, OP>(e, tag, cols, spin_limit, v, idx);
+            if (ok) m.merge(v, idx);
+            clear_candidate<C>(e);
         }
-        block_merge(m);
-        if (threadIdx.x == 0) {
-            out[r] = s_timeout ? int64_t{-1} : Cand<C, OP>::result(m.i);
-            if (s_timeout) __hip_atomic_fetch_add(timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool gave_up = __ballot(!ok) != 0;
+        group_merge<kWave>(m);
+        if (threadIdx.x == kWave - 1) {
+            __hip_atomic_store(&out[r], gave_up ? int64_t{-1} : K::result(m.i), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (gave_up)
+                __hip_atomic_fetch_add(&g_wait_timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        return;
+    }
+    K m;
+    if (threadIdx.x == 0) {
+        m = c;
+    } else {
+        m.init();
+    }
+    for (uint32_t k = threadIdx.x; k + 1 < B; k += kBlockThreads) {
+        uint64_t* e = rs + static_cast<size_t>(k) * Words<C>::kStride;
+        C v;
+        uint32_t idx;
+        if (poll_candidate<C, OP>(e, tag, cols, spin_limit, v, idx))
+            m.merge(v, idx);
+        else
+            s_timeout = 1;
+        clear_candidate<C>(e);
+    }
+    block_merge(m);
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(&out[r], s_timeout ? int64_t{-1} : K::result(m.i), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (s_timeout)
+            __hip_atomic_fetch_add(&g_wait_timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -514,9 +636,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_read_floor(const u32x4* __res
     if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
 }
 
-// Bounded waits that gave up, per device (read by argreduce_wait_timeouts).
-__device__ unsigned long long g_wait_timeouts;
-
 std::atomic<uint32_t> g_nonce{0};
 
 uint32_t next_nonce() {
@@ -566,24 +685,24 @@ uint8_t* noalloc_scratch() {
     return p;
 }
 
-unsigned long long* wait_timeouts_counter() {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSymbolDevices) return nullptr;
-    unsigned long long* p = g_timeouts_addr[dev].load(std::memory_order_acquire);
-    if (p != nullptr) return p;
-    // the device's own copy of the counter: host code never passes the variable's name
-    void* addr = nullptr;
-    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(g_wait_timeouts)) != hipSuccess || addr == nullptr)
-        return nullptr;
-    p = static_cast<unsigned long long*>(addr);
-    g_timeouts_addr[dev].store(p, std::memory_order_release);
-    return p;
-}
-
 hipError_t read_wait_timeouts(unsigned long long* count) {
-    unsigned long long* p = wait_timeouts_counter();
-    if (p == nullptr) return hipErrorInvalidSymbol;
-    return hipMemcpy(count, p, sizeof(*count), hipMemcpyDeviceToHost);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSymbolDevices)
+        return hipErrorInvalidDevice;
+    unsigned long long* p = g_timeouts_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // the device's own copy of the counter: host code never passes the variable's name
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(g_wait_timeouts)) != hipSuccess || addr == nullptr)
+            return hipErrorInvalidSymbol;
+        p = static_cast<unsigned long long*>(addr);
+        g_timeouts_addr[dev].store(p, std::memory_order_release);
+    }
+    unsigned long long split = 0, scan = 0;
+    hipError_t e = hipMemcpy(&split, p, sizeof(split), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = read_scan_wait_timeouts(&scan);
+    if (e == hipSuccess) *count = split + scan;
+    return e;
 }
 
 namespace {
@@ -597,10 +716,13 @@ void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows
 
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
-                   uint64_t* slots, unsigned long long* timeouts, hipStream_t s) {
-    launch_scan(k_blocks<Fmt, OP, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, rows,
-                p.grid_rows, out, slots, cols, static_cast<uint32_t>(p.blocks_per_row),
-                p.blocks_per_row > 1 ? next_nonce() : 0u, spin_limit(), timeouts);
+                   uint64_t* slots, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+    if (p.blocks_per_row > 1)
+        launch_scan(k_split<Fmt, OP, U>, grid, s, x, out, slots, cols,
+                    static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
+    else
+        launch_scan(k_blocks<Fmt, OP, U>, grid, s, x, rows, out, cols);
 }
 
 template <typename Fmt, int OP>
@@ -609,8 +731,26 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
     const uint8_t* x = static_cast<const uint8_t*>(xv);
     const uint32_t c32 = static_cast<uint32_t>(cols);
     if (p.path == ARGREDUCE_PATH_SUBWAVE) {
-        // Narrow groups cover their row with one vector per lane; a wavefront per row keeps
-        // up to 8 vectors per lane in flight.
+        // Rows of whole 16-byte vectors starting 16-byte aligned, at most 32 of them: the
+        // narrow kernel (one vector per lane, no head, tail or seed load).
+        const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
+        if (p.lanes_per_row <= 32 && p.unroll == 1 && row_bytes % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+            const uint32_t nvec = static_cast<uint32_t>(row_bytes / 16);
+            const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+            switch (p.lanes_per_row) {
+                case 1: launch_scan(k_narrow<Fmt, OP, 1>, grid, s, x, nvec, rows, out); break;
+                case 2: launch_scan(k_narrow<Fmt, OP, 2>, grid, s, x, nvec, rows, out); break;
+                case 4: launch_scan(k_narrow<Fmt, OP, 4>, grid, s, x, nvec, rows, out); break;
+                case 8: launch_scan(k_narrow<Fmt, OP, 8>, grid, s, x, nvec, rows, out); break;
+                case 16: launch_scan(k_narrow<Fmt, OP, 16>, grid, s, x, nvec, rows, out); break;
+                case 32: launch_scan(k_narrow<Fmt, OP, 32>, grid, s, x, nvec, rows, out); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+        // Other narrow rows: groups cover their row with one vector per lane; a wavefront per
+        // row keeps up to 8 vectors per lane in flight.
         switch (p.lanes_per_row * 100 + p.unroll) {
             case 101: launch_subwave<Fmt, OP, 1, 1>(p, x, c32, rows, out, s); break;
             case 201: launch_subwave<Fmt, OP, 2, 1>(p, x, c32, rows, out, s); break;
@@ -643,16 +783,11 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
         return hipGetLastError();
     }
     uint64_t* slots = p.blocks_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
-    unsigned long long* tmo = nullptr;
-    if (p.blocks_per_row > 1) {
-        tmo = wait_timeouts_counter();
-        if (tmo == nullptr) return hipErrorInvalidSymbol;
-    }
     switch (p.unroll) {
-        case 1: launch_blocks<Fmt, OP, 1>(p, x, c32, rows, out, slots, tmo, s); break;
-        case 2: launch_blocks<Fmt, OP, 2>(p, x, c32, rows, out, slots, tmo, s); break;
-        case 4: launch_blocks<Fmt, OP, 4>(p, x, c32, rows, out, slots, tmo, s); break;
-        case 8: launch_blocks<Fmt, OP, 8>(p, x, c32, rows, out, slots, tmo, s); break;
+        case 1: launch_blocks<Fmt, OP, 1>(p, x, c32, rows, out, slots, s); break;
+        case 2: launch_blocks<Fmt, OP, 2>(p, x, c32, rows, out, slots, s); break;
+        case 4: launch_blocks<Fmt, OP, 4>(p, x, c32, rows, out, slots, s); break;
+        case 8: launch_blocks<Fmt, OP, 8>(p, x, c32, rows, out, slots, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -20,10 +20,8 @@ uint32_t next_nonce();
 uint32_t spin_limit();
 void set_spin_limit(uint32_t polls);  // 0 restores the default
 
-// The current device's counter of bounded waits that gave up (a device variable of the
-// library, located on first use per device); null when it cannot be located. Kernels that
-// wait take it as an argument and add 1 per row or tile whose wait gave up.
-unsigned long long* wait_timeouts_counter();
+// Copies the current device's count of look-back waits of the scan that gave up (synchronous).
+hipError_t read_scan_wait_timeouts(unsigned long long* count);
 
 // Measurement events (argreduce_debug_set_kernel_events); null when unset.
 extern std::atomic<hipEvent_t> g_ev_start;

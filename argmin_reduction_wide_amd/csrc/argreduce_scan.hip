@@ -47,7 +47,7 @@
 // workgroups it is given in id order (then every wait ends, by induction on the id), the
 // assumption of any look-back scan whose tile ids are workgroup ids. The wait is bounded
 // all the same: on a timeout the tile's indices are -1 and the device's timeout counter
-// goes up by one (never observed outside tests that force it).
+// g_scan_wait_timeouts goes up by one (never observed outside tests that force it).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -59,6 +59,19 @@
 #include "argreduce_launch.hpp"
 
 namespace argreduce {
+
+// Look-back waits that gave up, one copy per device (added into argreduce_wait_timeouts).
+// Named directly by the kernel, like the split kernel's counter, so that no argument
+// carries its address.
+__device__ unsigned long long g_scan_wait_timeouts;
+
+hipError_t read_scan_wait_timeouts(unsigned long long* count) {
+    void* addr = nullptr;  // the current device's copy
+    hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(g_scan_wait_timeouts));
+    if (e != hipSuccess) return e;
+    return hipMemcpy(count, addr, sizeof(*count), hipMemcpyDeviceToHost);
+}
+
 namespace {
 
 constexpr uint32_t kEmpty = 0xffffffffu;  // index of the empty piece
@@ -359,8 +372,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
                                                        uint32_t T, uint8_t* __restrict__ out_val,
                                                        int64_t* __restrict__ out_idx,
                                                        uint64_t* __restrict__ states, uint32_t nonce,
-                                                       uint32_t spin_limit,
-                                                       unsigned long long* __restrict__ timeouts) {
+                                                       uint32_t spin_limit) {
     using C = typename Fmt::C;
     using Op = ScanOp<C, OP>;
     using S = typename Out<Fmt>::S;
@@ -487,7 +499,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_cum(const uint8_t* __restrict
             s_i[kWaves] = pi;
             if (!ok) {
                 s_fail = 1;
-                __hip_atomic_fetch_add(timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&g_scan_wait_timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -583,10 +595,7 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
                          uint8_t* scratch16, hipStream_t s) {
     uint64_t* states = p.tiles_per_row > 1 ? reinterpret_cast<uint64_t*>(scratch16) : nullptr;
     uint32_t nonce = 0;
-    unsigned long long* tmo = nullptr;
     if (states != nullptr) {
-        tmo = wait_timeouts_counter();
-        if (tmo == nullptr) return hipErrorInvalidSymbol;
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess) return hipErrorInvalidValue;
         if (cs == hipStreamCaptureStatusActive) {
@@ -605,17 +614,17 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
     constexpr int UT = kScanUnrollTiny, US = kScanUnrollShort, UL = kScanUnrollLong;
     if (p.unroll == UT && p.vecio)
-        launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == UT)
-        launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == US && p.vecio)
-        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, US, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == US)
-        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, US, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.vecio)
-        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, UL, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else
-        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit(), tmo);
+        launch_scan(k_cum<Fmt, OP, UL, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     return hipGetLastError();
 }
 

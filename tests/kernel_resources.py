@@ -20,19 +20,25 @@ VGPR_GRANULE = 8
 MAX_WAVES_PER_SIMD = 8
 
 
-def _sections(elf: bytes) -> dict[str, tuple[int, int, int]]:
-    """name -> (type, offset, size) of every section of a 64-bit little-endian ELF."""
+def _section_headers(elf: bytes) -> list[tuple]:
+    """(name, type, addr, offset, size, link, entsize) of every section of a 64-bit
+    little-endian ELF."""
     assert elf[:4] == b"\x7fELF" and elf[4] == 2 and elf[5] == 1, "not an ELF64 LE file"
     shoff = struct.unpack_from("<Q", elf, 0x28)[0]
     shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
     hdrs = [struct.unpack_from("<IIQQQQIIQQ", elf, shoff + k * shentsize) for k in range(shnum)]
     stroff = hdrs[shstrndx][4]
-    out = {}
+    out = []
     for h in hdrs:
-        name_off, stype, _, _, off, size = h[:6]
+        name_off, stype, _, addr, off, size, link, _, _, entsize = h
         end = elf.index(b"\0", stroff + name_off)
-        out[elf[stroff + name_off:end].decode()] = (stype, off, size)
+        out.append((elf[stroff + name_off:end].decode(), stype, addr, off, size, link, entsize))
     return out
+
+
+def _sections(elf: bytes) -> dict[str, tuple[int, int, int]]:
+    """name -> (type, offset, size) of every section of a 64-bit little-endian ELF."""
+    return {h[0]: (h[1], h[3], h[4]) for h in _section_headers(elf)}
 
 
 def _code_objects(lib_bytes: bytes, arch: str) -> list[bytes]:
@@ -70,8 +76,30 @@ def _metadata(code_object: bytes) -> dict:
     raise ValueError("no AMDGPU metadata note in the code object")
 
 
+def _kernel_descriptors(code_object: bytes) -> dict[str, bytes]:
+    """symbol name (without ".kd") -> the 64-byte kernel descriptor, from the symbol table."""
+    hdrs = _section_headers(code_object)
+    out = {}
+    for name, stype, _, off, size, link, entsize in hdrs:
+        if stype != 2:  # SHT_SYMTAB
+            continue
+        stroff = hdrs[link][3]
+        for k in range(size // entsize):
+            st_name, _, _, shndx, value, sz = struct.unpack_from("<IBBHQQ", code_object, off + k * entsize)
+            end = code_object.index(b"\0", stroff + st_name)
+            sym = code_object[stroff + st_name:end].decode()
+            if sym.endswith(".kd") and sz == 64:
+                sec = hdrs[shndx]
+                at = sec[3] + (value - sec[2])
+                out[sym[:-3]] = code_object[at:at + 64]
+    return out
+
+
 def kernels(lib_path: str, arch: str = "gfx950") -> list[dict]:
-    """One metadata record per kernel of every ``arch`` code object in the library."""
+    """One metadata record per kernel of every ``arch`` code object in the library, with
+    ".preload_dwords" added: the kernel-argument dwords the descriptor has the hardware
+    preload into SGPRs at wave launch (KERNARG_PRELOAD_SPEC_LENGTH, bits 0-6 of the 16-bit
+    field at byte 58 of the descriptor); arguments beyond them are loaded from memory."""
     with open(lib_path, "rb") as f:
         data = f.read()
     objs = _code_objects(data, arch)
@@ -79,8 +107,18 @@ def kernels(lib_path: str, arch: str = "gfx950") -> list[dict]:
         raise ValueError(f"no {arch} code object in {lib_path}")
     out = []
     for co in objs:
-        out.extend(_metadata(co)["amdhsa.kernels"])
+        kds = _kernel_descriptors(co)
+        for k in _metadata(co)["amdhsa.kernels"]:
+            kd = kds.get(k[".symbol"][:-3] if k[".symbol"].endswith(".kd") else k[".symbol"])
+            k[".preload_dwords"] = None if kd is None else struct.unpack_from("<H", kd, 58)[0] & 0x7F
+            out.append(k)
     return out
+
+
+def explicit_arg_bytes(k: dict) -> int:
+    """Bytes of a kernel's own arguments (the hidden ones the runtime appends excluded)."""
+    args = [a for a in k[".args"] if not a[".value_kind"].startswith("hidden")]
+    return max((a[".offset"] + a[".size"] for a in args), default=0)
 
 
 def waves_per_simd(k: dict) -> int:

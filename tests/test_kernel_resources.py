@@ -3,7 +3,7 @@ metadata of the library (CPU only), and the split plans checked against them.
 
 The split path's finalizing workgroup waits for the other workgroups of its row. The
 automatic plans launch at most one device wave of 256-thread workgroups (CUs * 2048 / 256)
-and k_blocks is compiled for eight waves per SIMD, so every workgroup of such a grid is
+and the split kernel (k_split) is compiled for eight waves per SIMD, so every workgroup of such a grid is
 resident at once on an otherwise idle device: no wait depends on the order in which the
 dispatcher starts workgroups. These tests pin both halves of that argument.
 """
@@ -36,8 +36,8 @@ def blocks_per_cu(k: dict) -> int:
 
 
 def split_kernels(kernels, fmt: str, unroll: int) -> list[dict]:
-    """The k_blocks<fmt, op, unroll> instances, every op."""
-    pat = re.compile(rf"k_blocksINS_\d+{fmt}ELi\dELi{unroll}EEE")
+    """The k_split<fmt, op, unroll> instances, every op."""
+    pat = re.compile(rf"k_splitINS_\d+{fmt}ELi\dELi{unroll}EEE")
     return [k for k in kernels if pat.search(k[".name"])]
 
 
@@ -48,9 +48,9 @@ def test_every_format_op_and_unroll_of_the_split_kernel_is_present(kernels):
 
 
 def test_split_kernel_holds_a_full_cu(kernels):
-    """Every k_blocks instance: at most 64 VGPRs (eight waves per SIMD), no private
+    """Every k_split instance: at most 64 VGPRs (eight waves per SIMD), no private
     (spill) memory, LDS for eight workgroups per CU."""
-    ks = [k for k in kernels if "k_blocks" in k[".name"]]
+    ks = [k for k in kernels if "k_split" in k[".name"]]
     assert len(ks) == 4 * 4 * 4
     for k in ks:
         assert k[".wavefront_size"] == 64
@@ -65,6 +65,16 @@ def test_no_kernel_uses_private_memory(kernels):
     for k in kernels:
         assert k[".private_segment_fixed_size"] == 0, k[".name"]
         assert not k.get(".uses_dynamic_stack", False), k[".name"]
+
+
+def test_every_kernel_argument_is_preloaded(kernels):
+    """Each kernel's own arguments fit the SGPRs the hardware preloads at wave launch (at
+    most 14 dwords here): an argument beyond them would be read from kernel-argument memory
+    by every wave, which with arguments kept in host memory is a read across PCIe per wave."""
+    for k in kernels:
+        assert k[".preload_dwords"] is not None, k[".name"]
+        assert K.explicit_arg_bytes(k) <= 4 * k[".preload_dwords"], (
+            k[".name"], K.explicit_arg_bytes(k), k[".preload_dwords"])
 
 
 SHAPES = [(r, c) for r in (1, 2, 3, 8, 32, 100, 255, 256, 1000)
@@ -110,7 +120,7 @@ def test_fp64_split_at_a_full_device_wave(kernels):
 
 def test_metadata_reader_sees_both_sources(kernels):
     names = " ".join(k[".name"] for k in kernels)
-    for kernel in ("k_subwave", "k_blocks", "k_axis", "k_axis_merge", "k_wide", "k_cum",
-                   "k_read_floor"):
+    for kernel in ("k_narrow", "k_subwave", "k_blocks", "k_split", "k_axis", "k_axis_merge",
+                   "k_wide", "k_cum", "k_read_floor"):
         assert kernel in names, kernel
     assert os.path.getsize(B.LIB_PATH) > 0

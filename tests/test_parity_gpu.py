@@ -109,6 +109,38 @@ def test_forced_paths_ragged_misaligned(oracle_lib, hooks, path, cap):
                           f"plan={B.argreduce_plan(rows, cols, dtype)}", offset_elems=offset)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_narrow_aligned_rows(oracle_lib, hooks, dtype):
+    """Rows of 1..32 whole 16-byte vectors starting 16-byte aligned (the narrow kernel: a
+    group of G = next power of two lanes per row, lanes past the row masked, position 0 from
+    lane 0's own vector): every vector count around the powers of two, special values with a
+    leading NaN in some rows, every op; then, under a four-workgroup capacity, more rows
+    than the grid holds (groups loop over rows); and the same widths one element short
+    (misaligned: the generic lane-group kernel) for contrast."""
+    rng = np.random.default_rng(1300 + DTYPES.index(dtype))
+    v = VW[dtype]
+    for nvec in (1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 24, 31, 32):
+        cols = nvec * v
+        for rows in (1, 7, 300):
+            for kind in ("special", "ties", "mixed"):
+                arr = W.random_rows(rng, rows, cols, dtype, kind)
+                if kind == "special":
+                    arr[::3, 0] = W.to_storage(np.array([np.nan]), dtype)[0]
+                for op in OPS:
+                    check(oracle_lib, arr, dtype, op, f"narrow nvec={nvec} rows={rows} kind={kind} "
+                          f"plan={B.argreduce_plan(rows, cols, dtype)}")
+        if cols > 1:
+            arr = W.random_rows(rng, 5, cols - 1, dtype, "ties")
+            check(oracle_lib, arr, dtype, "max", f"narrow-minus-one cols={cols - 1}")
+    B.argreduce_debug_set_capacity(1024)
+    for nvec in (3, 8, 32):
+        arr = W.random_rows(rng, 20000, nvec * v, dtype, "ties")
+        p = B.argreduce_plan(20000, nvec * v, dtype)
+        assert p["grid_rows"] < 20000, p
+        for op in OPS:
+            check(oracle_lib, arr, dtype, op, f"narrow row loop nvec={nvec} plan={p}")
+
+
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
 def test_special_value_fuzz(oracle_lib, hooks, cap):
     """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal} under several capacities."""
