@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kBlock = 256;
+constexpr int64_t kWave = 64;
 // Rows of up to this many 16-byte vectors (4 KiB) are scanned by one wavefront; rows of up
 // to kBlockRowMaxVec (32 KiB) by one workgroup with all of a lane's loads in one step.
 constexpr int64_t kWaveRowMaxVec = 256;
@@ -155,19 +156,26 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
     const int64_t rows1 = rows > 0 ? rows : 1;
     // Split rows: the fewest 16-byte loads per lane (U) for which one step of
-    // B = ceil(vec_row / (256 U)) workgroups per row covers the row, while the workgroups of
-    // every row fit in one device wave and the row's finalizing workgroup polls at most one
-    // published word per thread (B <= 256; a second word per thread costs a second round
-    // trip). A call of a few rows is latency-bound: the time after the last load arrives
-    // (the lane's compares, then the merges) grows with U, and more workgroups cost little.
-    // Failing that, 8 loads per lane and a share of the device's workgroups per row; the row
-    // then takes several steps.
+    // B = ceil(vec_row / (256 U)) workgroups per row covers the row, with the workgroups of
+    // every row in one device wave. First with U <= 4 and B <= 65, so that the row's
+    // finalizing workgroup receives at most one published candidate per lane of one
+    // wavefront, which then polls and merges them alone; then with U <= 8 and B <= 256 (at
+    // most one candidate per thread of the finalizer: a second costs a second round trip).
+    // Measured per call on MI355X: [1,202048] fp32 3.58 us with B = 198, U = 1, against
+    // 3.24-3.28 with U = 2 or 4 (B = 99, 50) and 3.60 with U = 8; [8,202048] fp32 4.39 (U =
+    // 1), 4.24 (U = 4); [32,202048] fp16 5.26 (U = 2, B = 50), 5.80 (U = 8); [1,2^20] fp32
+    // 3.96 (U = 4, B = 256), 4.08 (U = 8). Failing both, 8 loads per lane and a share of the
+    // device's workgroups per row; the row then takes several steps.
     int64_t split_b = 0;
-    for (int64_t u = 1; u <= kMaxUnrollBlocks; u *= 2) {
-        const int64_t b = ceil_div(vec_row, kBlock * u);
-        if (b <= kBlock && b * rows1 <= cap_blocks) {
-            split_b = b;
-            break;
+    for (int tier = 0; tier < 2 && split_b == 0; ++tier) {
+        const int64_t max_b = tier == 0 ? kWave + 1 : kBlock;
+        const int64_t max_u = tier == 0 ? 4 : kMaxUnrollBlocks;
+        for (int64_t u = 1; u <= max_u; u *= 2) {
+            const int64_t b = ceil_div(vec_row, kBlock * u);
+            if (b <= max_b && b * rows1 <= cap_blocks) {
+                split_b = b;
+                break;
+            }
         }
     }
     if (split_b == 0) {

@@ -10,14 +10,14 @@ configuration of the workload set ([1,32000] fp32, [1,202048] fp32 ArgMax and Ar
 ArgMin, [65536,64] fp16), each at the same steps and warm-up. A step is one call of the
 library (every kernel it enqueues), on inputs already resident in HBM.
 
-Timing: W untimed warm-up calls, then exactly K calls between two HIP events on the stream
-the library launches on, synchronised on both sides; the inputs rotate through copies that
+Timing: ten trials of 200 calls (below), then W untimed warm-up calls, then exactly K calls
+between two HIP events on the stream the library launches on, synchronised on both sides; the inputs rotate through copies that
 together exceed the 256 MB Infinity Cache, so every call reads HBM ("hot" repeats one
 buffer and is reported beside it). The timed region divided by K is the per-call time
 (`value`); the roofline divides the algorithmic bytes by that per-call time. HIP events
 recorded around the main kernel of single calls (the library's measurement hook) give
-`kernel_event_us`, a cross-check that includes the events' own overhead. Ten further trials of 200 calls give the
-spread of the per-call figure (`trials_us_per_call`); `host_enqueue_us_per_call` is the host's
+`kernel_event_us`, a cross-check that includes the events' own overhead. The ten trials give
+the spread of the per-call figure (`trials_us_per_call`); `host_enqueue_us_per_call` is the host's
 time to enqueue one call, which at these sizes is close to the GPU's time per call (the host
 launch path, not only the kernel, sets the rate). The launch floor is an empty kernel
 launched the same way; the read floor (`read_floor`, read-only workloads) is a plain
@@ -319,13 +319,15 @@ def roofline(bytes_per_call: int, kernel_us: float, workload: str = "") -> dict:
 def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
     c = Case(w, op)
     log(f"[bench] {w.name} {op}: plan {c.plan}, {c.n_rot} rotated copies")
-    us = c.timed(steps, warmup, rotate=True)
+    # ten trials of 200 rotated calls, each continuing the rotation where the last one
+    # stopped (no copy is read again while it can still sit in the Infinity Cache): the
+    # spread of the per-call figure. They run first, so that the host's launch path is in
+    # its steady state when the W warm-up and K timed calls follow (a host core that has
+    # just been generating inputs enqueues the first few hundred calls up to twice as
+    # slowly, which at these sizes the GPU would wait for).
+    trials = sorted(c.timed(200, 0, rotate=True, start=200 * k) for k in range(10))
+    us = c.timed(steps, warmup, rotate=True, start=2000)
     host_us = c.host_us
-    # ten further trials of 200 rotated calls, each continuing the rotation where the last
-    # one stopped (no copy is read again while it can still sit in the Infinity Cache):
-    # the spread of the per-call figure
-    trials = sorted(c.timed(200, 0, rotate=True, start=warmup + steps + 200 * k)
-                    for k in range(10))
     hot = c.timed(steps, warmup // 4 + 1, rotate=False)
     kus = c.kernel_timed(min(steps, 1000))
     gus = c.graph_timed(min(steps, 200), max(1, steps // 200)) if graph else None

@@ -146,41 +146,68 @@ def test_plan_paths_for_the_measured_shapes(mi355x):
     assert B.argreduce_plan(4096, 8, B.F32)["lanes_per_row"] == 2
 
 
+def split_rule(rows, vec, cap_blocks):
+    """(B, U) of the split plan's rule, written out: the fewest U <= 4 with B =
+    ceil(vec / (256 U)) <= 65 and rows * B within a device wave; else the fewest U <= 8 with
+    B <= 256 and the same bound; else None (several steps)."""
+    for max_b, us in ((65, (1, 2, 4)), (256, (1, 2, 4, 8))):
+        for u in us:
+            b = -(-vec // (256 * u))
+            if b <= max_b and rows * b <= cap_blocks:
+                return b, u
+    return None
+
+
 def test_plan_keeps_every_lane_busy_and_one_device_wave(mi355x):
     """Split rows take the fewest 16-byte loads per lane (U) for which one step of
-    ceil(vectors / (256 U)) <= 256 workgroups per row covers the row with all rows'
-    workgroups in one device wave (so no workgroup is idle), else 8 loads per lane and
-    several steps."""
+    ceil(vectors / (256 U)) workgroups per row covers the row with all rows' workgroups in
+    one device wave (so no workgroup is idle): first at most 65 workgroups per row with
+    U <= 4 (one candidate per lane of the finalizer's first wavefront), then at most 256
+    with U <= 8; else 8 loads per lane and several steps."""
     cap_blocks = MI355X_THREADS // 256
+    seen = set()
     for rows, cols, dtype in [(1, 32000, B.F32), (1, 202048, B.F32), (8, 202048, B.F32),
                               (32, 202048, B.F16), (64, 202048, B.BF16), (1, 2 ** 24, B.F64),
                               (100, 50000, B.BF16), (300, 40000, B.F32), (256, 202048, B.F16),
-                              (1, 1 << 20, B.F32), (1, 1 << 21, B.F32)]:
+                              (1, 1 << 20, B.F32), (1, 1 << 21, B.F32), (1, 500000, B.F32),
+                              (8, 65536, B.F32), (32, 65536, B.F32)]:
         p = B.argreduce_plan(rows, cols, dtype)
         assert p["path"] == B.PATH_SPLIT, (rows, cols, p)
         esize = {B.F32: 4, B.F16: 2, B.BF16: 2, B.F64: 8}[dtype]
         vec = -(-cols * esize // 16)
         b, u = p["blocks_per_row"], p["unroll"]
         assert p["grid_blocks"] == rows * b <= cap_blocks and p["grid_rows"] == rows
-        fits = [uu for uu in (1, 2, 4, 8)
-                if -(-vec // (256 * uu)) <= 256 and rows * -(-vec // (256 * uu)) <= cap_blocks]
-        if fits:
-            assert u == fits[0] and b == -(-vec // (256 * u))  # one step, fewest loads
-            assert b * 256 * u >= vec > (b - 1) * 256 * u
+        want = split_rule(rows, vec, cap_blocks)
+        if want:
+            assert (b, u) == want, (rows, cols, p)
+            assert b * 256 * u >= vec > (b - 1) * 256 * u  # one step, no idle workgroup
+            seen.add("wave" if b <= 65 else "block")
         else:
             assert u == 8 and b == cap_blocks // 4 // rows  # several steps of 8 loads
+            seen.add("steps")
+    assert seen == {"wave", "block", "steps"}
+    assert (B.argreduce_plan(1, 202048, B.F32)["blocks_per_row"],
+            B.argreduce_plan(1, 202048, B.F32)["unroll"]) == (50, 4)
+    assert (B.argreduce_plan(32, 202048, B.F16)["blocks_per_row"],
+            B.argreduce_plan(32, 202048, B.F16)["unroll"]) == (50, 2)
 
 
 def test_split_is_bounded_by_capacity(lib):
-    """At an H200-sized capacity (1056 workgroups of 256 threads) [1, 202048] fp32 takes one
-    vector per lane (198 workgroups), and [32, 202048] fp32 needs 8 per lane for its 32 rows
-    to fit: 25 workgroups per row, 800 in all."""
+    """At an H200-sized capacity (1056 workgroups of 256 threads) [1, 202048] fp32 takes four
+    vectors per lane (50 workgroups), and [32, 202048] fp32 needs 8 per lane for its 32 rows
+    to fit: 25 workgroups per row, 800 in all. [8, 202048] fp32 takes 4 per lane at MI355X
+    capacity (400 workgroups) but 8 at an eight-times smaller one (256 workgroups)."""
     B.argreduce_debug_set_capacity(H200_THREADS)
     p = B.argreduce_plan(1, 202048, B.F32)
-    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 198 and p["unroll"] == 1
+    assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 50 and p["unroll"] == 4
     p = B.argreduce_plan(32, 202048, B.F32)
     assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] == 25 and p["unroll"] == 8
     assert p["grid_blocks"] == 800 <= H200_THREADS // 256
+    B.argreduce_debug_set_capacity(MI355X_THREADS)
+    assert B.argreduce_plan(8, 202048, B.F32)["unroll"] == 4
+    B.argreduce_debug_set_capacity(MI355X_THREADS // 8)
+    p = B.argreduce_plan(8, 202048, B.F32)
+    assert p["unroll"] == 8 and p["grid_blocks"] == 200
     p = B.argreduce_plan(512, 202048, B.F32)  # no one-step split fits: a quarter device wave
     assert p["path"] == B.PATH_BLOCK and p["unroll"] == 8
 
