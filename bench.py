@@ -29,7 +29,9 @@ rows split across the host's threads (at most 16), with the host's core count an
 
 `--pmc-pass` runs a fixed sequence for hardware-counter collection instead (a 256 MiB
 device copy, whose known bytes calibrate FETCH_SIZE / WRITE_SIZE, then 100 calls of each
-timed workload) and prints nothing on stdout.
+configuration and op, and of three more workloads) and prints nothing on stdout;
+`--traffic-summary`, `--counter-summary` and `--trace-summary` turn rocprofv3's CSV output
+of such runs into the committed summaries (no GPU).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -68,6 +70,17 @@ PAGES_US_1x202048 = 6.4  # ArgMax fp32 [1,202048] per call on the pages' H200
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes one call must move: the input read once and an int64 per output (and, for a
+    cumulative scan, a value per element)."""
+    if w.kind == "scan":
+        return 2 * w.nbytes + w.rows * w.cols * 8
+    if w.axis_shape is not None:
+        outer, _, inner = w.axis_shape
+        return w.nbytes + outer * inner * 8
+    return w.nbytes + w.rows * 8
 
 
 class Case:
@@ -122,8 +135,7 @@ class Case:
         self.scratch = torch.empty(max(self.need, 1), dtype=torch.uint8, device="cuda")
         self.binding = "cpython-fastcall" if B.fast() is not None else "ctypes"
         self._argv_cache = None
-        # input read once, one int64 per output (and, for a scan, one value per element)
-        self.bytes = w.nbytes + n_out * 8 + (w.nbytes if self.vals is not None else 0)
+        self.bytes = algorithmic_bytes(w)
 
     def argv(self, k: int) -> tuple:
         """The C call's arguments for rotated copy k (built once per copy and stream)."""
@@ -296,8 +308,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary (scaled by the
-    copy-kernel calibration), or None when absent or taken on other kernel sources."""
+    """HBM bytes per launch of ``workload`` ("name:op") from the committed FETCH_SIZE /
+    WRITE_SIZE summary (scaled by the copy-kernel calibration), or None when absent or taken
+    on other kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -353,7 +366,7 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
         # average time per launch, which rocprofv3's kernel trace of the same command agrees
         # with; events recorded around each single launch (kernel_event_us) carry their own
         # overhead and serve as a cross-check only.
-        "roofline": roofline(c.bytes, us, w.name if op == "max" else ""),
+        "roofline": roofline(c.bytes, us, f"{w.name}:{op}"),
     }
     log(f"[bench]   {json.dumps(rec)}")
     rec["_case"] = c
@@ -363,14 +376,29 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True) -> dict:
 COPY_BYTES = 256 << 20
 
 
+def pmc_workloads() -> list:
+    """(workload, op) of the counter pass, in launch order: every configuration of the
+    metric's workload set, each op, then the [64,4096,256] middle-axis ArgMax and the
+    [4096,4096] and [1,2^24] fp32 cummax workloads."""
+    from argmin_reduction_wide_amd import workloads as W
+
+    out = []
+    for name in W.CONFIG_NAMES:
+        for w in W.config_workloads(name):
+            out.extend((w, op) for op in w.ops)
+    out += [(W.axis_many_outputs_f32(), "max"), (W.scan_many_rows_f32(), "max"),
+            (W.scan_long_row_f32(), "max")]
+    return out
+
+
+PMC_CALLS = 100
+
+
 def pmc_pass() -> int:
     """Fixed kernel sequence for counter collection: a device-to-device copy of COPY_BYTES
-    (the calibration: it reads and writes exactly that many bytes), then 100 calls each of
-    the [1,202048] and [4096,4096] fp32 ArgMax workloads, the [64,4096,256] middle-axis
-    ArgMax and the [4096,4096] and [1,2^24] fp32 cummax workloads, on rotated inputs."""
+    (the calibration: it reads and writes exactly that many bytes), then PMC_CALLS calls of
+    each (workload, op) of pmc_workloads(), on rotated inputs."""
     import torch
-
-    from argmin_reduction_wide_amd import workloads as W
 
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -380,15 +408,145 @@ def pmc_pass() -> int:
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    for w in (W.c2_row202048_f32(), W.c4_square_f32_f64("f32"), W.axis_many_outputs_f32(),
-              W.scan_many_rows_f32(), W.scan_long_row_f32()):
-        c = Case(w, "max")
-        for i in range(100):
+    for w, op in pmc_workloads():
+        c = Case(w, op)
+        for i in range(PMC_CALLS):
             c.call(i)
         torch.cuda.synchronize()
-        log(f"[pmc] {w.name}: 100 calls, {c.bytes} algorithmic bytes per call, plan {c.plan}")
+        log(f"[pmc] {w.name} {op}: {PMC_CALLS} calls, {c.bytes} algorithmic bytes per call, "
+            f"plan {c.plan}")
         del c
         torch.cuda.empty_cache()
+    return 0
+
+
+def _csv_rows(directory: str, suffix: str) -> list:
+    import csv
+    import glob
+
+    paths = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not paths:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    rows = []
+    for path in paths:
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name: str) -> str:
+    """A kernel's name without its argument list (and the return type)."""
+    anon = "(anonymous namespace)"
+    name = name.replace(anon, "\0").split("(")[0].replace("\0", anon)
+    return name[5:] if name.startswith("void ") else name
+
+
+def _dispatch_values(directory: str, counter: str) -> list:
+    """[(kernel name, value)] of one counter in dispatch order (rocprofv3 --pmc CSV)."""
+    vals = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            key = int(r["Dispatch_Id"])
+            prev = vals.get(key)
+            vals[key] = (r["Kernel_Name"], float(r["Counter_Value"]) + (prev[1] if prev else 0.0))
+    if not vals:
+        raise ValueError(f"no {counter} values under {directory}")
+    return [vals[k] for k in sorted(vals)]
+
+
+def _per_workload(disp: list):
+    """Assigns the library's dispatches of a --pmc-pass run to pmc_workloads() in launch
+    order (PMC_CALLS calls each; a split middle-axis call has a second, merge dispatch) and
+    yields (workload, op, first kernel's name, that kernel's values)."""
+    lib = [(n, v) for n, v in disp if "argreduce::" in n]
+    pos = 0
+    for w, op in pmc_workloads():
+        first = lib[pos][0]
+        per_call = 2 if pos + 1 < len(lib) and "merge" in lib[pos + 1][0] else 1
+        vals = [v for n, v in lib[pos:pos + PMC_CALLS * per_call] if n == first]
+        assert len(vals) == PMC_CALLS, (w.name, op, first, len(vals))
+        pos += PMC_CALLS * per_call
+        yield w, op, first, vals
+
+
+def traffic_summary(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per dispatch from the rocprofv3 FETCH_SIZE and WRITE_SIZE passes over
+    --pmc-pass: the calibration copy's readings give the scale factors, and the library's
+    dispatches are assigned to pmc_workloads() in launch order. Writes the traffic file
+    bench.py reads (keyed by workload and op, tagged with the source hash) and prints a
+    markdown table."""
+    fetch = _dispatch_values(fetch_dir, "FETCH_SIZE")
+    write = _dispatch_values(write_dir, "WRITE_SIZE")
+    assert [n for n, _ in fetch] == [n for n, _ in write], "the two passes launched different kernels"
+    cal_f = next(v for n, v in fetch if "copyBuffer" in n)
+    cal_w = next(v for n, v in write if "copyBuffer" in n)
+    fetch_factor = COPY_BYTES / (cal_f * 1024.0)
+    write_factor = COPY_BYTES / (cal_w * 1024.0)
+    rec = {"source_hash": kernel_source_hash(), "fetch_factor": fetch_factor,
+           "write_factor": write_factor,
+           "calibration": f"device copy of {COPY_BYTES} bytes: FETCH_SIZE {cal_f} KiB, "
+                          f"WRITE_SIZE {cal_w} KiB", "kernels": {}}
+    lines = ["| kernel | workload | op | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | traffic bytes "
+             "| algorithmic bytes | traffic / algorithmic |",
+             "|---|---|---|---:|---:|---:|---:|---:|---:|"]
+    for (w, op, first, vf), (_, _, _, vw) in zip(_per_workload(fetch), _per_workload(write)):
+        fk, wk = sum(vf) / len(vf), sum(vw) / len(vw)
+        traffic = fk * 1024 * fetch_factor + wk * 1024 * write_factor
+        c_bytes = algorithmic_bytes(w)
+        rec["kernels"][f"{w.name}:{op}"] = {"kernel": first, "fetch_kib": fk, "write_kib": wk,
+                                           "traffic_bytes": traffic, "algorithmic_bytes": c_bytes}
+        lines.append(f"| `{_short(first)}` | {w.name} | {op} | {len(vf)} | {fk:.2f} | {wk:.2f} | "
+                     f"{traffic:,.0f} | {c_bytes:,} | {traffic / c_bytes:.4f} |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"Calibration: {rec['calibration']}; fetch factor {fetch_factor:.4f}, write factor "
+          f"{write_factor:.4f}. Source hash {rec['source_hash']}.\n")
+    print("\n".join(lines))
+    return 0
+
+
+def counter_summary(directories: list) -> int:
+    """Per-workload averages of every counter found in rocprofv3 --pmc runs of --pmc-pass
+    (one directory per run), as a markdown table."""
+    import csv  # noqa: F401
+
+    columns = []
+    for d in directories:
+        names = sorted({r["Counter_Name"] for r in _csv_rows(d, "counter_collection.csv")})
+        columns += [(d, n) for n in names]
+    tables = [list(_per_workload(_dispatch_values(d, n))) for d, n in columns]
+    print("| kernel | workload | op | dispatches | " + " | ".join(n for _, n in columns) + " |")
+    print("|---|---|---|---:|" + "---:|" * len(columns))
+    for rows in zip(*tables):
+        w, op, first, vals = rows[0]
+        avgs = " | ".join(f"{sum(r[3]) / len(r[3]):.2f}" for r in rows)
+        print(f"| `{_short(first)}` | {w.name} | {op} | {len(vals)} | {avgs} |")
+    return 0
+
+
+def trace_summary(directory: str) -> int:
+    """A markdown table of rocprofv3's kernel statistics (--kernel-trace --stats), with the
+    median duration per kernel when the per-dispatch trace is there too."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    medians = {}
+    try:
+        per = {}
+        for r in _csv_rows(directory, "kernel_trace.csv"):
+            per.setdefault(r["Kernel_Name"], []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        for name, d in per.items():
+            d.sort()
+            medians[name] = d[len(d) // 2] / 1e3
+    except FileNotFoundError:
+        pass
+    print("| kernel | calls | avg µs | median µs | min µs | max µs | % of GPU time |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for r in rows:
+        med = medians.get(r["Name"])
+        print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+              f"{'—' if med is None else f'{med:.3f}'} | {float(r['MinNs']) / 1e3:.3f} | "
+              f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f} |")
     return 0
 
 
@@ -507,7 +665,21 @@ def main() -> int:
                     help="also time the middle-axis, cumulative-scan and wide-row workloads")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run the counter-collection sequence (for rocprofv3 --pmc) and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise the rocprofv3 FETCH_SIZE / WRITE_SIZE passes over --pmc-pass "
+                         "(writes the traffic file, prints a table; no GPU)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="per-workload averages of the counters of rocprofv3 --pmc runs over "
+                         "--pmc-pass (no GPU)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print rocprofv3's kernel statistics under DIR as a table (no GPU)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
               "has no multi-GPU path (rows, or column slices of one wide row, would shard "
