@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_narrow(const uint8_t* __restr
 // each carries this call's nonce and the index is one a lane's scan can produce, at most
 // about spin_limit polls. The polls are unrolled four at a time with the bound checked once
 // per four: a loop that tested the bound and the words' validity on separate branches every
-// poll measured 0.1-0.15 us slower per call on split rows.
+// poll measured 0.1-0.15 us slower per call on split rows. One sleep unit (64 cycles)
+// between polls measured 0.03-0.05 us faster than two, and no faster than none.
 template <typename C, int OP>
 __device__ inline bool poll_candidate(const uint64_t* e, uint64_t tag, uint32_t cols,
                                       uint32_t spin_limit, C& v, uint32_t& idx) {
@@ -162,7 +163,7 @@ __device__ inline bool poll_candidate(const uint64_t* e, uint64_t tag, uint32_t 
                 Words<C>::unpack(pay, v, idx);
                 return true;
             }
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(1);
         }
         if (spins >= spin_limit) return false;
     }
@@ -175,8 +176,9 @@ __device__ inline void clear_candidate(uint64_t* e) {
         __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup per row; rows beyond the grid are looped over.
-template <typename Fmt, int OP, int U>
+// One workgroup per row; rows beyond the grid are looped over. ALIGNED: every row is
+// 16-byte aligned whole vectors, at most 256 * U of them (one step: scan_row_aligned).
+template <typename Fmt, int OP, int U, bool ALIGNED>
 __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restrict__ x,
                                                           int64_t rows,
                                                           int64_t* __restrict__ out,
@@ -185,8 +187,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
     const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         K c;
-        scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, threadIdx.x,
-                             kBlockThreads, c);
+        const uint8_t* row = x + static_cast<size_t>(r) * row_bytes;
+        if constexpr (ALIGNED)
+            scan_row_aligned<Fmt, OP, U>(row, cols / Fmt::VW, threadIdx.x, kBlockThreads, c);
+        else
+            scan_row<Fmt, OP, U>(row, cols, threadIdx.x, kBlockThreads, c);
         block_merge(c);
         if (threadIdx.x == 0) out[r] = K::result(c.i);
     }
@@ -195,14 +200,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
 // A row split over B > 1 workgroups: workgroup b of row r = blockIdx / B scans the row's
 // lanes b * 256 .. b * 256 + 255 of a team of B * 256 lanes (one row per team, every row's
 // team launched at once). Workgroups b < B - 1 publish their candidate; workgroup B - 1
-// finalizes the row.
+// finalizes the row. ALIGNED as for k_blocks (one step of B * 256 lanes).
 //
 // Eight waves per SIMD (at most 64 VGPRs): eight workgroups of 256 threads per CU, so a
 // grid of up to (CUs * 2048 / 256) workgroups, the most an automatic split plan launches,
 // is resident at once on an otherwise idle device, whatever the format and unroll. (A row
 // loop here cost registers: values the compiler hoisted out of it stayed live through the
 // scan and pushed the U = 8 instances past 64 VGPRs.)
-template <typename Fmt, int OP, int U>
+template <typename Fmt, int OP, int U, bool ALIGNED>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_split(const uint8_t* __restrict__ x, int64_t* __restrict__ out,
              uint64_t* __restrict__ slots, uint32_t cols, uint32_t B, uint32_t nonce,
@@ -214,8 +219,12 @@ void k_split(const uint8_t* __restrict__ x, int64_t* __restrict__ out,
     const uint32_t r = blockIdx.x / B;
     if (threadIdx.x == 0) s_timeout = 0;  // read after the barriers of the last merge
     K c;
-    scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * cols * Fmt::kSize, cols,
-                         b * kBlockThreads + threadIdx.x, B * kBlockThreads, c);
+    const uint8_t* row = x + static_cast<size_t>(r) * cols * Fmt::kSize;
+    if constexpr (ALIGNED)
+        scan_row_aligned<Fmt, OP, U>(row, cols / Fmt::VW, b * kBlockThreads + threadIdx.x,
+                                     B * kBlockThreads, c);
+    else
+        scan_row<Fmt, OP, U>(row, cols, b * kBlockThreads + threadIdx.x, B * kBlockThreads, c);
     block_merge(c);
     uint64_t* rs = slots + static_cast<size_t>(r) * B * Words<C>::kStride;
     const uint64_t tag = static_cast<uint64_t>(nonce) << 32;
@@ -714,15 +723,29 @@ void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows
                 cols, rows, out);
 }
 
+template <typename Fmt, int OP, int U, bool ALIGNED>
+void launch_blocks_a(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
+                     uint64_t* slots, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+    if (p.blocks_per_row > 1)
+        launch_scan(k_split<Fmt, OP, U, ALIGNED>, grid, s, x, out, slots, cols,
+                    static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
+    else
+        launch_scan(k_blocks<Fmt, OP, U, ALIGNED>, grid, s, x, rows, out, cols);
+}
+
+// The one-step aligned kernels when the rows are 16-byte aligned whole vectors that one step
+// of the team's lanes covers; the general scan otherwise.
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                    uint64_t* slots, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
-    if (p.blocks_per_row > 1)
-        launch_scan(k_split<Fmt, OP, U>, grid, s, x, out, slots, cols,
-                    static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
+    const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
+    const bool aligned = row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                         row_bytes / 16 <= static_cast<size_t>(p.blocks_per_row) * kBlockThreads * U;
+    if (aligned)
+        launch_blocks_a<Fmt, OP, U, true>(p, x, cols, rows, out, slots, s);
     else
-        launch_scan(k_blocks<Fmt, OP, U>, grid, s, x, rows, out, cols);
+        launch_blocks_a<Fmt, OP, U, false>(p, x, cols, rows, out, slots, s);
 }
 
 template <typename Fmt, int OP>

@@ -36,22 +36,22 @@ def blocks_per_cu(k: dict) -> int:
 
 
 def split_kernels(kernels, fmt: str, unroll: int) -> list[dict]:
-    """The k_split<fmt, op, unroll> instances, every op."""
-    pat = re.compile(rf"k_splitINS_\d+{fmt}ELi\dELi{unroll}EEE")
+    """The k_split<fmt, op, unroll, aligned> instances, every op, both scans."""
+    pat = re.compile(rf"k_splitINS_\d+{fmt}ELi\dELi{unroll}ELb[01]EEE")
     return [k for k in kernels if pat.search(k[".name"])]
 
 
 def test_every_format_op_and_unroll_of_the_split_kernel_is_present(kernels):
     for fmt in FMT.values():
         for u in (1, 2, 4, 8):
-            assert len(split_kernels(kernels, fmt, u)) == 4, (fmt, u)
+            assert len(split_kernels(kernels, fmt, u)) == 8, (fmt, u)
 
 
 def test_split_kernel_holds_a_full_cu(kernels):
     """Every k_split instance: at most 64 VGPRs (eight waves per SIMD), no private
     (spill) memory, LDS for eight workgroups per CU."""
     ks = [k for k in kernels if "k_split" in k[".name"]]
-    assert len(ks) == 4 * 4 * 4
+    assert len(ks) == 4 * 4 * 4 * 2
     for k in ks:
         assert k[".wavefront_size"] == 64
         assert K.waves_per_simd(k) == 8, (k[".name"], k[".vgpr_count"])
