@@ -141,6 +141,41 @@ def test_narrow_aligned_rows(oracle_lib, hooks, dtype):
             check(oracle_lib, arr, dtype, op, f"narrow row loop nvec={nvec} plan={p}")
 
 
+@pytest.mark.parametrize("path", [B.PATH_BLOCK, B.PATH_SPLIT])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_aligned_one_step_rows(oracle_lib, hooks, path, dtype):
+    """Rows of whole 16-byte vectors from a 16-byte aligned base that one step covers (the
+    aligned scan: every lane loads its U vectors once, lanes past the row masked, position 0
+    taken from the first lane's own first vector): rows that fill the B x 256 x U vectors
+    exactly and rows 1, 64 and 255 vectors short of that, with a NaN at position 0, a NaN in
+    the row's last vector, and the extreme value tied at the first and the last position.
+    Under a four-workgroup capacity the workgroup-per-row kernel loops over rows."""
+    rng = np.random.default_rng(1400 + DTYPES.index(dtype) + 10 * path)
+    v = VW[dtype]
+    nan = W.to_storage(np.array([np.nan]), dtype)[0]
+    B.argreduce_debug_force_path(path)
+    for cap in (0, 1024):
+        B.argreduce_debug_set_capacity(cap)
+        for full in (256, 512, 1024, 2048):
+            for short in (0, 1, 64, 255):
+                cols = (full - short) * v
+                rows = 9
+                p = B.argreduce_plan(rows, cols, dtype)
+                covered = p["blocks_per_row"] * 256 * p["unroll"]
+                if p["path"] != path or covered < full - short:
+                    continue
+                arr = W.random_rows(rng, rows, cols, dtype, "ties")
+                arr[1, 0] = nan
+                arr[2, -1] = nan
+                arr[3, max(cols - v - 1, 0)] = nan
+                arr[4, :] = arr[4, 0]
+                arr[5, 0] = arr[5, -1] = W.to_storage(np.array([np.inf]), dtype)[0]
+                arr[6, 0] = arr[6, -1] = W.to_storage(np.array([-np.inf]), dtype)[0]
+                for op in OPS:
+                    check(oracle_lib, arr, dtype, op,
+                          f"aligned one step cap={cap} vectors={full - short} plan={p}")
+
+
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
 def test_special_value_fuzz(oracle_lib, hooks, cap):
     """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal} under several capacities."""
