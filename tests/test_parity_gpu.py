@@ -315,12 +315,14 @@ def test_graph_capture_and_replay(oracle_lib):
 
 
 def test_axis_graph_capture_and_replay(oracle_lib):
-    """The middle-axis reduction captured into a HIP graph, split (two dispatches) and not,
-    replayed on new inputs with eager calls in between; every result matches the oracle."""
+    """The middle-axis reduction captured into a HIP graph, split (two dispatches; with
+    16-byte and with element loads) and not, replayed on new inputs with eager calls in
+    between; every result matches the oracle."""
     import torch
 
     rng = np.random.default_rng(32)
-    for outer, length, inner, dtype in [(1, 1 << 16, 32, "f32"), (256, 16, 256, "f16")]:
+    for outer, length, inner, dtype in [(1, 1 << 16, 32, "f32"), (1, 1 << 16, 33, "f32"),
+                                        (256, 16, 256, "f16")]:
         tdt = {"f32": torch.float32, "f16": torch.float16}[dtype]
         x = torch.empty((outer, length * inner), dtype=tdt, device="cuda")
         out = torch.empty(outer * inner, dtype=torch.int64, device="cuda")
@@ -448,6 +450,28 @@ def test_axis_forced_split_and_capacities(oracle_lib, hooks, path, cap):
             arr = W.random_rows(rng, outer * length, inner, dtype, "special").reshape(outer, length, inner)
             for op in OPS:
                 check_axis(oracle_lib, arr, dtype, op, f"axis forced={path} cap={cap}", dirty=True)
+
+
+# Split middle axes (B workgroups per tile, merged by the second dispatch) across its
+# shapes: B from 3 to 625 workgroups per tile against 4 to 256 outputs per tile (one to
+# eight partials per thread of the merge), every format, ragged last tiles.
+SPLIT_AXIS = [(1, 20000, 32, "f32"), (1, 300000, 8, "f32"), (1, 2000000, 4, "f32"),
+              (1, 600000, 8, "f64"), (1, 100000, 16, "bf16"), (2, 300000, 24, "f16"),
+              (1, 40000, 200, "bf16"), (1, 50000, 264, "f32"), (3, 20000, 136, "f64"),
+              (1, 8000, 1000, "f32"), (1, 3000, 520, "f32"), (1, 4096, 4096, "f32"),
+              (1, 96, 256, "f32")]
+
+
+@pytest.mark.parametrize("shape", SPLIT_AXIS, ids=lambda s: "x".join(map(str, s)))
+def test_axis_split_shapes(oracle_lib, shape):
+    outer, length, inner, dtype = shape
+    p = B.argreduce_axis_plan(outer, length, inner, dtype)
+    assert p["blocks_per_row"] > 2 and p["dispatches"] == 2, p
+    rng = np.random.default_rng(1500 + length % 1000 + inner)
+    for kind in ("ties", "special"):
+        arr = W.random_rows(rng, outer * length, inner, dtype, kind).reshape(outer, length, inner)
+        for op in OPS:
+            check_axis(oracle_lib, arr, dtype, op, f"axis split kind={kind}", dirty=True)
 
 
 def test_axis_torch_wrapper_dims(oracle_lib):
