@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libargreduce.so")
 F32, F16, BF16, F64, I32, I64 = 0, 1, 2, 3, 4, 5
 MAX, MIN, MAX_LAST, MIN_LAST = 0, 1, 2, 3
 PATH_AUTO, PATH_SUBWAVE, PATH_BLOCK, PATH_SPLIT, PATH_AXIS, PATH_SCAN, PATH_WIDE = -1, 0, 1, 2, 3, 4, 5
+PATH_THREAD = 6  # forced only: one lane per row (the serial "before" kernel)
 OK = 0
 ERRORS = {
     -1: "ARGREDUCE_ERR_INVALID_ARG",

@@ -204,6 +204,9 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         }
     } else if (path == ARGREDUCE_PATH_SUBWAVE) {
         group = next_pow2(vec_row) < 64 ? next_pow2(vec_row) : 64;
+    } else if (path == ARGREDUCE_PATH_THREAD) {
+        path = ARGREDUCE_PATH_SUBWAVE;  // a group of one lane, one load in flight
+        group = 1;
     } else if (path == ARGREDUCE_PATH_SPLIT) {
         blocks_per_row = split_b > 2 ? split_b : 2;
     }
@@ -499,7 +502,8 @@ ARGREDUCE_EXPORT int argreduce_debug_set_window(int64_t elements) {
 }
 
 ARGREDUCE_EXPORT int argreduce_debug_force_path(int path) {
-    if (path < ARGREDUCE_PATH_AUTO || (path > ARGREDUCE_PATH_SPLIT && path != ARGREDUCE_PATH_WIDE))
+    if (path < ARGREDUCE_PATH_AUTO ||
+        (path > ARGREDUCE_PATH_SPLIT && path != ARGREDUCE_PATH_WIDE && path != ARGREDUCE_PATH_THREAD))
         return ARGREDUCE_ERR_INVALID_ARG;
     argreduce::g_force_path.store(path, std::memory_order_relaxed);
     return ARGREDUCE_OK;

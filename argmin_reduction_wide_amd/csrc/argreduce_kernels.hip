@@ -754,10 +754,12 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
     const uint8_t* x = static_cast<const uint8_t*>(xv);
     const uint32_t c32 = static_cast<uint32_t>(cols);
     if (p.path == ARGREDUCE_PATH_SUBWAVE) {
-        // Rows of whole 16-byte vectors starting 16-byte aligned, at most 32 of them: the
-        // narrow kernel (one vector per lane, no head, tail or seed load).
+        // Rows of whole 16-byte vectors starting 16-byte aligned, at most one per lane of
+        // the group (at most 32): the narrow kernel (one vector per lane, no head, tail or
+        // seed load).
         const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
         if (p.lanes_per_row <= 32 && p.unroll == 1 && row_bytes % 16 == 0 &&
+            row_bytes / 16 <= static_cast<size_t>(p.lanes_per_row) &&
             reinterpret_cast<uintptr_t>(x) % 16 == 0) {
             const uint32_t nvec = static_cast<uint32_t>(row_bytes / 16);
             const dim3 grid(static_cast<uint32_t>(p.grid_blocks));

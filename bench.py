@@ -66,6 +66,11 @@ KERNEL_SOURCES = ("argmin_reduction_wide_amd/csrc/argreduce_kernels.hip",
                   "include/argreduce.h")
 ROTATE_BYTES = 1 << 29  # 512 MiB of rotated inputs, twice the Infinity Cache
 PAGES_US_1x202048 = 6.4  # ArgMax fp32 [1,202048] per call on the pages' H200
+# The pages' own before / after pairs for shapes and formats measured here (NVIDIA H200,
+# per call: "[CUDA] Parallelize ArgMax/ArgMin over wide last axes", Description / Results;
+# before = the serial thread-per-row kernel, after = the cooperative kernel): context only.
+PAGES_BEFORE_AFTER_US = {("argmax_f32_1x32000", "max"): (695.6, 5.9),
+                         ("argmax_argmin_f32_1x202048", "max"): (5056.5, 6.4)}
 
 
 def log(msg: str) -> None:
@@ -335,6 +340,31 @@ def roofline(bytes_per_call: int, kernel_us: float, workload: str = "") -> dict:
             "traffic": measured_traffic(workload)}
 
 
+def cooperative_off(c) -> dict:
+    """The same calls with the cooperative (split) path disabled: the pages compare their
+    kernel with the serial thread-per-row kernel from the same binary and data ("[CUDA]
+    Parallelize ArgMax/ArgMin over wide last axes", Verification log). Here the library's
+    path override runs one lane per row (one 16-byte load in flight: milliseconds per call,
+    so three timed calls) and one workgroup per row (200 calls), on the same rotated
+    inputs; both must return the automatic path's indices."""
+    B = c.B
+    c.call(0)
+    want = c.result().copy()
+    rec = {"source": "this library with the split path overridden, same inputs and harness"}
+    try:
+        for name, path, steps, warm in (("thread_per_row", B.PATH_THREAD, 3, 1),
+                                        ("block_per_row", B.PATH_BLOCK, 200, 20)):
+            B.argreduce_debug_force_path(path)
+            us = c.timed(steps, warm, rotate=True, start=4000)
+            c.call(0)
+            rec[name] = {"us_per_call": round(us, 3), "calls": steps,
+                         "same_indices": bool((c.result() == want).all())}
+            log(f"[bench]   split path off ({name}): {us:.3f} us per call")
+    finally:
+        B.argreduce_debug_force_path(B.PATH_AUTO)
+    return rec
+
+
 def measure(w, op: str, steps: int, warmup: int, graph: bool = True, case=None) -> dict:
     """One (workload, op) record; ``case`` reuses another op's rotated inputs of the same
     workload (a second 512 MiB allocation of the same data measured up to 0.35 us per call
@@ -378,6 +408,15 @@ def measure(w, op: str, steps: int, warmup: int, graph: bool = True, case=None) 
         # overhead and serve as a cross-check only.
         "roofline": roofline(c.bytes, us, f"{w.name}:{op}"),
     }
+    if c.plan["path"] == c.B.PATH_SPLIT:
+        off = cooperative_off(c)
+        for name in ("thread_per_row", "block_per_row"):
+            off[name]["speedup_of_split"] = round(off[name]["us_per_call"] / us, 1)
+        pages = PAGES_BEFORE_AFTER_US.get((w.name, op))
+        if pages is not None:
+            off["pages_h200"] = {"before_us": pages[0], "after_us": pages[1],
+                                 "speedup": round(pages[0] / pages[1], 1)}
+        rec["before"] = off
     log(f"[bench]   {json.dumps(rec)}")
     rec["_case"] = c
     return rec
@@ -798,6 +837,9 @@ def main() -> int:
         "hip_kernel_args": "device memory" if os.environ.get("HIP_FORCE_DEV_KERNARG") == "1"
                            else "host memory",
         "hot_us_per_call": prim["hot_us_per_call"],
+        # the same calls with the split path overridden (one lane per row: the pages'
+        # "before" kernel; one workgroup per row), same library and inputs
+        "before": prim.get("before"),
         "trials_us_per_call": prim["trials_us_per_call"],
         "graph_us_per_call": prim["graph_us_per_call"],
         "kernel_event_us": prim["kernel_event_us"],

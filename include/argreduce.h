@@ -166,8 +166,13 @@ typedef enum {
                                    workgroup, thread rows along the axis (argreduce_axis) */
     ARGREDUCE_PATH_SCAN = 4,    /* cumulative scan: a tile of a row per workgroup, tiles of
                                    a row chained by look-back (argreduce_scan_lastaxis) */
-    ARGREDUCE_PATH_WIDE = 5     /* rows wider than INT32_MAX: windows of <= 2^30 elements,
+    ARGREDUCE_PATH_WIDE = 5,    /* rows wider than INT32_MAX: windows of <= 2^30 elements,
                                    one workgroup each, merged by a second dispatch */
+    ARGREDUCE_PATH_THREAD = 6   /* forced only, never chosen: one lane scans each row alone,
+                                   the pages' serial thread-per-row kernel, for a "before"
+                                   timing from the same library ("[CUDA] Parallelize
+                                   ArgMax/ArgMin over wide last axes", Verification log);
+                                   its plan reads as ARGREDUCE_PATH_SUBWAVE with one lane */
 } argreduce_path_t;
 
 typedef struct {
@@ -200,7 +205,9 @@ int argreduce_debug_set_capacity(int64_t threads);
 /* Force one path (ARGREDUCE_PATH_AUTO restores the automatic choice). Process-wide.
  * A forced path keeps its own geometry rules; a forced SPLIT uses at least two workgroups
  * per row, however short the row; a forced WIDE cuts every row into windows (of the size
- * set below, else the automatic one). SUBWAVE, BLOCK, SPLIT and WIDE can be forced. */
+ * set below, else the automatic one). SUBWAVE, BLOCK, SPLIT, WIDE and THREAD can be
+ * forced (THREAD: 16-byte loads, one in flight per lane, so milliseconds per call on rows
+ * of 10^5 elements). */
 int argreduce_debug_force_path(int path);
 
 /* Window size of the WIDE path in elements, 1 .. 2^30 (0 = automatic). Process-wide. Lets

@@ -230,7 +230,14 @@ def test_forced_paths(mi355x):
     assert B.argreduce_debug_force_path(B.PATH_SUBWAVE) == 0
     p = B.argreduce_plan(1, 202048, B.F32)
     assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == 64
-    assert B.argreduce_debug_force_path(6) == -1 and B.argreduce_debug_force_path(B.PATH_AXIS) == -1
+    # one lane per row (the serial "before" kernel): a one-lane group, one load in flight,
+    # 256 rows per workgroup; never chosen without the override
+    assert B.argreduce_debug_force_path(B.PATH_THREAD) == 0
+    for rows, cols, dtype in [(1, 202048, B.F32), (32, 202048, B.F16), (700, 129, B.F64), (1, 1, B.F32)]:
+        p = B.argreduce_plan(rows, cols, dtype)
+        assert (p["path"], p["lanes_per_row"], p["unroll"], p["scratch_bytes"]) == (B.PATH_SUBWAVE, 1, 1, 0), p
+        assert p["grid_blocks"] == -(-rows // 256)
+    assert B.argreduce_debug_force_path(7) == -1 and B.argreduce_debug_force_path(B.PATH_AXIS) == -1
     assert B.argreduce_debug_set_capacity(-5) == -1
 
 

@@ -93,7 +93,7 @@ def test_axis_length_sweep(oracle_lib, dtype, op):
 FORCED_SHAPES = [(1, 1), (1, 5), (2, 17), (5, 300), (33, 1000), (3, 40000), (700, 129), (4, 70001)]
 
 
-@pytest.mark.parametrize("path", [B.PATH_SUBWAVE, B.PATH_BLOCK, B.PATH_SPLIT])
+@pytest.mark.parametrize("path", [B.PATH_SUBWAVE, B.PATH_BLOCK, B.PATH_SPLIT, B.PATH_THREAD])
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
 def test_forced_paths_ragged_misaligned(oracle_lib, hooks, path, cap):
     rng = np.random.default_rng(7 + path * 10 + cap % 97)
