@@ -14,6 +14,8 @@
 //              a tree within the group; here on the DPP crossbar).
 //   k_blocks   a workgroup of 256 threads per row; rows beyond the grid are looped over.
 //   k_split    B > 1 workgroups per row, every row's team launched at once.
+//              Both have an aligned variant for rows of 16-byte aligned whole vectors that
+//              one step of the team covers (scan_row_aligned: no head, tail or seed load).
 //   k_wide     rows wider than INT32_MAX: one workgroup per window of at most 2^30
 //              elements (32-bit positions inside it), k_wide_merge as a second dispatch.
 //
@@ -42,7 +44,7 @@
 // word equals this call's nonce in its upper half (and, for the index word, holds an
 // in-range index). Only finalizers wait, and only on lower-numbered workgroups, which wait
 // on nothing. The automatic plans launch at most one device wave of workgroups (CUs * 2048
-// threads / 256), and k_blocks is compiled for eight waves per SIMD, so on an otherwise idle
+// threads / 256), and k_split is compiled for eight waves per SIMD, so on an otherwise idle
 // device every workgroup is resident at once. Larger grids (forced plans), or a device
 // shared with other work, rely on each XCD starting the workgroups it is given in id order,
 // which makes every wait end by induction on the id. The poll is bounded all the same:
