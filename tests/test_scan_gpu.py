@@ -127,13 +127,28 @@ def test_scan_special_values_and_offsets(oracle_lib, dtype):
 
 
 def test_scan_long_rows_many_windows(oracle_lib):
-    """Rows of several hundred tiles: the look-back folds several 256-tile windows of
-    aggregates when the nearer tiles have not published their prefixes yet."""
+    """Rows of several hundred tiles: each tile folds the aggregates of the earlier groups of
+    64 tiles (published by each group's last tile) and of the earlier tiles of its own
+    group, ragged last groups and tiles included."""
     rng = np.random.default_rng(901)
     for dtype, cols in (("f32", 3 << 20), ("i64", 1 << 20), ("f16", 5 << 20), ("f32", 9 << 20)):
         arr = inputs(rng, 1, cols, dtype, "ties")
         for op in OPS:
             check_scan(oracle_lib, arr, dtype, op, "long row")
+
+
+def test_scan_rows_of_more_than_64_groups(oracle_lib):
+    """More than 64 groups of tiles in a row (int64: 4096 elements per tile, so 17100007
+    elements are 4175 tiles, 66 groups): the earlier groups' aggregates are folded in two
+    rounds of polls, and the row ends in a partial tile of a partial group (an odd length:
+    element loads; an even one: 16-byte loads)."""
+    rng = np.random.default_rng(903)
+    for dtype, cols in (("i64", 17100007), ("f64", 17100006)):
+        plan = B.argreduce_scan_plan(1, cols, dtype)
+        assert plan["blocks_per_row"] > 65 * 64, plan
+        arr = inputs(rng, 1, cols, dtype, "ties")
+        for op in OPS:
+            check_scan(oracle_lib, arr, dtype, op, f"more than 64 groups, {cols} elements")
 
 
 def test_scan_workloads_full_size(oracle_lib):
@@ -208,7 +223,8 @@ def test_scan_torch_wrapper(oracle_lib):
 
 def test_scan_bounded_look_back_gives_up_cleanly(oracle_lib):
     """The look-back's bounded wait with a one-poll limit: each index is the oracle's or -1
-    (a tile that gave up, and the tiles after it), every tile with -1 indices is all -1, and
+    (a tile that gave up, or one that needed the aggregate of a group whose last tile gave
+    up), every tile with -1 indices is all -1, and
     the device's timeout count goes up by exactly the number of such tiles; with the default
     limit restored the same scratch gives exact results and the count stays."""
     import torch
