@@ -371,11 +371,17 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
     // smallest tile that holds it whole (no look-back: a second tile costs a handoff). A
     // longer row takes U = 1 while it needs at most 64 such tiles and the grid stays within
     // two device waves of workgroups (more, smaller tiles: more loads in flight, the
-    // look-back still one round), else U = 2 under the same 64-tile bound, else U = 8 (the
-    // look-back's depth matters). Measured against U = 4 for every short row: [1,65536]
-    // int64 5.9 -> 5.35 us, fp32 6.0 -> 4.1, [64,1024] int64 4.0 -> 3.2, [1024,64] int64
-    // 4.4 -> 3.0, [4096,1024] fp32 15.5 -> 12.7, [4096,4096] fp32 48.9 -> 45.5 (U = 2, two
-    // tiles per row; U = 1 with four: 52.7).
+    // look-back still one round), else U = 2 under the same 64-tile bound. Measured against
+    // U = 4 for every short row: [1,65536] int64 5.9 -> 5.35 us, fp32 6.0 -> 4.1, [64,1024]
+    // int64 4.0 -> 3.2, [1024,64] int64 4.4 -> 3.0, [4096,1024] fp32 15.5 -> 12.7,
+    // [4096,4096] fp32 48.9 -> 45.5 (U = 2, two tiles per row; U = 1 with four: 52.7).
+    // Longer rows take the smallest of U = 2, 4, 8 whose grid is at most a quarter of a
+    // device wave of workgroups (one or two tiles per CU), else U = 8: fewer tiles leave CUs
+    // idle, and more than fit at once wait for one another. Measured, U = 8 / 4 / 2: [1,2^18]
+    // fp32 8.30 / 6.65 / 6.31 us; [1,2^20] 9.83 / 8.52 / 7.99; [1,2^21] 10.40 / 10.14 /
+    // 10.12; [1,2^22] 15.15 / 15.17 / 16.82; [1,2^24] 50.2 / 54.6 / -; [1,2^21] fp16 12.48 /
+    // 9.63 / 8.81; [1,2^20] int64 9.47 / 9.25 / 11.09; [1,2^22] int64 20.9 / 28.7 / -;
+    // [8,2^18] fp32 9.76 / 9.44 / 9.48. The rule is within 4% of the best on every one.
     const int64_t vec_elems = 16 / es;
     const int64_t cap_blocks = cap / kBlock > 0 ? cap / kBlock : 1;
     const auto tiles_of = [&](int64_t u) { return ceil_div(cols, kBlock * u * vec_elems); };
@@ -386,6 +392,10 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
         p->unroll = kScanUnrollTiny;
     else if (t2 <= 64)
         p->unroll = kScanUnrollShort;
+    else if (rows <= cap_blocks / kSplitFillDiv / t2)
+        p->unroll = kScanUnrollShort;
+    else if (rows <= cap_blocks / kSplitFillDiv / tiles_of(kScanUnrollMid))
+        p->unroll = kScanUnrollMid;
     else
         p->unroll = kScanUnrollLong;
     p->tile_elems = kBlock * p->unroll * (16 / es);

@@ -42,11 +42,12 @@ struct AxisPlan {
 };
 
 // Cumulative extremum with indices (cummax / cummin) along the last axis.
-// 16-byte chunks per lane per tile: 1 or 2 while a row needs at most 64 tiles of that size,
-// 8 for longer rows (bigger tiles: fewer tiles for the look-back to walk through). The
+// 16-byte chunks per lane per tile: 1 or 2 while a row needs at most 64 tiles of that size;
+// for longer rows 2, 4 or 8, the smallest whose grid fits a quarter of a device wave. The
 // choice between them is the scan plan's.
 constexpr int kScanUnrollTiny = 1;
 constexpr int kScanUnrollShort = 2;
+constexpr int kScanUnrollMid = 4;
 constexpr int kScanUnrollLong = 8;
 
 struct ScanPlan {

@@ -584,8 +584,13 @@ hipError_t launch_cum_op(const ScanPlan& p, const void* x, void* out_val, int64_
     uint8_t* vb = static_cast<uint8_t*>(out_val);
     const uint32_t cols = static_cast<uint32_t>(p.cols);
     const uint32_t T = static_cast<uint32_t>(p.tiles_per_row);
-    constexpr int UT = kScanUnrollTiny, US = kScanUnrollShort, UL = kScanUnrollLong;
-    if (p.unroll == UT && p.vecio)
+    constexpr int UT = kScanUnrollTiny, US = kScanUnrollShort, UM = kScanUnrollMid,
+                  UL = kScanUnrollLong;
+    if (p.unroll == UM && p.vecio)
+        launch_scan(k_cum<Fmt, OP, UM, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+    else if (p.unroll == UM)
+        launch_scan(k_cum<Fmt, OP, UM, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
+    else if (p.unroll == UT && p.vecio)
         launch_scan(k_cum<Fmt, OP, UT, true>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());
     else if (p.unroll == UT)
         launch_scan(k_cum<Fmt, OP, UT, false>, grid, s, xb, cols, T, vb, out_idx, states, nonce, spin_limit());

@@ -335,7 +335,8 @@ def test_other_entry_points_refuse_integers(lib):
 def test_scan_plans_and_scratch(mi355x):
     # tiles: 256 lanes x U chunks of 16 bytes. A row that fits one tile of U <= 2 takes the
     # smallest such tile; else U = 1 while a row needs <= 64 tiles and the grid stays within
-    # two device waves, else U = 2 within 64 tiles, else U = 8.
+    # two device waves, else U = 2 within 64 tiles; longer rows the smallest of U = 2, 4, 8
+    # whose grid is at most a quarter of a device wave (512 workgroups), else U = 8.
     p = B.argreduce_scan_plan(1, 65536, B.I64)  # 128 tiles of U = 1: U = 2
     assert p["path"] == B.PATH_SCAN and p["unroll"] == 2 and p["outputs_per_block"] == 1024
     assert p["blocks_per_row"] == 64 and p["grid_blocks"] == 64 and p["load_bytes"] == 16
@@ -354,10 +355,18 @@ def test_scan_plans_and_scratch(mi355x):
     p = B.argreduce_scan_plan(3, 8193, B.F16)
     assert p["unroll"] == 1 and p["outputs_per_block"] == 2048 and p["blocks_per_row"] == 5
     assert p["load_bytes"] == 2 and p["scratch_bytes"] == 15 + 3 * 5 * 2 * 2 * 8
-    p = B.argreduce_scan_plan(1, 64 * 4096 + 1, B.F32)
-    assert p["unroll"] == 8 and p["outputs_per_block"] == 8192 and p["blocks_per_row"] == 33
+    p = B.argreduce_scan_plan(1, 64 * 4096 + 1, B.F32)  # 129 tiles of U = 2
+    assert p["unroll"] == 2 and p["outputs_per_block"] == 2048 and p["blocks_per_row"] == 129
     assert B.argreduce_scan_plan(1, 64 * 2048, B.F32)["unroll"] == 2
-    assert B.argreduce_scan_plan(1, 64 * 2048 + 1, B.F32)["unroll"] == 8
+    assert B.argreduce_scan_plan(1, 64 * 2048 + 1, B.F32)["unroll"] == 2
+    for rows, cols, dtype, u in [(1, 1 << 20, B.F32, 2), (1, 512 * 2048 + 1, B.F32, 4),
+                                 (1, 1 << 21, B.F32, 4), (1, 1 << 22, B.F32, 8),
+                                 (8, 1 << 18, B.F32, 4), (4, 1 << 18, B.F32, 2),
+                                 (16, 1 << 18, B.F32, 8), (1, 1 << 21, B.F16, 2),
+                                 (1, 1 << 20, B.I64, 4), (1, 1 << 22, B.I64, 8)]:
+        p = B.argreduce_scan_plan(rows, cols, dtype)
+        assert p["unroll"] == u, (rows, cols, dtype, p)
+        assert u == 8 or p["grid_blocks"] <= 512
     assert B.argreduce_scan_plan(2, 1 << 24, B.F32)["blocks_per_row"] == 2048
     assert B.argreduce_scan_scratch_bytes(2, 0, B.F32) == B.SIZE_MAX
     assert B.argreduce_scan_scratch_bytes(2, 8, 9) == B.SIZE_MAX

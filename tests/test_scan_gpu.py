@@ -137,6 +137,24 @@ def test_scan_long_rows_many_windows(oracle_lib):
             check_scan(oracle_lib, arr, dtype, op, "long row")
 
 
+def test_scan_long_row_tile_sizes(oracle_lib):
+    """Rows longer than 64 short tiles take the smallest of U = 2, 4, 8 chunks per lane whose
+    grid fits a quarter of a device wave (on MI355X: U = 2 for [1,2^20] fp32 and [1,3*2^19]
+    fp16, U = 4 for [1,2^21] fp32 and [1,2^20 - 3] int64, U = 8 for [8,2^18 + 5] fp32 and
+    [1,2^21] fp64): rows of several groups of tiles, ragged last tiles, every op."""
+    rng = np.random.default_rng(905)
+    seen = set()
+    for dtype, rows, cols in [("f32", 1, 1 << 20), ("f16", 1, 3 << 19), ("f32", 1, 1 << 21),
+                              ("i64", 1, (1 << 20) - 3), ("f32", 8, (1 << 18) + 5),
+                              ("f64", 1, 1 << 21)]:
+        plan = B.argreduce_scan_plan(rows, cols, dtype)
+        seen.add(plan["unroll"])
+        arr = inputs(rng, rows, cols, dtype, "ties")
+        for op in OPS:
+            check_scan(oracle_lib, arr, dtype, op, f"long row U={plan['unroll']} plan={plan}")
+    assert {2, 4, 8} <= seen, seen
+
+
 def test_scan_rows_of_more_than_64_groups(oracle_lib):
     """More than 64 groups of tiles in a row (int64: 4096 elements per tile, so 17100007
     elements are 4175 tiles, 66 groups): the earlier groups' aggregates are folded in two
