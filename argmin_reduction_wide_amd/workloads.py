@@ -424,6 +424,29 @@ def special_alphabet(dtype: str) -> np.ndarray:
     return np.array([math.nan, -math.inf, -m, -1.0, -s, -0.0, 0.0, s, 1.0, m, math.inf])
 
 
+# Bit layout of each floating-point storage format's NaNs: (bits type, exponent field all
+# ones, payload bits below the quiet bit, sign bit). The quiet bit is the payload's top bit.
+NAN_LAYOUT = {"f16": (np.uint16, 0x7C00, 0x01FF, 0x8000),
+              "bf16": (np.uint16, 0x7F80, 0x003F, 0x8000),
+              "f32": (np.uint32, 0x7F800000, 0x003FFFFF, 0x80000000),
+              "f64": (np.uint64, 0x7FF0000000000000, 0x0007FFFFFFFFFFFF, 0x8000000000000000)}
+
+
+def random_bit_rows(rng: np.random.Generator, rows: int, cols: int, dtype: str) -> np.ndarray:
+    """A (rows, cols) storage array of uniformly random bit patterns (every class of the
+    format: subnormals, both zeros, quiet NaNs of any payload and sign), with about one
+    entry in eight, and element 0 of every fourth row, replaced by a signalling NaN (quiet
+    bit clear, a non-zero payload below it, either sign)."""
+    bt, expo, payload, sign = NAN_LAYOUT[dtype]
+    u = rng.integers(0, np.iinfo(bt).max, size=(rows, cols), dtype=bt, endpoint=True)
+    snan = (bt(expo) | rng.integers(1, payload, size=(rows, cols), dtype=bt, endpoint=True)
+            | (rng.integers(0, 2, size=(rows, cols), dtype=bt) * bt(sign)))
+    mask = rng.random((rows, cols)) < 0.125
+    mask[::4, 0] = True
+    u = np.where(mask, snan, u).astype(bt)
+    return np.ascontiguousarray(u if dtype == "bf16" else u.view(STORAGE[dtype]))
+
+
 def random_rows(rng: np.random.Generator, rows: int, cols: int, dtype: str, kind: str) -> np.ndarray:
     """A (rows, cols) storage array of one of several value kinds.
 
@@ -432,7 +455,10 @@ def random_rows(rng: np.random.Generator, rows: int, cols: int, dtype: str, kind
     special  iid draws from the special-value alphabet (NaN, +-inf, +-0, subnormals, ...)
     mixed    N(0,1) with ~1% of entries replaced by alphabet draws
     constant one N(0,1) draw per row, repeated
+    bits     uniformly random bit patterns with signalling NaNs planted (random_bit_rows)
     """
+    if kind == "bits":
+        return random_bit_rows(rng, rows, cols, dtype)
     if kind == "normal":
         v = rng.standard_normal((rows, cols))
     elif kind == "ties":

@@ -11,7 +11,10 @@ disagrees with something fixed from outside it:
 * the scan against the fixed cases the ONNX Runtime pages state (tests/golden);
 * the scan against numpy.argmax / numpy.argmin, which return the first occurrence of the
   extremum and agree with the definition on NaN-free rows (on reversed rows for the
-  last-index ops).
+  last-index ops);
+* the scan and the cumulative scan on arbitrary bit patterns with signalling NaNs planted,
+  against the closed form on numpy's decoding of the same bits (a signalling NaN compares
+  like any NaN), values passed through bit for bit.
 
 The closed form is derived as follows. If element 0 is NaN the scan never moves (every
 comparison with NaN is false), so the result is 0. Otherwise the running best is never
@@ -163,6 +166,50 @@ def pin_brute_force(o, dtype: str, op: str, max_len: int = 5) -> None:
                                f"{vals[bad[0]].tolist()} -> {got[bad[0]]}, want {want[bad[0]]}")
 
 
+# (bits type, exponent field all ones, payload bits below the quiet bit, sign bit) per format
+NAN_BITS = {"f16": (np.uint16, 0x7C00, 0x01FF, 0x8000), "bf16": (np.uint16, 0x7F80, 0x003F, 0x8000),
+            "f32": (np.uint32, 0x7F800000, 0x003FFFFF, 0x80000000),
+            "f64": (np.uint64, 0x7FF0000000000000, 0x0007FFFFFFFFFFFF, 0x8000000000000000)}
+FLOAT_NP = {"f16": np.float16, "f32": np.float32, "f64": np.float64}
+
+
+def raw_bit_rows(rng, dtype: str, rows: int, cols: int) -> np.ndarray:
+    """Storage array of uniformly random bit patterns in which every third entry, and
+    element 0 of every other row, is a signalling NaN (quiet bit clear, random non-zero
+    payload below it, random sign)."""
+    bt, expo, payload, sign = NAN_BITS[dtype]
+    u = rng.integers(0, np.iinfo(bt).max, size=(rows, cols), dtype=bt, endpoint=True)
+    snan = (bt(expo) | rng.integers(1, payload, size=(rows, cols), dtype=bt, endpoint=True)
+            | (rng.integers(0, 2, size=(rows, cols), dtype=bt) * bt(sign)))
+    pick = (np.arange(cols)[None, :] % 3 == 1) | ((np.arange(rows)[:, None] % 2 == 0)
+                                                   & (np.arange(cols)[None, :] == 0))
+    u = np.where(pick, snan, u).astype(bt)
+    quiet = bt(payload + 1)
+    assert (((u[pick] & bt(expo)) == bt(expo)) & ((u[pick] & quiet) == 0)).all()
+    return np.ascontiguousarray(u if dtype == "bf16" else u.view(FLOAT_NP[dtype]))
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 values of a storage array by numpy's own conversions; every NaN, signalling
+    or quiet, becomes a NaN, which is all the closed form asks of it."""
+    if dtype == "bf16":
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def pin_raw_bit_patterns(o, dtype: str, op: str) -> None:
+    """Arbitrary bit patterns with signalling NaNs planted (leading ones included): a
+    signalling NaN compares like any NaN (every comparison false), so the scan agrees with
+    the closed form on numpy's decoding of the same bits."""
+    rng = np.random.default_rng(71 + DTYPES.index(dtype) * 4 + OPS.index(op))
+    for rows, cols in ((64, 1), (64, 2), (200, 7), (50, 64), (8, 1001)):
+        x = raw_bit_rows(rng, dtype, rows, cols)
+        got = o.argreduce_lastaxis(x, dtype, op)
+        want = closed_form(decode(x, dtype), op)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, f"{dtype} {op} {rows}x{cols} raw bits: row {bad[0]} -> {got[bad[0]]}, want {want[bad[0]]}"
+
+
 def pin_fixed_cases(o, section: str = "cases") -> None:
     for case in golden_cases(section):
         for dtype in case["dtypes"]:
@@ -311,6 +358,21 @@ def cum_nan_free_rows(rng, dtype: str, rows: int, cols: int, kind: str) -> np.nd
                      "f64": np.float64}[dtype]).astype(np.float64)
 
 
+def pin_cum_raw_bit_patterns(o, dtype: str, op: str) -> None:
+    """Arbitrary bit patterns with signalling NaNs planted: every prefix's index is the
+    closed form's on numpy's decoding of the bits, and each value is the input element at
+    that index, bit for bit (a signalling NaN is passed through, not quieted)."""
+    rng = np.random.default_rng(81 + CUM_DTYPES.index(dtype) * 2 + CUM_OPS.index(op))
+    for rows, cols in ((64, 1), (40, 9), (6, 150)):
+        x = raw_bit_rows(rng, dtype, rows, cols)
+        want = prefix_indices(decode(x, dtype), dtype, op)
+        got_v, got_i = o.cumulative(x, dtype, op)
+        bad = np.argwhere(got_i != want)
+        assert bad.size == 0, f"{dtype} {op} raw bits: index differs at {tuple(bad[0])}"
+        assert np.array_equal(storage_bits(got_v), storage_bits(np.take_along_axis(x, want, axis=1))), \
+            f"{dtype} {op} raw bits: values"
+
+
 def pin_cum_numpy_accumulate(o, dtype: str, op: str) -> None:
     """NaN-free rows: the values are numpy's running maximum / minimum, and the index is
     the first position (within the prefix) holding that running value."""
@@ -418,6 +480,7 @@ def all_pins(o, fast: bool = False):
             pins.append((f"numpy_{dtype}_{op}",
                          lambda d=dtype, p=op: pin_numpy_first_occurrence(o, d, p)))
             pins.append((f"axis_{dtype}_{op}", lambda d=dtype, p=op: pin_axis(o, d, p)))
+            pins.append((f"bits_{dtype}_{op}", lambda d=dtype, p=op: pin_raw_bit_patterns(o, d, p)))
     pins += [("cum_fixed_cases", lambda: pin_cum_fixed_cases(o, "cases")),
              ("cum_readings", lambda: pin_cum_fixed_cases(o, "readings")),
              ("cum_page_examples", lambda: pin_cum_page_examples(o)),
@@ -428,4 +491,7 @@ def all_pins(o, fast: bool = False):
                          lambda d=dtype, p=op: pin_cum_brute_force(o, d, p, 3 if fast else 4)))
             pins.append((f"cum_numpy_{dtype}_{op}", lambda d=dtype, p=op: pin_cum_numpy_accumulate(o, d, p)))
             pins.append((f"cum_two_pass_{dtype}_{op}", lambda d=dtype, p=op: pin_cum_two_pass(o, d, p)))
+            if dtype not in INT_NP:
+                pins.append((f"cum_bits_{dtype}_{op}",
+                             lambda d=dtype, p=op: pin_cum_raw_bit_patterns(o, d, p)))
     return pins

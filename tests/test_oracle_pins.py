@@ -45,6 +45,12 @@ def test_middle_axis_against_closed_form(oracle_lib, dtype, op):
     P.pin_axis(oracle_lib, dtype, op)
 
 
+@pytest.mark.parametrize("dtype", P.DTYPES)
+@pytest.mark.parametrize("op", P.OPS)
+def test_raw_bit_patterns_with_signalling_nans(oracle_lib, dtype, op):
+    P.pin_raw_bit_patterns(oracle_lib, dtype, op)
+
+
 def test_rejects_empty_rows(oracle_lib):
     P.pin_rejects_empty_rows(oracle_lib)
 
@@ -73,6 +79,12 @@ def test_cumulative_brute_force_against_prefix_closed_form(oracle_lib, dtype, op
 @pytest.mark.parametrize("op", P.CUM_OPS)
 def test_cumulative_against_numpy_accumulate(oracle_lib, dtype, op):
     P.pin_cum_numpy_accumulate(oracle_lib, dtype, op)
+
+
+@pytest.mark.parametrize("dtype", [d for d in P.CUM_DTYPES if d not in P.INT_NP])
+@pytest.mark.parametrize("op", P.CUM_OPS)
+def test_cumulative_raw_bit_patterns_with_signalling_nans(oracle_lib, dtype, op):
+    P.pin_cum_raw_bit_patterns(oracle_lib, dtype, op)
 
 
 @pytest.mark.parametrize("dtype", P.CUM_DTYPES)

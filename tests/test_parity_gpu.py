@@ -85,7 +85,7 @@ def test_axis_length_sweep(oracle_lib, dtype, op):
         for rows in (1, 3, 300):
             if rows * cols > 8_000_000:
                 continue
-            for kind in ("normal", "ties", "constant", "mixed"):
+            for kind in ("normal", "ties", "constant", "mixed", "bits"):
                 arr = W.random_rows(rng, rows, cols, dtype, kind)
                 check(oracle_lib, arr, dtype, op, f"sweep cols={cols} rows={rows} kind={kind}")
 
@@ -122,7 +122,7 @@ def test_narrow_aligned_rows(oracle_lib, hooks, dtype):
     for nvec in (1, 2, 3, 4, 5, 7, 8, 9, 13, 16, 17, 24, 31, 32):
         cols = nvec * v
         for rows in (1, 7, 300):
-            for kind in ("special", "ties", "mixed"):
+            for kind in ("special", "ties", "mixed", "bits"):
                 arr = W.random_rows(rng, rows, cols, dtype, kind)
                 if kind == "special":
                     arr[::3, 0] = W.to_storage(np.array([np.nan]), dtype)[0]
@@ -178,14 +178,15 @@ def test_aligned_one_step_rows(oracle_lib, hooks, path, dtype):
 
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
 def test_special_value_fuzz(oracle_lib, hooks, cap):
-    """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal} under several capacities."""
+    """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal}, and raw bit patterns with
+    signalling NaNs planted, under several capacities."""
     rng = np.random.default_rng(1000 + cap % 1013)
     B.argreduce_debug_set_capacity(cap)
     for trial in range(40):
         dtype = DTYPES[trial % 4]
         rows = int(rng.integers(1, 200))
         cols = int(rng.choice([1, 2, 5, 31, 64, 100, 257, 1000, 5000, 33333]))
-        kind = "special" if trial % 2 == 0 else "mixed"
+        kind = ("special", "mixed", "bits")[trial % 3]
         arr = W.random_rows(rng, rows, cols, dtype, kind)
         for op in OPS:
             check(oracle_lib, arr, dtype, op, f"fuzz trial={trial} cap={cap} kind={kind}")
@@ -430,7 +431,7 @@ AXIS_SHAPES = [(1, 1, 2), (3, 7, 3), (2, 300, 5), (4, 33, 16), (2, 1000, 17), (5
 def test_axis_shapes_all_ops(oracle_lib, hooks, dtype):
     rng = np.random.default_rng(400 + DTYPES.index(dtype))
     for outer, length, inner in AXIS_SHAPES:
-        for kind in ("ties", "mixed"):
+        for kind in ("ties", "mixed", "bits"):
             arr = W.random_rows(rng, outer * length, inner, dtype, kind).reshape(outer, length, inner)
             for op in OPS:
                 # offset 1: a base that is not 16-byte aligned takes the element loads
@@ -468,7 +469,7 @@ def test_axis_split_shapes(oracle_lib, shape):
     p = B.argreduce_axis_plan(outer, length, inner, dtype)
     assert p["blocks_per_row"] > 2 and p["dispatches"] == 2, p
     rng = np.random.default_rng(1500 + length % 1000 + inner)
-    for kind in ("ties", "special"):
+    for kind in ("ties", "special", "bits"):
         arr = W.random_rows(rng, outer * length, inner, dtype, kind).reshape(outer, length, inner)
         for op in OPS:
             check_axis(oracle_lib, arr, dtype, op, f"axis split kind={kind}", dirty=True)
@@ -582,16 +583,20 @@ def test_concurrent_streams_and_host_threads(oracle_lib):
         assert B.argreduce_plan(r, c, d)["path"] == B.PATH_SPLIT
 
     def call(k, stream, reps):
+        # the outputs' fills and the scratch are made on the stream the library launches on,
+        # so that each fill is ordered before its call (a fill on another stream could land
+        # after the call's result) and freed scratch is reused only behind the calls
         r, c, d = cases[k]
         need = B.argreduce_scratch_bytes(r, c, d)
-        scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
         outs = []
-        for _ in range(reps):
-            out = torch.full((r,), -7, dtype=torch.int64, device="cuda")
-            rc = B.argreduce_lastaxis(xs[k].data_ptr(), d, r, c, "max", out.data_ptr(),
-                                      scratch.data_ptr(), need, stream.cuda_stream)
-            assert rc == 0
-            outs.append(out)
+        with torch.cuda.stream(stream):
+            scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+            for _ in range(reps):
+                out = torch.full((r,), -7, dtype=torch.int64, device="cuda")
+                rc = B.argreduce_lastaxis(xs[k].data_ptr(), d, r, c, "max", out.data_ptr(),
+                                          scratch.data_ptr(), need, stream.cuda_stream)
+                assert rc == 0
+                outs.append(out)
         return outs
 
     announce("two streams, interleaved split calls")
@@ -611,8 +616,7 @@ def test_concurrent_streams_and_host_threads(oracle_lib):
     def worker(k):
         try:
             s = torch.cuda.Stream()
-            with torch.cuda.stream(s):
-                results[k] = call(k, s, 10)
+            results[k] = call(k, s, 10)
             s.synchronize()
         except Exception as e:  # reported below
             errors.append(repr(e))

@@ -46,7 +46,7 @@ def inputs(rng, rows: int, cols: int, dtype: str, kind: str) -> np.ndarray:
     if dtype in INTS:
         return W.random_int_rows(rng, rows, cols, dtype, {"ties": "ties", "special": "full",
                                                           "mixed": "full", "constant": "constant",
-                                                          "normal": "full"}[kind])
+                                                          "normal": "full", "bits": "full"}[kind])
     return W.random_rows(rng, rows, cols, dtype, kind)
 
 
@@ -103,7 +103,7 @@ SHAPES = [(1, 1), (1, 7), (3, 5), (2, 100), (2, 511), (2, 513), (1, 1023), (1, 1
 def test_scan_shapes_all_ops(oracle_lib, dtype):
     rng = np.random.default_rng(700 + DTYPES.index(dtype))
     for rows, cols in SHAPES:
-        for kind in ("ties", "mixed"):
+        for kind in ("ties", "mixed", "bits"):
             arr = inputs(rng, rows, cols, dtype, kind)
             for op in OPS:
                 check_scan(oracle_lib, arr, dtype, op, f"shape kind={kind}")

@@ -38,7 +38,7 @@ def test_forced_windows_against_oracle(oracle_lib, window):
         shapes = shapes[:4]  # one workgroup per element: keep the grid small
     for dtype in DTYPES:
         for rows, cols in shapes:
-            for kind, offset in (("ties", 0), ("special", 1), ("mixed", 3)):
+            for kind, offset in (("ties", 0), ("special", 1), ("mixed", 3), ("bits", 2)):
                 arr = W.random_rows(rng, rows, cols, dtype, kind)
                 for op in OPS:
                     check(oracle_lib, arr, dtype, op,

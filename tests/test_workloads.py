@@ -81,3 +81,20 @@ def test_wide_workload_is_tiled():
     assert np.abs(w.data.astype(np.float32)).max() < 8.0
     assert w.planted["max"][0] == min(k for k, v in plants.items() if v == 8.0) > 2 ** 31
     assert w.planted["min"][0] == min(k for k, v in plants.items() if v == -8.0) == 5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16", "f64"])
+def test_bit_rows_plant_signalling_nans(dtype):
+    """The "bits" kind: storage-typed random bit patterns; about one entry in eight, and
+    element 0 of every fourth row, a signalling NaN (exponent all ones, quiet bit clear,
+    payload non-zero); the rest spans the other classes."""
+    a = W.random_rows(np.random.default_rng(5), 64, 33, dtype, "bits")
+    assert a.dtype == W.STORAGE[dtype] and a.shape == (64, 33) and a.flags.c_contiguous
+    bt, expo, payload, sign = W.NAN_LAYOUT[dtype]
+    b = a.view(bt)
+    nan = ((b & bt(expo)) == bt(expo)) & ((b & bt(2 * payload + 1)) != 0)
+    snan = nan & ((b & bt(payload + 1)) == 0)
+    assert snan[::4, 0].all()
+    assert 0.1 < snan.mean() < 0.2
+    assert (b[snan] & bt(sign)).any() and not (b[snan] & bt(sign)).all()
+    assert (~nan).sum() > 0.8 * a.size
