@@ -310,6 +310,20 @@ def _torch_dtype_code(t) -> int:
         raise ArgreduceError(-2, f"argreduce on {t.dtype}") from None
 
 
+def _check_buffer(b, name: str, device, dtype=None, numel=None) -> None:
+    """A caller-supplied output or scratch tensor: on the input's device and contiguous,
+    and, for an output, int64 with one element per result. The kernels write through its
+    address with no bounds of their own, so a mismatch is refused before anything runs."""
+    if not b.is_cuda or b.device != device:
+        raise ValueError(f"{name} must be on {device}; got {b.device}")
+    if not b.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and b.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}; got {b.dtype}")
+    if numel is not None and b.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements; got {b.numel()}")
+
+
 def _reduce(t, op: int, out=None, scratch=None, dim: int = -1):
     import math
 
@@ -328,9 +342,13 @@ def _reduce(t, op: int, out=None, scratch=None, dim: int = -1):
     inner = math.prod(t.shape[dim + 1:])
     if out is None:
         out = torch.empty(t.shape[:dim] + t.shape[dim + 1:], dtype=torch.int64, device=t.device)
+    else:
+        _check_buffer(out, "out", t.device, torch.int64, outer * inner)
     need = argreduce_axis_scratch_bytes(outer, length, inner, dtype)
     if need == SIZE_MAX:
         raise ArgreduceError(-1, f"argreduce_axis_scratch_bytes({outer}, {length}, {inner})")
+    if scratch is not None:
+        _check_buffer(scratch, "scratch", t.device)
     if need and (scratch is None or scratch.numel() * scratch.element_size() < need):
         scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
     sptr = scratch.data_ptr() if (need and scratch is not None) else 0
@@ -374,6 +392,8 @@ def _scan(t, op: int, dim: int, scratch=None):
     need = argreduce_scan_scratch_bytes(rows, cols, dtype)
     if need == SIZE_MAX:
         raise ArgreduceError(-1, f"argreduce_scan_scratch_bytes({rows}, {cols})")
+    if scratch is not None:
+        _check_buffer(scratch, "scratch", t.device)
     if need and (scratch is None or scratch.numel() * scratch.element_size() < need):
         scratch = torch.empty(need, dtype=torch.uint8, device=t.device)
     sptr = scratch.data_ptr() if need else 0

@@ -368,6 +368,24 @@ def test_torch_wrapper_shapes(oracle_lib):
     assert np.array_equal(got.reshape(-1).cpu().numpy(), oracle_lib.argreduce_lastaxis(arr, "f32", "min"))
     with pytest.raises(ValueError):
         ar.argmax(torch.zeros(4, 4))  # CPU tensors are refused, never computed on the host
+    # a caller's output must be an int64 CUDA tensor of one element per result, and
+    # scratch a CUDA tensor: anything else is refused before a kernel runs
+    good = torch.empty(6, dtype=torch.int64, device="cuda")
+    assert ar.argmax(t, out=good.view(2, 3)) is not None
+    assert np.array_equal(good.cpu().numpy(), oracle_lib.argreduce_lastaxis(arr, "f32", "max"))
+    for bad in (torch.empty(5, dtype=torch.int64, device="cuda"),
+                torch.empty(6, dtype=torch.int32, device="cuda"),
+                torch.empty(12, dtype=torch.int64, device="cuda")[::2],
+                torch.empty(6, dtype=torch.int64)):
+        sentinel = bad.clone()
+        with pytest.raises(ValueError):
+            ar.argmax(t, out=bad)
+        torch.cuda.synchronize()
+        assert torch.equal(bad.cpu(), sentinel.cpu())
+    with pytest.raises(ValueError):
+        ar.argmin(t, scratch=torch.empty(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ar.cummax(t, scratch=torch.empty(1 << 16, dtype=torch.uint8))
 
 
 def test_int32_max_wide_rows():
