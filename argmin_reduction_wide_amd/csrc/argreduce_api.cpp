@@ -297,7 +297,9 @@ int make_axis_plan(int64_t outer, int64_t len, int64_t inner, int dtype, uintptr
     p->tiles_per_o = ceil_div(inner, tile);
     p->tiles = outer * p->tiles_per_o;
     const int64_t tiles1 = p->tiles > 0 ? p->tiles : 1;
-    p->unroll = (p->vec && vw == 2) ? 4 : 8;
+    // positions per thread and step: the kernel's unroll (16-byte loads: 8, or 4 for 8-byte
+    // elements; element loads: 64 bytes per lane, 32 / 16 / 8 elements of 2 / 4 / 8 bytes)
+    p->unroll = p->vec ? (vw == 2 ? 4 : 8) : 64 / esize;
     // Split the axis over workgroups while the tiles leave a quarter of a device wave of
     // workgroups unfilled, but not beyond one step (unroll positions) per thread. Filling the
     // whole wave measured 2-22% slower (more partials, and the 100-register kernel runs only

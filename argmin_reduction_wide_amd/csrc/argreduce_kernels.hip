@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
                 else
                     seed = Fmt::load1(col);
             }
-            // step <= 1024 * 256 * 8, so base + step cannot wrap below len <= INT32_MAX
+            // step <= 1024 * 256 * 32 (B * TR * U), so base + step cannot wrap below
+            // len <= INT32_MAX
             const uint32_t full = len - len % step;
             for (uint32_t base = 0; base < full; base += step) scan(base, std::false_type{});
             if (full < len) scan(full, std::true_type{});
@@ -853,15 +854,20 @@ hipError_t launch_axis_fmt(const AxisPlan& p, const void* xv, int64_t* out, uint
                            hipStream_t s) {
     const uint8_t* x = static_cast<const uint8_t*>(xv);
     // 16-byte loads: U = 8 (4 for 8-byte elements, whose vectors need twice the registers
-    // per output); element loads: U = 8. Element loads have inner >= 2, so at least 2 lanes.
+    // per output). Element loads: 64 bytes in flight per lane, U = 32 / 16 / 8 for 2- / 4- /
+    // 8-byte elements; with U = 8 for every size, a lane of 2-byte elements had 16 bytes in
+    // flight and the calls ran 3.7-6.3 times longer ([1,100000,1100] fp16 327.7 -> 51.9 us,
+    // [256,2048,5] fp16 25.6 -> 5.2 us), 4-byte ones 16-32% longer. Element loads have
+    // inner >= 2, so at least 2 lanes.
     constexpr int UV = Fmt::VW == 2 ? 4 : 8;
+    constexpr int UE = Fmt::kSize == 2 ? 32 : (Fmt::kSize == 4 ? 16 : 8);
     switch (p.vec * 1000 + p.lanes) {
-        case 2: launch_axis_tl<Fmt, OP, 2, false, 8>(p, x, out, scratch16, s); break;
-        case 4: launch_axis_tl<Fmt, OP, 4, false, 8>(p, x, out, scratch16, s); break;
-        case 8: launch_axis_tl<Fmt, OP, 8, false, 8>(p, x, out, scratch16, s); break;
-        case 16: launch_axis_tl<Fmt, OP, 16, false, 8>(p, x, out, scratch16, s); break;
-        case 32: launch_axis_tl<Fmt, OP, 32, false, 8>(p, x, out, scratch16, s); break;
-        case 64: launch_axis_tl<Fmt, OP, 64, false, 8>(p, x, out, scratch16, s); break;
+        case 2: launch_axis_tl<Fmt, OP, 2, false, UE>(p, x, out, scratch16, s); break;
+        case 4: launch_axis_tl<Fmt, OP, 4, false, UE>(p, x, out, scratch16, s); break;
+        case 8: launch_axis_tl<Fmt, OP, 8, false, UE>(p, x, out, scratch16, s); break;
+        case 16: launch_axis_tl<Fmt, OP, 16, false, UE>(p, x, out, scratch16, s); break;
+        case 32: launch_axis_tl<Fmt, OP, 32, false, UE>(p, x, out, scratch16, s); break;
+        case 64: launch_axis_tl<Fmt, OP, 64, false, UE>(p, x, out, scratch16, s); break;
         case 1001: launch_axis_tl<Fmt, OP, 1, true, UV>(p, x, out, scratch16, s); break;
         case 1002: launch_axis_tl<Fmt, OP, 2, true, UV>(p, x, out, scratch16, s); break;
         case 1004: launch_axis_tl<Fmt, OP, 4, true, UV>(p, x, out, scratch16, s); break;

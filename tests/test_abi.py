@@ -279,6 +279,10 @@ def test_axis_plans(mi355x):
     }.items():
         p = B.argreduce_axis_plan(3, 100, inner, dtype)
         assert (p["outputs_per_block"], p["load_bytes"]) == (tile, load), (inner, dtype, p)
+        # positions per thread and step: 8 with 16-byte loads (4 for fp64); element loads keep
+        # 64 bytes in flight per lane
+        want_u = (4 if dtype == B.F64 else 8) if load == 16 else 64 // ESIZE[dtype]
+        assert p["unroll"] == want_u, (inner, dtype, p)
         lanes = tile // (16 // ESIZE[dtype] if load == 16 else 1)  # lanes along inner
         assert p["lanes_per_row"] == p["blocks_per_row"] * (256 // lanes)  # threads per output
 
