@@ -255,6 +255,20 @@ def axis_few_outputs_f32(seed: int = 8, outer: int = 1, length: int = 1 << 20,
     )
 
 
+def axis_element_loads_f16(seed: int = 15, outer: int = 4, length: int = 16384,
+                           inner: int = 1001) -> Workload:
+    """ArgMax fp16 over the middle axis of [4, 16384, 1001]: rows of 1001 halves (2002
+    bytes) are not whole 16-byte vectors, so every lane loads one element per position;
+    N(0,1) quantised to 16 levels."""
+    rng = np.random.default_rng(seed)
+    v = quantised_normal(rng, (outer, length * inner))
+    return Workload(
+        name=f"argmax_f16_axis1_{outer}x{length}x{inner}", dtype="f16", ops=("max",),
+        data=to_storage(v, "f16"), seed=seed, axis_shape=(outer, length, inner),
+        recipe="N(0,1) quantised to 16 levels, f16, reduced over the middle axis (element loads)",
+    )
+
+
 # ----------------------------------------------------------------------------------------
 # cummax / cummin workloads. The PaddlePaddle issue on the cummax/cummin kernel measures
 # [1, N] and [rows, 65536 / rows] int64 scans along the last axis (reproduction A, B), a
@@ -397,7 +411,7 @@ def config_workloads(which: str) -> list[Workload]:
     if which == "c5b":
         return [c5b_narrow_rows_f16()]
     if which == "axis":
-        return [axis_many_outputs_f32(), axis_few_outputs_f32()]
+        return [axis_many_outputs_f32(), axis_few_outputs_f32(), axis_element_loads_f16()]
     if which == "wide":
         return [wide_row_f16()]
     if which == "scan":

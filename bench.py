@@ -427,15 +427,16 @@ COPY_BYTES = 256 << 20
 
 def pmc_workloads() -> list:
     """(workload, op) of the counter pass, in launch order: every configuration of the
-    metric's workload set, each op, then the [64,4096,256] middle-axis ArgMax and the
-    [4096,4096] and [1,2^24] fp32 cummax workloads."""
+    metric's workload set, each op, then the [64,4096,256] fp32 and [4,16384,1001] fp16
+    middle-axis ArgMax and the [4096,4096] and [1,2^24] fp32 cummax workloads."""
     from argmin_reduction_wide_amd import workloads as W
 
     out = []
     for name in W.CONFIG_NAMES:
         for w in W.config_workloads(name):
             out.extend((w, op) for op in w.ops)
-    out += [(W.axis_many_outputs_f32(), "max"), (W.scan_many_rows_f32(), "max"),
+    out += [(W.axis_many_outputs_f32(), "max"), (W.axis_element_loads_f16(), "max"),
+            (W.scan_many_rows_f32(), "max"),
             (W.scan_long_row_f32(), "max")]
     return out
 

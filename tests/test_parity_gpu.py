@@ -515,7 +515,8 @@ def test_axis_torch_wrapper_dims(oracle_lib):
 
 
 def test_axis_workloads_full_size(oracle_lib):
-    """The two middle-axis bench workloads at full size, every output against the oracle."""
+    """The middle-axis bench workloads at full size (16-byte and element loads), every
+    output against the oracle."""
     for w in W.config_workloads("axis"):
         outer, length, inner = w.axis_shape
         arr = w.data.reshape(outer, length, inner)

@@ -63,13 +63,16 @@ def test_planted_counts():
 
 def test_axis_workloads_shapes(oracle_lib):
     ws = W.config_workloads("axis")
-    assert [w.axis_shape for w in ws] == [(64, 4096, 256), (1, 1 << 20, 32)]
+    assert [w.axis_shape for w in ws] == [(64, 4096, 256), (1, 1 << 20, 32), (4, 16384, 1001)]
+    assert [w.dtype for w in ws] == ["f32", "f32", "f16"]
     for w in ws:
         outer, length, inner = w.axis_shape
-        assert w.data.shape == (outer, length * inner) and w.data.dtype == np.float32
-        got = oracle_lib.argreduce_axis(w.data.reshape(outer, length, inner), "f32", "max")
+        assert w.data.shape == (outer, length * inner) and w.data.dtype == W.STORAGE[w.dtype]
+        got = oracle_lib.argreduce_axis(w.data.reshape(outer, length, inner), w.dtype, "max")
         want = np.argmax(w.data.reshape(outer, length, inner), axis=1)  # NaN-free: first occurrence
         assert np.array_equal(got, want)
+    # the fp16 rows are not whole 16-byte vectors: the element-load path
+    assert (ws[2].axis_shape[2] * 2) % 16 != 0
 
 
 def test_wide_workload_is_tiled():
