@@ -227,10 +227,19 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         }
         const int64_t rows_per_block = kBlock / group;
         const int64_t need = ceil_div(rows1, rows_per_block);
+        // Groups narrower than a wavefront on rows of whole 16-byte vectors: at most one
+        // device wave of workgroups, each group looping over rows. A workgroup per 256 / G
+        // rows measured 10-22% slower wherever that exceeded the wave (the dispatch of the
+        // extra workgroups): [65536,100] fp32 8.16 -> 6.76 us, [200000,40] fp32 10.57 ->
+        // 8.24, [65536,96] fp16 5.50 -> 4.67, [131072,24] fp64 8.30 -> 6.88. Rows that are not
+        // whole vectors (the generic lane-group kernel, head and tail loads) gained nothing
+        // (bf16 [65536,250] 12.35 us, 12.97 capped) and keep a group per row.
+        const bool whole = (cols * elem_size(dtype)) % 16 == 0;
+        const int64_t grid_cap = (group < 64 && whole) ? cap_blocks : max_grid;
         p->lanes_per_row = static_cast<int>(group);
         p->blocks_per_row = 1;
         p->unroll = static_cast<int>(unroll);
-        p->grid_blocks = need < max_grid ? need : max_grid;
+        p->grid_blocks = need < grid_cap ? need : grid_cap;
         p->grid_rows = p->grid_blocks * rows_per_block;
     } else {
         int64_t unroll = next_pow2(ceil_div(vec_row, blocks_per_row * kBlock));

@@ -212,6 +212,21 @@ def test_split_is_bounded_by_capacity(lib):
     assert p["path"] == B.PATH_BLOCK and p["unroll"] == 8
 
 
+def test_narrow_groups_take_at_most_one_device_wave(mi355x):
+    """Groups narrower than a wavefront on rows of whole 16-byte vectors launch at most one
+    device wave of workgroups (2048 on MI355X) and loop over rows; rows that are not whole
+    vectors, and a wavefront per row, keep a workgroup per 256 / G rows."""
+    cases = [((65536, 100, B.F32), 32, 2048), ((200000, 40, B.F32), 16, 2048),
+             ((65536, 64, B.F16), 8, 2048), ((1 << 21, 4, B.F32), 1, 2048),
+             ((40000, 64, B.F16), 8, 1250), ((65536, 250, B.BF16), 32, 8192),
+             ((300000, 10, B.F32), 4, 4688), ((65536, 1024, B.F32), 64, 16384)]
+    for (rows, cols, dtype), lanes, grid in cases:
+        p = B.argreduce_plan(rows, cols, dtype)
+        assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == lanes, (rows, cols, p)
+        assert p["grid_blocks"] == grid, (rows, cols, p)
+        assert p["grid_rows"] == grid * (256 // lanes)
+
+
 def test_small_capacity_forces_row_loops(lib):
     B.argreduce_debug_set_capacity(1024)  # four workgroups; grids hold 64 device-fulls
     p = B.argreduce_plan(1000, 100000, B.F32)
