@@ -624,4 +624,92 @@ __device__ inline void scan_row_aligned(const uint8_t* __restrict__ row, uint32_
     }
 }
 
+// One step over a row at any element-aligned address whose 16-byte vectors, from the one
+// holding the row's first byte to the one holding its last, number nv <= team * U: lane
+// `lane` of a team of `team` lanes loads vectors lane, lane + team, ..., all U at once, with
+// no head, tail, seed load or step loop. Every vector is read whole from its 16-byte aligned
+// address: the bytes of it outside the row lie in the same aligned 16 bytes, so the same
+// page, as a byte of the row. The lanes holding the row's first and last vector (a branch
+// no other lane takes) turn the elements outside the row into NaN, and a lane past the span
+// re-reads the last vector and turns it into all-ones bits (a NaN in every format); a NaN is
+// never taken. Position 0 enters as its own candidate (fix(x0), 0) from lane 0's first
+// vector. Same results as scan_row; it saves scan_row's element loads of the head and tail
+// and its seed load. The split kernel takes it for rows that scan_row_aligned does not
+// cover (a start off 16 bytes or a partial last vector): measured per call against
+// scan_row, [64,32001] fp32 5.19 -> 4.48 us, [1,32001] fp32 3.23 -> 3.01, [1,50257] fp32
+// 3.05 -> 2.90, [32,202047] fp16 5.50 -> 5.27. On aligned whole-vector rows its edge tests
+// cost 2-7% against scan_row_aligned, and with one workgroup per row ([4096,4097] fp32,
+// [300,4099] bf16) it was 5-8% slower than scan_row.
+template <typename Fmt, int OP, int U>
+__device__ inline void scan_row_span(const uint8_t* __restrict__ row, uint32_t cols,
+                                        uint32_t lane, uint32_t team, Cand<typename Fmt::C, OP>& c) {
+    using C = typename Fmt::C;
+    using Vec = typename Fmt::Vec;
+    using K = Cand<C, OP>;
+    constexpr int VW = Fmt::VW;
+    static_assert(U * VW <= 64, "step slots must be inline constants");
+    constexpr uint32_t kNoSlot = 0xffffffffu;
+    // at most 32 elements per lane: with 64 (2-byte formats, U = 8) the edge handling does
+    // not fit the split kernel's 64 registers
+    static_assert(U * VW <= 32, "edge handling needs registers");
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
+    const uint8_t* base = row - mis;           // 16-byte aligned
+    const uint32_t lead = mis / Fmt::kSize;    // elements of vector 0 before the row
+    const uint32_t span = lead + cols;         // elements from `base` to the row's end
+    const uint32_t nv = (span + VW - 1) / VW;  // vectors (span <= INT32_MAX + 7: no wrap)
+    Vec q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t d = lane + static_cast<uint32_t>(u) * team;
+        q[u] = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(base) + (d < nv ? d : nv - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    C lv = K::identity();
+    uint32_t ls = kNoSlot;
+    C x0 = lv;  // position 0 (lane 0, vector 0, element `lead`)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t d = lane + static_cast<uint32_t>(u) * team;
+        const bool past = d >= nv;
+        u32x4 w = __builtin_bit_cast(u32x4, q[u]);
+        w.x = past ? 0xffffffffu : w.x;
+        w.y = past ? 0xffffffffu : w.y;
+        w.z = past ? 0xffffffffu : w.z;
+        w.w = past ? 0xffffffffu : w.w;
+        C e[VW];
+        Fmt::unpack(__builtin_bit_cast(Vec, w), e);
+        if (u == 0) {
+            x0 = e[0];
+#pragma unroll
+            for (int k = 1; k < VW; ++k) x0 = (static_cast<uint32_t>(k) == lead) ? e[k] : x0;
+        }
+        // the first vector's elements before the row, the last one's after it
+        const uint32_t lo = d == 0 ? lead : 0u;
+        const uint32_t hi = d + 1 == nv ? span - d * VW : static_cast<uint32_t>(VW);
+        if ((lo != 0) | (hi < static_cast<uint32_t>(VW))) {
+#pragma unroll
+            for (int k = 0; k < VW; ++k) {
+                const uint32_t kk = static_cast<uint32_t>(k);
+                e[k] = (kk >= lo && kk < hi) ? e[k] : static_cast<C>(__builtin_nan(""));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+            const uint32_t slot = static_cast<uint32_t>(u * VW + k);
+            const bool t = K::kLast ? (K::better(e[k], lv) | (e[k] == lv)) : K::better(e[k], lv);
+            lv = t ? e[k] : lv;
+            ls = t ? slot : ls;
+        }
+    }
+    constexpr uint32_t kShift = VW == 8 ? 3 : (VW == 4 ? 2 : 1);
+    c.init();
+    c.merge(lv, ls == kNoSlot ? K::kNone
+                              : (lane + (ls >> kShift) * team) * VW + (ls & (VW - 1)) - lead);
+    if (lane == 0) {
+        K f;
+        f.take_first(x0);
+        c.merge(f.v, f.i);
+    }
+}
+
 }  // namespace argreduce

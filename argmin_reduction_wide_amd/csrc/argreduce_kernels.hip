@@ -15,7 +15,9 @@
 //   k_blocks   a workgroup of 256 threads per row; rows beyond the grid are looped over.
 //   k_split    B > 1 workgroups per row, every row's team launched at once.
 //              Both have an aligned variant for rows of 16-byte aligned whole vectors that
-//              one step of the team covers (scan_row_aligned: no head, tail or seed load).
+//              one step of the team covers (scan_row_aligned: no head, tail or seed load);
+//              k_split also a span variant for other rows one step covers (scan_row_span:
+//              aligned vector loads, the elements outside the row masked).
 //   k_wide     rows wider than INT32_MAX: one workgroup per window of at most 2^30
 //              elements (32-bit positions inside it), k_wide_merge as a second dispatch.
 //
@@ -202,14 +204,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
 // A row split over B > 1 workgroups: workgroup b of row r = blockIdx / B scans the row's
 // lanes b * 256 .. b * 256 + 255 of a team of B * 256 lanes (one row per team, every row's
 // team launched at once). Workgroups b < B - 1 publish their candidate; workgroup B - 1
-// finalizes the row. ALIGNED as for k_blocks (one step of B * 256 lanes).
+// finalizes the row. MODE: 0 the general scan (scan_row); 1 as ALIGNED for k_blocks (one
+// step of B * 256 lanes); 2 rows whose 16-byte vectors, counted from the one holding the
+// row's first byte, one step covers (scan_row_span; at most 32 elements per lane).
 //
 // Eight waves per SIMD (at most 64 VGPRs): eight workgroups of 256 threads per CU, so a
 // grid of up to (CUs * 2048 / 256) workgroups, the most an automatic split plan launches,
 // is resident at once on an otherwise idle device, whatever the format and unroll. (A row
 // loop here cost registers: values the compiler hoisted out of it stayed live through the
 // scan and pushed the U = 8 instances past 64 VGPRs.)
-template <typename Fmt, int OP, int U, bool ALIGNED>
+template <typename Fmt, int OP, int U, int MODE>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_split(const uint8_t* __restrict__ x, int64_t* __restrict__ out,
              uint64_t* __restrict__ slots, uint32_t cols, uint32_t B, uint32_t nonce,
@@ -222,9 +226,11 @@ void k_split(const uint8_t* __restrict__ x, int64_t* __restrict__ out,
     if (threadIdx.x == 0) s_timeout = 0;  // read after the barriers of the last merge
     K c;
     const uint8_t* row = x + static_cast<size_t>(r) * cols * Fmt::kSize;
-    if constexpr (ALIGNED)
+    if constexpr (MODE == 1)
         scan_row_aligned<Fmt, OP, U>(row, cols / Fmt::VW, b * kBlockThreads + threadIdx.x,
                                      B * kBlockThreads, c);
+    else if constexpr (MODE == 2)
+        scan_row_span<Fmt, OP, U>(row, cols, b * kBlockThreads + threadIdx.x, B * kBlockThreads, c);
     else
         scan_row<Fmt, OP, U>(row, cols, b * kBlockThreads + threadIdx.x, B * kBlockThreads, c);
     block_merge(c);
@@ -726,29 +732,47 @@ void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows
                 cols, rows, out);
 }
 
-template <typename Fmt, int OP, int U, bool ALIGNED>
-void launch_blocks_a(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
-                     uint64_t* slots, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
-    if (p.blocks_per_row > 1)
-        launch_scan(k_split<Fmt, OP, U, ALIGNED>, grid, s, x, out, slots, cols,
-                    static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
-    else
-        launch_scan(k_blocks<Fmt, OP, U, ALIGNED>, grid, s, x, rows, out, cols);
+template <typename Fmt, int OP, int U, int MODE>
+void launch_split(const Plan& p, const uint8_t* x, uint32_t cols, int64_t* out, uint64_t* slots,
+                  hipStream_t s) {
+    launch_scan(k_split<Fmt, OP, U, MODE>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x, out,
+                slots, cols, static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
 }
 
 // The one-step aligned kernels when the rows are 16-byte aligned whole vectors that one step
-// of the team's lanes covers; the general scan otherwise.
+// of the team's lanes covers. Otherwise a split row takes the span scan when one step covers
+// every row's vectors and a lane holds at most 32 elements, and every other row the general
+// scan. Row r starts at byte x + r * row_bytes, 16-byte misaligned by (x + r * row_bytes)
+// mod 16: at most 16 - g + (x mod g) over the rows, where g is the largest power of two (at
+// most 16) dividing row_bytes, and exactly x mod 16 when there is one row.
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                    uint64_t* slots, hipStream_t s) {
-    const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
-    const bool aligned = row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-                         row_bytes / 16 <= static_cast<size_t>(p.blocks_per_row) * kBlockThreads * U;
-    if (aligned)
-        launch_blocks_a<Fmt, OP, U, true>(p, x, cols, rows, out, slots, s);
-    else
-        launch_blocks_a<Fmt, OP, U, false>(p, x, cols, rows, out, slots, s);
+    const uint64_t row_bytes = static_cast<uint64_t>(cols) * Fmt::kSize;
+    const uint64_t xm = reinterpret_cast<uintptr_t>(x) & 15u;
+    const uint64_t step = static_cast<uint64_t>(p.blocks_per_row) * kBlockThreads * U;
+    const bool aligned = row_bytes % 16 == 0 && xm == 0 && row_bytes / 16 <= step;
+    if (p.blocks_per_row <= 1) {
+        const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+        if (aligned)
+            launch_scan(k_blocks<Fmt, OP, U, true>, grid, s, x, rows, out, cols);
+        else
+            launch_scan(k_blocks<Fmt, OP, U, false>, grid, s, x, rows, out, cols);
+        return;
+    }
+    if (aligned) {
+        launch_split<Fmt, OP, U, 1>(p, x, cols, out, slots, s);
+        return;
+    }
+    if constexpr (U * Fmt::VW <= 32) {
+        const uint64_t g = row_bytes % 16 == 0 ? 16 : (row_bytes & (~row_bytes + 1));
+        const uint64_t mis = (rows <= 1 || g == 16) ? xm : 16 - g + (xm & (g - 1));
+        if ((mis + row_bytes + 15) / 16 <= step) {
+            launch_split<Fmt, OP, U, 2>(p, x, cols, out, slots, s);
+            return;
+        }
+    }
+    launch_split<Fmt, OP, U, 0>(p, x, cols, out, slots, s);
 }
 
 template <typename Fmt, int OP>

@@ -35,23 +35,32 @@ def blocks_per_cu(k: dict) -> int:
     return min(K.waves_per_simd(k), by_lds, THREADS_PER_CU // BLOCK)
 
 
+VW = {"F32": 4, "F16": 8, "BF16": 8, "F64": 2}
+
+
 def split_kernels(kernels, fmt: str, unroll: int) -> list[dict]:
-    """The k_split<fmt, op, unroll, aligned> instances, every op, both scans."""
-    pat = re.compile(rf"k_splitINS_\d+{fmt}ELi\dELi{unroll}ELb[01]EEE")
+    """The k_split<fmt, op, unroll, mode> instances, every op and scan mode (general,
+    aligned, span)."""
+    pat = re.compile(rf"k_splitINS_\d+{fmt}ELi\dELi{unroll}ELi[012]EEE")
     return [k for k in kernels if pat.search(k[".name"])]
+
+
+def split_modes(fmt: str, unroll: int) -> int:
+    """Scan modes built per op: the span scan only where a lane holds at most 32 elements."""
+    return 3 if unroll * VW[fmt] <= 32 else 2
 
 
 def test_every_format_op_and_unroll_of_the_split_kernel_is_present(kernels):
     for fmt in FMT.values():
         for u in (1, 2, 4, 8):
-            assert len(split_kernels(kernels, fmt, u)) == 8, (fmt, u)
+            assert len(split_kernels(kernels, fmt, u)) == 4 * split_modes(fmt, u), (fmt, u)
 
 
 def test_split_kernel_holds_a_full_cu(kernels):
     """Every k_split instance: at most 64 VGPRs (eight waves per SIMD), no private
     (spill) memory, LDS for eight workgroups per CU."""
     ks = [k for k in kernels if "k_split" in k[".name"]]
-    assert len(ks) == 4 * 4 * 4 * 2
+    assert len(ks) == sum(4 * split_modes(f, u) for f in FMT.values() for u in (1, 2, 4, 8))
     for k in ks:
         assert k[".wavefront_size"] == 64
         assert K.waves_per_simd(k) == 8, (k[".name"], k[".vgpr_count"])

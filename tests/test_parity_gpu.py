@@ -176,6 +176,48 @@ def test_aligned_one_step_rows(oracle_lib, hooks, path, dtype):
                           f"aligned one step cap={cap} vectors={full - short} plan={p}")
 
 
+SPAN_WIDTHS = {"f32": [32001, 50257, 202047, 65533, 65534, 65535], "f16": [202047, 50257, 32001],
+               "bf16": [151937, 100003], "f64": [100003, 25001]}
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_rows_not_whole_vectors(oracle_lib, dtype):
+    """Split rows that start off a 16-byte boundary or end in a partial vector: when one
+    step covers every row's vectors, the split kernel reads whole aligned vectors and the
+    lanes holding a row's first and last vector mask the elements outside the row (else the
+    general scan). Row r holds values in a band of its own (1000 r plus noise), so an element
+    leaking in from the next row would beat the whole row under the max ops and one from the
+    previous row under the min ops; the elements before and after the tensor hold +inf for
+    the max ops and -inf for the min ops. Every element
+    offset within 16 bytes; one and three rows; widths at, and one or two elements past, a
+    whole step ([1,65533..65535] fp32 at U = 1, B = 64)."""
+    import torch
+
+    rng = np.random.default_rng(1600 + DTYPES.index(dtype))
+    v = VW[dtype]
+    for cols in SPAN_WIDTHS[dtype]:
+        for rows in (1, 3):
+            p = B.argreduce_plan(rows, cols, dtype)
+            assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] > 1, p
+            band = 1000.0 * np.arange(rows)[:, None] + np.rint(rng.uniform(0, 400, (rows, cols)))
+            arr = W.to_storage(band, dtype)
+            flat = arr.reshape(-1)
+            for offset in range(v):
+                for op in OPS:
+                    poison = W.to_storage(np.array([np.inf if op.startswith("max") else -np.inf]), dtype)
+                    host = np.concatenate([np.repeat(poison, v + offset), flat, np.repeat(poison, v)])
+                    buf = to_device(host, dtype)
+                    t = buf[v + offset: v + offset + flat.size].view(rows, cols)
+                    assert (t.data_ptr() % 16) == (offset * (16 // v)) % 16
+                    announce(f"span rows={rows} cols={cols} {dtype} offset={offset} op={op} plan={p}")
+                    rc, got = run(t, dtype, op)
+                    assert rc == 0
+                    want = oracle_lib.argreduce_lastaxis(arr, dtype, op)
+                    assert np.array_equal(got, want), (rows, cols, dtype, offset, op, got, want)
+                    del buf, t
+            torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
 def test_special_value_fuzz(oracle_lib, hooks, cap):
     """Random rows over {NaN, +-inf, +-max, +-1, +-0, +-subnormal}, and raw bit patterns with
