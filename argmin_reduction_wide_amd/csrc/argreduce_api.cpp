@@ -99,6 +99,15 @@ int64_t next_pow2(int64_t v) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 16-byte vectors from the one holding a row's first byte to the one holding its last, for
+// the worst row of a 16-byte aligned tensor: row r starts r * row_bytes bytes in, so its
+// misalignment is at most 16 - g, where g is the largest power of two (at most 16) dividing
+// row_bytes (0 for a single row).
+int64_t span_vecs(int64_t rows, int64_t row_bytes) {
+    const int64_t g = row_bytes % 16 == 0 ? 16 : (row_bytes & -row_bytes);
+    return ceil_div((rows <= 1 ? 0 : 16 - g) + row_bytes, 16);
+}
+
 int check_shape(int64_t rows, int64_t cols, int dtype) {
     if (elem_size(dtype) == 0) return ARGREDUCE_ERR_UNSUPPORTED_DTYPE;
     if (rows < 0 || cols < 1) return ARGREDUCE_ERR_INVALID_ARG;
@@ -227,15 +236,17 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
         }
         const int64_t rows_per_block = kBlock / group;
         const int64_t need = ceil_div(rows1, rows_per_block);
-        // Groups narrower than a wavefront on rows of whole 16-byte vectors: at most one
-        // device wave of workgroups, each group looping over rows. A workgroup per 256 / G
-        // rows measured 10-22% slower wherever that exceeded the wave (the dispatch of the
-        // extra workgroups): [65536,100] fp32 8.16 -> 6.76 us, [200000,40] fp32 10.57 ->
-        // 8.24, [65536,96] fp16 5.50 -> 4.67, [131072,24] fp64 8.30 -> 6.88. Rows that are not
-        // whole vectors (the generic lane-group kernel, head and tail loads) gained nothing
-        // (bf16 [65536,250] 12.35 us, 12.97 capped) and keep a group per row.
-        const bool whole = (cols * elem_size(dtype)) % 16 == 0;
-        const int64_t grid_cap = (group < 64 && whole) ? cap_blocks : max_grid;
+        // Groups narrower than a wavefront on rows of whole 16-byte vectors, or on rows whose
+        // span of vectors the group covers (in a 16-byte aligned tensor): at most one device
+        // wave of workgroups, each group looping over rows. A workgroup per 256 / G rows
+        // measured 10-22% slower wherever that exceeded the wave (the dispatch of the extra
+        // workgroups): [65536,100] fp32 8.16 -> 6.76 us, [200000,40] fp32 10.57 -> 8.24,
+        // [65536,96] fp16 5.50 -> 4.67, [131072,24] fp64 8.30 -> 6.88. Rows that the general
+        // scan takes (head and tail loads) gained nothing (bf16 [65536,250] 12.35 us, 12.97
+        // capped) and keep a group per row.
+        const int64_t row_bytes = cols * elem_size(dtype);
+        const bool covered = row_bytes % 16 == 0 || span_vecs(rows, row_bytes) <= group;
+        const int64_t grid_cap = (group < 64 && covered) ? cap_blocks : max_grid;
         p->lanes_per_row = static_cast<int>(group);
         p->blocks_per_row = 1;
         p->unroll = static_cast<int>(unroll);

@@ -9,15 +9,16 @@
 //              of G lanes (G = 1..32, a power of two) per row, one vector per lane.
 //   k_subwave  a group of G lanes (G = 1..64, a power of two) of one wavefront per row, any
 //              alignment; G = 64 is a wavefront per row. Rows beyond the grid are looped over.
+//              A span variant for rows whose 16-byte vectors one step of the group covers.
 //              Narrow rows use the group idea of TVM's shared-memory reduction page
 //              ("reduction -> shared", Algorithm: group size from the reduction length,
 //              a tree within the group; here on the DPP crossbar).
 //   k_blocks   a workgroup of 256 threads per row; rows beyond the grid are looped over.
 //   k_split    B > 1 workgroups per row, every row's team launched at once.
 //              Both have an aligned variant for rows of 16-byte aligned whole vectors that
-//              one step of the team covers (scan_row_aligned: no head, tail or seed load);
-//              k_split also a span variant for other rows one step covers (scan_row_span:
-//              aligned vector loads, the elements outside the row masked).
+//              one step of the team covers (scan_row_aligned: no head, tail or seed load),
+//              and a span variant for other rows one step covers (scan_row_span: aligned
+//              vector loads, the elements outside the row masked).
 //   k_wide     rows wider than INT32_MAX: one workgroup per window of at most 2^30
 //              elements (32-bit positions inside it), k_wide_merge as a second dispatch.
 //
@@ -69,7 +70,7 @@ namespace argreduce {
 // and a fifteenth would be read from kernel-argument memory, on the host, by every wave.
 __device__ unsigned long long g_wait_timeouts;
 
-template <typename Fmt, int OP, int G, int U>
+template <typename Fmt, int OP, int G, int U, bool SPAN>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
                                                            uint32_t cols, int64_t rows,
                                                            int64_t* __restrict__ out) {
@@ -79,7 +80,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
     const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
     for (int64_t r = first; r < rows; r += stride) {
         Cand<typename Fmt::C, OP> c;
-        scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
+        if constexpr (SPAN)
+            scan_row_span<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
+        else
+            scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
         group_merge<G>(c);
         if (lane == G - 1) out[r] = Cand<typename Fmt::C, OP>::result(c.i);
     }
@@ -180,9 +184,10 @@ __device__ inline void clear_candidate(uint64_t* e) {
         __hip_atomic_store(&e[j], uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup per row; rows beyond the grid are looped over. ALIGNED: every row is
-// 16-byte aligned whole vectors, at most 256 * U of them (one step: scan_row_aligned).
-template <typename Fmt, int OP, int U, bool ALIGNED>
+// One workgroup per row; rows beyond the grid are looped over. MODE as for k_split below:
+// 0 the general scan, 1 every row 16-byte aligned whole vectors, at most 256 * U of them
+// (one step: scan_row_aligned), 2 every row's span of vectors within one step.
+template <typename Fmt, int OP, int U, int MODE>
 __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restrict__ x,
                                                           int64_t rows,
                                                           int64_t* __restrict__ out,
@@ -192,8 +197,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_blocks(const uint8_t* __restr
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
         K c;
         const uint8_t* row = x + static_cast<size_t>(r) * row_bytes;
-        if constexpr (ALIGNED)
+        if constexpr (MODE == 1)
             scan_row_aligned<Fmt, OP, U>(row, cols / Fmt::VW, threadIdx.x, kBlockThreads, c);
+        else if constexpr (MODE == 2)
+            scan_row_span<Fmt, OP, U>(row, cols, threadIdx.x, kBlockThreads, c);
         else
             scan_row<Fmt, OP, U>(row, cols, threadIdx.x, kBlockThreads, c);
         block_merge(c);
@@ -725,11 +732,30 @@ hipError_t read_wait_timeouts(unsigned long long* count) {
 
 namespace {
 
+// 16-byte vectors of the longest row counted from the one holding its first byte. Row r
+// starts at byte x + r * row_bytes, 16-byte misaligned by (x + r * row_bytes) mod 16: at
+// most 16 - g + (x mod g) over the rows, where g is the largest power of two (at most 16)
+// dividing row_bytes, and exactly x mod 16 when there is one row.
+uint64_t span_vectors(const uint8_t* x, uint64_t row_bytes, int64_t rows) {
+    const uint64_t xm = reinterpret_cast<uintptr_t>(x) & 15u;
+    const uint64_t g = row_bytes % 16 == 0 ? 16 : (row_bytes & (~row_bytes + 1));
+    const uint64_t mis = (rows <= 1 || g == 16) ? xm : 16 - g + (xm & (g - 1));
+    return (mis + row_bytes + 15) / 16;
+}
+
+// The span scan when one step of the group covers every row's vectors and a lane holds at
+// most 32 elements, else the general scan.
 template <typename Fmt, int OP, int G, int U>
 void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                     hipStream_t s) {
-    launch_scan(k_subwave<Fmt, OP, G, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
-                cols, rows, out);
+    const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+    if constexpr (U * Fmt::VW <= 32) {
+        if (span_vectors(x, static_cast<uint64_t>(cols) * Fmt::kSize, rows) <= G * U) {
+            launch_scan(k_subwave<Fmt, OP, G, U, true>, grid, s, x, cols, rows, out);
+            return;
+        }
+    }
+    launch_scan(k_subwave<Fmt, OP, G, U, false>, grid, s, x, cols, rows, out);
 }
 
 template <typename Fmt, int OP, int U, int MODE>
@@ -739,40 +765,38 @@ void launch_split(const Plan& p, const uint8_t* x, uint32_t cols, int64_t* out, 
                 slots, cols, static_cast<uint32_t>(p.blocks_per_row), next_nonce(), spin_limit());
 }
 
+template <typename Fmt, int OP, int U, int MODE>
+void launch_rows(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
+                 uint64_t* slots, hipStream_t s) {
+    if (p.blocks_per_row <= 1)
+        launch_scan(k_blocks<Fmt, OP, U, MODE>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
+                    rows, out, cols);
+    else
+        launch_split<Fmt, OP, U, MODE>(p, x, cols, out, slots, s);
+}
+
 // The one-step aligned kernels when the rows are 16-byte aligned whole vectors that one step
-// of the team's lanes covers. Otherwise a split row takes the span scan when one step covers
-// every row's vectors and a lane holds at most 32 elements, and every other row the general
-// scan. Row r starts at byte x + r * row_bytes, 16-byte misaligned by (x + r * row_bytes)
-// mod 16: at most 16 - g + (x mod g) over the rows, where g is the largest power of two (at
-// most 16) dividing row_bytes, and exactly x mod 16 when there is one row.
+// of the team's lanes covers. Otherwise a row takes the span scan when one step covers every
+// row's vectors and a lane holds at most 32 elements (a workgroup per row: at most 4 vectors
+// per lane; with 8 the span scan measured slower, [4096,4097] fp32 12.8 -> 13.7 us), and
+// every other row the general scan.
 template <typename Fmt, int OP, int U>
 void launch_blocks(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                    uint64_t* slots, hipStream_t s) {
     const uint64_t row_bytes = static_cast<uint64_t>(cols) * Fmt::kSize;
     const uint64_t xm = reinterpret_cast<uintptr_t>(x) & 15u;
     const uint64_t step = static_cast<uint64_t>(p.blocks_per_row) * kBlockThreads * U;
-    const bool aligned = row_bytes % 16 == 0 && xm == 0 && row_bytes / 16 <= step;
-    if (p.blocks_per_row <= 1) {
-        const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
-        if (aligned)
-            launch_scan(k_blocks<Fmt, OP, U, true>, grid, s, x, rows, out, cols);
-        else
-            launch_scan(k_blocks<Fmt, OP, U, false>, grid, s, x, rows, out, cols);
-        return;
-    }
-    if (aligned) {
-        launch_split<Fmt, OP, U, 1>(p, x, cols, out, slots, s);
+    if (row_bytes % 16 == 0 && xm == 0 && row_bytes / 16 <= step) {
+        launch_rows<Fmt, OP, U, 1>(p, x, cols, rows, out, slots, s);
         return;
     }
     if constexpr (U * Fmt::VW <= 32) {
-        const uint64_t g = row_bytes % 16 == 0 ? 16 : (row_bytes & (~row_bytes + 1));
-        const uint64_t mis = (rows <= 1 || g == 16) ? xm : 16 - g + (xm & (g - 1));
-        if ((mis + row_bytes + 15) / 16 <= step) {
-            launch_split<Fmt, OP, U, 2>(p, x, cols, out, slots, s);
+        if ((p.blocks_per_row > 1 || U <= 4) && span_vectors(x, row_bytes, rows) <= step) {
+            launch_rows<Fmt, OP, U, 2>(p, x, cols, rows, out, slots, s);
             return;
         }
     }
-    launch_split<Fmt, OP, U, 0>(p, x, cols, out, slots, s);
+    launch_rows<Fmt, OP, U, 0>(p, x, cols, rows, out, slots, s);
 }
 
 template <typename Fmt, int OP>

@@ -213,13 +213,17 @@ def test_split_is_bounded_by_capacity(lib):
 
 
 def test_narrow_groups_take_at_most_one_device_wave(mi355x):
-    """Groups narrower than a wavefront on rows of whole 16-byte vectors launch at most one
-    device wave of workgroups (2048 on MI355X) and loop over rows; rows that are not whole
-    vectors, and a wavefront per row, keep a workgroup per 256 / G rows."""
+    """Groups narrower than a wavefront on rows of whole 16-byte vectors, or on rows whose
+    span of vectors (from the one holding the row's first byte, in a 16-byte aligned tensor)
+    the group covers, launch at most one device wave of workgroups (2048 on MI355X) and loop
+    over rows; other rows, and a wavefront per row, keep a workgroup per 256 / G rows.
+    [65536,250] bf16: 500-byte rows from offsets up to 12, 32 vectors for 32 lanes;
+    [300000,10] fp32: 3 of 4; [100000,63] fp16: 9 for 8; [300000,7] fp32: 3 for 2."""
     cases = [((65536, 100, B.F32), 32, 2048), ((200000, 40, B.F32), 16, 2048),
              ((65536, 64, B.F16), 8, 2048), ((1 << 21, 4, B.F32), 1, 2048),
-             ((40000, 64, B.F16), 8, 1250), ((65536, 250, B.BF16), 32, 8192),
-             ((300000, 10, B.F32), 4, 4688), ((65536, 1024, B.F32), 64, 16384)]
+             ((40000, 64, B.F16), 8, 1250), ((65536, 250, B.BF16), 32, 2048),
+             ((300000, 10, B.F32), 4, 2048), ((100000, 63, B.F16), 8, 3125),
+             ((300000, 7, B.F32), 2, 2344), ((65536, 1024, B.F32), 64, 16384)]
     for (rows, cols, dtype), lanes, grid in cases:
         p = B.argreduce_plan(rows, cols, dtype)
         assert p["path"] == B.PATH_SUBWAVE and p["lanes_per_row"] == lanes, (rows, cols, p)

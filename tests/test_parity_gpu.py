@@ -180,42 +180,83 @@ SPAN_WIDTHS = {"f32": [32001, 50257, 202047, 65533, 65534, 65535], "f16": [20204
                "bf16": [151937, 100003], "f64": [100003, 25001]}
 
 
+def check_banded_rows(oracle_lib, rng, dtype, rows, cols, label, offsets=None):
+    """Row r holds values in a band of its own (1000 (r mod 64) plus noise), so an element
+    leaking in from the next row would beat the whole row under the max ops and one from the
+    previous row under the min ops (except across a wrap of the band, every 64th row); the
+    elements before and after the tensor hold +inf for the max ops and -inf for the min ops.
+    Every element offset within 16 bytes unless given."""
+    import torch
+
+    v = VW[dtype]
+    band = 1000.0 * (np.arange(rows)[:, None] % 64) + np.rint(rng.uniform(0, 400, (rows, cols)))
+    arr = W.to_storage(band, dtype)
+    flat = arr.reshape(-1)
+    for offset in (range(v) if offsets is None else offsets):
+        for op in OPS:
+            poison = W.to_storage(np.array([np.inf if op.startswith("max") else -np.inf]), dtype)
+            host = np.concatenate([np.repeat(poison, v + offset), flat, np.repeat(poison, v)])
+            buf = to_device(host, dtype)
+            t = buf[v + offset: v + offset + flat.size].view(rows, cols)
+            assert (t.data_ptr() % 16) == (offset * (16 // v)) % 16
+            announce(f"{label} rows={rows} cols={cols} {dtype} offset={offset} op={op}")
+            rc, got = run(t, dtype, op)
+            assert rc == 0
+            want = oracle_lib.argreduce_lastaxis(arr, dtype, op)
+            assert np.array_equal(got, want), (rows, cols, dtype, offset, op, got, want)
+            del buf, t
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_split_rows_not_whole_vectors(oracle_lib, dtype):
     """Split rows that start off a 16-byte boundary or end in a partial vector: when one
     step covers every row's vectors, the split kernel reads whole aligned vectors and the
     lanes holding a row's first and last vector mask the elements outside the row (else the
-    general scan). Row r holds values in a band of its own (1000 r plus noise), so an element
-    leaking in from the next row would beat the whole row under the max ops and one from the
-    previous row under the min ops; the elements before and after the tensor hold +inf for
-    the max ops and -inf for the min ops. Every element
-    offset within 16 bytes; one and three rows; widths at, and one or two elements past, a
-    whole step ([1,65533..65535] fp32 at U = 1, B = 64)."""
-    import torch
-
+    general scan). Banded rows with poison around the tensor (check_banded_rows); every
+    element offset within 16 bytes; one and three rows; widths at, and one or two elements
+    past, a whole step ([1,65533..65535] fp32 at U = 1, B = 64)."""
     rng = np.random.default_rng(1600 + DTYPES.index(dtype))
-    v = VW[dtype]
     for cols in SPAN_WIDTHS[dtype]:
         for rows in (1, 3):
             p = B.argreduce_plan(rows, cols, dtype)
             assert p["path"] == B.PATH_SPLIT and p["blocks_per_row"] > 1, p
-            band = 1000.0 * np.arange(rows)[:, None] + np.rint(rng.uniform(0, 400, (rows, cols)))
-            arr = W.to_storage(band, dtype)
-            flat = arr.reshape(-1)
-            for offset in range(v):
-                for op in OPS:
-                    poison = W.to_storage(np.array([np.inf if op.startswith("max") else -np.inf]), dtype)
-                    host = np.concatenate([np.repeat(poison, v + offset), flat, np.repeat(poison, v)])
-                    buf = to_device(host, dtype)
-                    t = buf[v + offset: v + offset + flat.size].view(rows, cols)
-                    assert (t.data_ptr() % 16) == (offset * (16 // v)) % 16
-                    announce(f"span rows={rows} cols={cols} {dtype} offset={offset} op={op} plan={p}")
-                    rc, got = run(t, dtype, op)
-                    assert rc == 0
-                    want = oracle_lib.argreduce_lastaxis(arr, dtype, op)
-                    assert np.array_equal(got, want), (rows, cols, dtype, offset, op, got, want)
-                    del buf, t
-            torch.cuda.synchronize()
+            check_banded_rows(oracle_lib, rng, dtype, rows, cols, f"split span plan={p}")
+
+
+# (cols, lanes per row, loads per lane) of lane-group and workgroup-per-row plans for rows that
+# are not whole vectors: spans that fill the group or step exactly (f32 61: 16 vectors from a
+# 12-byte offset in a group of 16; f16 121 likewise; f32 250: 64 vectors for a wavefront;
+# f32 2049: 513 of 1024), spans one vector past it (the general scan: f32 7, f16 63, f16 3,
+# f16 8191), 8 loads per lane (the general scan: f64 4001), and ordinary fits.
+SPAN_PATH_WIDTHS = {
+    "f32": [(5, 2, 1), (7, 2, 1), (61, 16, 1), (101, 32, 1), (250, 64, 1), (999, 64, 4),
+            (1500, 256, 2), (2049, 256, 4)],
+    "f16": [(3, 1, 1), (63, 8, 1), (65, 16, 1), (121, 16, 1), (1001, 64, 2), (3001, 256, 2),
+            (8191, 256, 4)],
+    "bf16": [(65, 16, 1), (250, 32, 1), (3001, 256, 2), (4099, 256, 4)],
+    "f64": [(25, 16, 1), (63, 32, 1), (1001, 256, 2), (4001, 256, 8)],
+}
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_group_and_block_rows_not_whole_vectors(oracle_lib, dtype):
+    """Lane-group and workgroup-per-row plans on rows that start off a 16-byte boundary or
+    end in a partial vector: the span scan (aligned vector loads, the elements outside the
+    row masked) when one step of the group or workgroup covers every row's vectors, else the
+    general scan. Banded rows with poison around the tensor, every element offset, one and
+    three rows; then a lane-group width with enough rows that the groups loop over rows."""
+    rng = np.random.default_rng(1700 + DTYPES.index(dtype))
+    for cols, lanes, unroll in SPAN_PATH_WIDTHS[dtype]:
+        for rows in (1, 3):
+            p = B.argreduce_plan(rows, cols, dtype)
+            assert (p["lanes_per_row"], p["blocks_per_row"], p["unroll"]) == (lanes, 1, unroll), p
+            check_banded_rows(oracle_lib, rng, dtype, rows, cols, f"group/block span plan={p}")
+    cols = {"f32": 61, "f16": 65, "bf16": 65, "f64": 25}[dtype]
+    rows = 70001
+    p = B.argreduce_plan(rows, cols, dtype)
+    assert p["grid_rows"] < rows, p  # the groups loop over rows
+    check_banded_rows(oracle_lib, rng, dtype, rows, cols, f"looping span plan={p}", offsets=(0, 1))
 
 
 @pytest.mark.parametrize("cap", [0, 1024, H200_THREADS])
