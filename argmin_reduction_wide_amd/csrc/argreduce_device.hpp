@@ -127,6 +127,22 @@ struct F64 {
     }
 };
 
+// One element of a floating-point format through a buffer resource (raw buffer load at
+// byte offset voff + soff; soff is uniform across the wavefront).
+template <typename Fmt>
+__device__ inline typename Fmt::C buffer_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (Fmt::kSize == 2) {
+        const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+        return Fmt::from_bits(h);
+    } else if constexpr (Fmt::kSize == 4) {
+        const unsigned int w = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+        return Fmt::from_bits(w);
+    } else {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+        return Fmt::from_bits(static_cast<uint64_t>(w[0]) | (static_cast<uint64_t>(w[1]) << 32));
+    }
+}
+
 // Integer formats (the cumulative scan): compared exactly in their own type.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef long i64x2 __attribute__((ext_vector_type(2)));

@@ -358,24 +358,27 @@ struct Partial {
 // laid out like the column kernel of AcceleratedKernels.jl's pull request on reductions of
 // wide matrices along dims (Wide matrices: a column kernel): a workgroup takes a tile of
 // consecutive outputs of one outer index, TL lanes along `inner`, so that every load of a
-// wavefront reads consecutive memory. With VEC each lane owns VW consecutive outputs and
-// loads them as one 16-byte vector (inner * sizeof(T) a multiple of 16, x 16-byte aligned);
-// otherwise one output and one element. The TR = 256 / TL thread rows split the reduced axis
+// wavefront reads consecutive memory. LD = 1: each lane owns VW consecutive outputs and
+// loads them as one 16-byte vector (inner * sizeof(T) a multiple of 16, x 16-byte aligned).
+// Otherwise one output and one element per lane: LD = 2 through a buffer resource over the
+// tile (a lane's fixed 32-bit offset plus a uniform offset per load, so U loads in flight
+// hold one address register, not U 64-bit addresses), when every offset of the tile fits in
+// 32 bits; LD = 0 with 64-bit addresses. The TR = 256 / TL thread rows split the reduced axis
 // (thread row tr takes positions tr, tr + TR, ..., U loads in flight) and tree-merge in LDS.
 //
 // With B > 1 the axis is also split over B workgroups per tile (few outputs, long axis):
 // each stores a plain (value, index) partial per output and k_axis_merge, the second
 // dispatch, merges them; the kernel boundary orders the two, so nothing waits.
-template <typename Fmt, int OP, int TL, bool VEC, int U>
+template <typename Fmt, int OP, int TL, int LD, int U>
 __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restrict__ x,
                                                         int64_t inner, int64_t tiles,
                                                         int64_t* __restrict__ out,
                                                         Partial<typename Fmt::C>* __restrict__ part,
                                                         uint32_t len, uint32_t B, uint32_t grid) {
     using C = typename Fmt::C;
-    using L = typename std::conditional<VEC, typename Fmt::Vec, C>::type;
+    using L = typename std::conditional<LD == 1, typename Fmt::Vec, C>::type;
     constexpr int TR = kBlockThreads / TL;
-    constexpr int EPL = VEC ? Fmt::VW : 1;  // outputs per lane
+    constexpr int EPL = LD == 1 ? Fmt::VW : 1;  // outputs per lane
     constexpr int TO = TL * EPL;            // outputs per tile
     __shared__ C s_v[EPL][kBlockThreads];
     __shared__ uint32_t s_i[EPL][kBlockThreads];
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
     for (int64_t t = slot; t < tiles; t += grid_tiles) {
         const int64_t o = t / tiles_per_o;
         const int64_t i0 = (t - o * tiles_per_o) * TO + static_cast<int64_t>(tl) * EPL;
-        const bool active = i0 < inner;  // with VEC all EPL outputs of a lane exist together
+        const bool active = i0 < inner;  // with LD = 1 all EPL outputs of a lane exist together
         Cand<C, OP> c[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) c[k].init();
@@ -406,9 +409,78 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
             // partial step a lane past the end re-reads the last position, and visiting a
             // real element again, with its own position and after every smaller position of
             // the lane, changes no result.
+            // LD = 2: the resource starts at the tile's first output of position 0; a lane's
+            // element at position d is at lane_off + d * rstride (all < 2^32: checked by the
+            // launcher), and the resource ends with the tensor.
+            // (built in every mode; the other modes leave it unused). Its base is computed
+            // from uniform values only and passed through readfirstlane, so that the resource
+            // sits in scalar registers: a resource the compiler takes for per-lane makes every
+            // load a loop over the lanes' distinct resources.
+            const uint64_t tfirst = static_cast<uint64_t>(o) * len * static_cast<uint64_t>(inner) +
+                                    static_cast<uint64_t>(t - o * tiles_per_o) * TO;
+            const uint64_t toff = tfirst * Fmt::kSize;
+            const uint64_t total = static_cast<uint64_t>(tiles / tiles_per_o) * len *
+                                   static_cast<uint64_t>(inner) * Fmt::kSize;
+            const uint64_t left = total - toff;
+            const uintptr_t ta = reinterpret_cast<uintptr_t>(x) + toff;
+            const uint32_t ta_lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ta));
+            const uint32_t ta_hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ta >> 32));
+            const int nrec = __builtin_amdgcn_readfirstlane(left < 0xffffffffull ? static_cast<int>(left) : -1);
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<void*>((static_cast<uintptr_t>(ta_hi) << 32) | ta_lo), 0, nrec,
+                0x00020000);
+            const uint32_t lane_off = static_cast<uint32_t>(rlane * rstride + tl * Fmt::kSize);
+            // A full step of element loads: the lane's positions p0 + u * rteam, u < U, in
+            // increasing order. The step keeps its best value with the slot u it came from
+            // (an inline constant) and merges (value, p0 + slot * rteam) into the lane's
+            // candidate once, which equals updating it position by position (the merge
+            // keeps the earlier index on ties, or the later one for the last-index ops, and
+            // an empty step merges nothing). Updating position by position, the compiler
+            // formed all U positions ahead of the compares and kept them live.
+            auto step_merge = [&](Cand<C, OP>& cc, const auto& q, uint32_t p0) {
+                if constexpr (LD != 1) {  // element values only
+                    using K = Cand<C, OP>;
+                    C lv = K::identity();
+                    uint32_t ls = 0xffffffffu;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool tk = K::kLast ? (K::better(q[u], lv) | (q[u] == lv)) : K::better(q[u], lv);
+                        lv = tk ? q[u] : lv;
+                        ls = tk ? static_cast<uint32_t>(u) : ls;
+                    }
+                    cc.merge(lv, ls == 0xffffffffu ? K::kNone : p0 + ls * rteam);
+                }
+            };
             auto scan = [&](uint32_t base, auto guard) {
                 constexpr bool kGuard = decltype(guard)::value;
                 const uint32_t rem = len - base;
+                if constexpr (LD == 2) {
+                    if constexpr (!kGuard) {
+                        C q[U];
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            q[u] = buffer_load1<Fmt>(rsrc, lane_off,
+                                                     (base + static_cast<uint32_t>(u) * rteam) * static_cast<uint32_t>(rstride));
+                        __builtin_amdgcn_sched_barrier(0);
+                        step_merge(c[0], q, base + rlane);
+                    } else {
+                        // the last, partial step at clamped positions (a lane past the end
+                        // re-reads the last position, as below), every load issued at once:
+                        // each offset is needed only until its load issues
+                        uint32_t dd[U];
+                        C q[U];
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const uint32_t d = rlane + static_cast<uint32_t>(u) * rteam;
+                            dd[u] = d < rem ? d : rem - 1;
+                            q[u] = buffer_load1<Fmt>(rsrc, tl * Fmt::kSize + (base + dd[u]) * static_cast<uint32_t>(rstride), 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int u = 0; u < U; ++u) c[0].update(q[u], base + dd[u]);
+                    }
+                    return;
+                }
                 uint32_t dd[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -419,7 +491,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint8_t* a = col + static_cast<size_t>(base + dd[u]) * rstride;
-                    if constexpr (VEC)
+                    if constexpr (LD == 1)
                         q[u] = __builtin_nontemporal_load(reinterpret_cast<const L*>(a));
                     else
                         q[u] = Fmt::load1(a);
@@ -427,15 +499,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    if constexpr (VEC) {
+                    if constexpr (LD == 1) {
                         C e[Fmt::VW];
                         Fmt::unpack(q[u], e);
 #pragma unroll
                         for (int k = 0; k < EPL; ++k) c[k].update(e[k], base + dd[u]);
-                    } else {
+                    } else if constexpr (kGuard) {
                         c[0].update(q[u], base + dd[u]);
                     }
                 }
+                if constexpr (LD == 0 && !kGuard) step_merge(c[0], q, base + rlane);
             };
             // Position 0 enters as its own candidate (fix(x0), 0), merged into the scan's
             // result at the end: the merge is commutative, so this equals taking it first.
@@ -444,7 +517,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
             // waited for after the scan.
             L seed;
             if (rlane == 0) {
-                if constexpr (VEC)
+                if constexpr (LD == 1)
                     seed = *reinterpret_cast<const L*>(col);
                 else
                     seed = Fmt::load1(col);
@@ -456,7 +529,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
             if (full < len) scan(full, std::true_type{});
             if (rlane == 0) {
                 C e[EPL];
-                if constexpr (VEC) {
+                if constexpr (LD == 1) {
                     Fmt::unpack(seed, e);
                 } else {
                     e[0] = seed;
@@ -869,13 +942,13 @@ hipError_t launch_fmt(const Plan& p, const void* xv, int64_t rows, int64_t cols,
     return hipGetLastError();
 }
 
-template <typename Fmt, int OP, int TL, bool VEC, int U>
+template <typename Fmt, int OP, int TL, int LD, int U>
 void launch_axis_tl(const AxisPlan& p, const uint8_t* x, int64_t* out, uint8_t* scratch16,
                     hipStream_t s) {
     using P = Partial<typename Fmt::C>;
     P* part = reinterpret_cast<P*>(scratch16);
     const uint32_t B = static_cast<uint32_t>(p.blocks_per_tile);
-    launch_scan(k_axis<Fmt, OP, TL, VEC, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
+    launch_scan(k_axis<Fmt, OP, TL, LD, U>, dim3(static_cast<uint32_t>(p.grid_blocks)), s, x,
                 p.inner, p.tiles, out, B > 1 ? part : nullptr, static_cast<uint32_t>(p.len), B,
                 static_cast<uint32_t>(p.grid_blocks));
     if (B == 1) return;
@@ -909,20 +982,32 @@ hipError_t launch_axis_fmt(const AxisPlan& p, const void* xv, int64_t* out, uint
     // inner >= 2, so at least 2 lanes.
     constexpr int UV = Fmt::VW == 2 ? 4 : 8;
     constexpr int UE = Fmt::kSize == 2 ? 32 : (Fmt::kSize == 4 ? 16 : 8);
-    switch (p.vec * 1000 + p.lanes) {
-        case 2: launch_axis_tl<Fmt, OP, 2, false, UE>(p, x, out, scratch16, s); break;
-        case 4: launch_axis_tl<Fmt, OP, 4, false, UE>(p, x, out, scratch16, s); break;
-        case 8: launch_axis_tl<Fmt, OP, 8, false, UE>(p, x, out, scratch16, s); break;
-        case 16: launch_axis_tl<Fmt, OP, 16, false, UE>(p, x, out, scratch16, s); break;
-        case 32: launch_axis_tl<Fmt, OP, 32, false, UE>(p, x, out, scratch16, s); break;
-        case 64: launch_axis_tl<Fmt, OP, 64, false, UE>(p, x, out, scratch16, s); break;
-        case 1001: launch_axis_tl<Fmt, OP, 1, true, UV>(p, x, out, scratch16, s); break;
-        case 1002: launch_axis_tl<Fmt, OP, 2, true, UV>(p, x, out, scratch16, s); break;
-        case 1004: launch_axis_tl<Fmt, OP, 4, true, UV>(p, x, out, scratch16, s); break;
-        case 1008: launch_axis_tl<Fmt, OP, 8, true, UV>(p, x, out, scratch16, s); break;
-        case 1016: launch_axis_tl<Fmt, OP, 16, true, UV>(p, x, out, scratch16, s); break;
-        case 1032: launch_axis_tl<Fmt, OP, 32, true, UV>(p, x, out, scratch16, s); break;
-        case 1064: launch_axis_tl<Fmt, OP, 64, true, UV>(p, x, out, scratch16, s); break;
+    // element loads through a buffer resource when every offset from a tile's first output
+    // at position 0 fits in 32 bits: positions up to len + one step, columns up to a tile
+    const uint64_t rstride = static_cast<uint64_t>(p.inner) * Fmt::kSize;
+    const uint64_t step = static_cast<uint64_t>(p.blocks_per_tile) * (kBlockThreads / p.lanes) * UE;
+    const bool buf = !p.vec && (static_cast<uint64_t>(p.len) + step) * rstride +
+                                   static_cast<uint64_t>(p.tile) * Fmt::kSize < (uint64_t{1} << 32);
+    switch (p.vec * 1000 + (buf ? 2000 : 0) + p.lanes) {
+        case 2: launch_axis_tl<Fmt, OP, 2, 0, UE>(p, x, out, scratch16, s); break;
+        case 2002: launch_axis_tl<Fmt, OP, 2, 2, UE>(p, x, out, scratch16, s); break;
+        case 4: launch_axis_tl<Fmt, OP, 4, 0, UE>(p, x, out, scratch16, s); break;
+        case 2004: launch_axis_tl<Fmt, OP, 4, 2, UE>(p, x, out, scratch16, s); break;
+        case 8: launch_axis_tl<Fmt, OP, 8, 0, UE>(p, x, out, scratch16, s); break;
+        case 2008: launch_axis_tl<Fmt, OP, 8, 2, UE>(p, x, out, scratch16, s); break;
+        case 16: launch_axis_tl<Fmt, OP, 16, 0, UE>(p, x, out, scratch16, s); break;
+        case 2016: launch_axis_tl<Fmt, OP, 16, 2, UE>(p, x, out, scratch16, s); break;
+        case 32: launch_axis_tl<Fmt, OP, 32, 0, UE>(p, x, out, scratch16, s); break;
+        case 2032: launch_axis_tl<Fmt, OP, 32, 2, UE>(p, x, out, scratch16, s); break;
+        case 64: launch_axis_tl<Fmt, OP, 64, 0, UE>(p, x, out, scratch16, s); break;
+        case 2064: launch_axis_tl<Fmt, OP, 64, 2, UE>(p, x, out, scratch16, s); break;
+        case 1001: launch_axis_tl<Fmt, OP, 1, 1, UV>(p, x, out, scratch16, s); break;
+        case 1002: launch_axis_tl<Fmt, OP, 2, 1, UV>(p, x, out, scratch16, s); break;
+        case 1004: launch_axis_tl<Fmt, OP, 4, 1, UV>(p, x, out, scratch16, s); break;
+        case 1008: launch_axis_tl<Fmt, OP, 8, 1, UV>(p, x, out, scratch16, s); break;
+        case 1016: launch_axis_tl<Fmt, OP, 16, 1, UV>(p, x, out, scratch16, s); break;
+        case 1032: launch_axis_tl<Fmt, OP, 32, 1, UV>(p, x, out, scratch16, s); break;
+        case 1064: launch_axis_tl<Fmt, OP, 64, 1, UV>(p, x, out, scratch16, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

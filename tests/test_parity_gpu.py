@@ -597,6 +597,49 @@ def test_axis_torch_wrapper_dims(oracle_lib):
         assert np.array_equal(got.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
 
 
+def test_axis_element_loads_past_32bit_offsets():
+    """[1, 2^21 + 3, 1025] fp16 (4.3 GB): the element offsets from a tile's first output pass
+    2^32 bytes, so the kernel takes 64-bit addresses instead of a buffer resource. Zeros with
+    values planted so that the expected indices are known by construction: column 1000 has
+    its +1 beyond 2^32 bytes and its -1 near the start, column 3 the reverse with its -1 at
+    the last position, column 0 a NaN at position 0 (index 0 for every op), column 1024 a NaN
+    past 2^32 bytes (never taken); every other column ties throughout."""
+    import torch
+
+    length, inner = 2 ** 21 + 3, 1025
+    assert length * inner * 2 > 2 ** 32
+    p = B.argreduce_axis_plan(1, length, inner, "f16")
+    assert p["load_bytes"] == 2, p
+    announce(f"axis element loads past 32-bit offsets plan={p}")
+    x = torch.zeros((length, inner), dtype=torch.float16, device="cuda")
+    x[2097000, 1000] = 1.0
+    x[7, 1000] = -1.0
+    x[5, 3] = 1.0
+    x[length - 1, 3] = -1.0
+    x[0, 0] = float("nan")
+    x[2 ** 21, 1024] = float("nan")
+    planted = {"max": {1000: 2097000, 3: 5}, "max_last": {1000: 2097000, 3: 5},
+               "min": {1000: 7, 3: length - 1}, "min_last": {1000: 7, 3: length - 1}}
+    out = torch.full((inner,), -7, dtype=torch.int64, device="cuda")
+    need = B.argreduce_axis_scratch_bytes(1, length, inner, "f16")
+    scratch = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    for op in OPS:
+        want = np.full(inner, length - 1 if op.endswith("_last") else 0, dtype=np.int64)
+        want[0] = 0
+        for col, idx in planted[op].items():
+            want[col] = idx
+        announce(f"axis past 32-bit offsets op={op}")
+        rc = B.argreduce_axis(x.data_ptr(), "f16", 1, length, inner, op, out.data_ptr(),
+                              scratch.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert rc == 0
+        got = out.cpu().numpy()
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (op, bad[:5], got[bad[:5]], want[bad[:5]])
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_axis_workloads_full_size(oracle_lib):
     """The middle-axis bench workloads at full size (16-byte and element loads), every
     output against the oracle."""
