@@ -9,7 +9,8 @@
 //              of G lanes (G = 1..32, a power of two) per row, one vector per lane.
 //   k_subwave  a group of G lanes (G = 1..64, a power of two) of one wavefront per row, any
 //              alignment; G = 64 is a wavefront per row. Rows beyond the grid are looped over.
-//              A span variant for rows whose 16-byte vectors one step of the group covers.
+//              Modes as for k_blocks: aligned (16-byte aligned whole vectors one step of the
+//              group covers), span (other rows whose 16-byte vectors one step covers), general.
 //              Narrow rows use the group idea of TVM's shared-memory reduction page
 //              ("reduction -> shared", Algorithm: group size from the reduction length,
 //              a tree within the group; here on the DPP crossbar).
@@ -70,7 +71,7 @@ namespace argreduce {
 // and a fifteenth would be read from kernel-argument memory, on the host, by every wave.
 __device__ unsigned long long g_wait_timeouts;
 
-template <typename Fmt, int OP, int G, int U, bool SPAN>
+template <typename Fmt, int OP, int G, int U, int MODE>
 __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __restrict__ x,
                                                            uint32_t cols, int64_t rows,
                                                            int64_t* __restrict__ out) {
@@ -80,7 +81,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_subwave(const uint8_t* __rest
     const size_t row_bytes = static_cast<size_t>(cols) * Fmt::kSize;
     for (int64_t r = first; r < rows; r += stride) {
         Cand<typename Fmt::C, OP> c;
-        if constexpr (SPAN)
+        if constexpr (MODE == 1)
+            scan_row_aligned<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols / Fmt::VW, lane, G, c);
+        else if constexpr (MODE == 2)
             scan_row_span<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
         else
             scan_row<Fmt, OP, U>(x + static_cast<size_t>(r) * row_bytes, cols, lane, G, c);
@@ -816,19 +819,26 @@ uint64_t span_vectors(const uint8_t* x, uint64_t row_bytes, int64_t rows) {
     return (mis + row_bytes + 15) / 16;
 }
 
-// The span scan when one step of the group covers every row's vectors and a lane holds at
-// most 32 elements, else the general scan.
+// The aligned scan for rows of 16-byte aligned whole vectors that one step of the group
+// covers; else the span scan when one step covers every row's vectors and a lane holds at
+// most 32 elements; else the general scan.
 template <typename Fmt, int OP, int G, int U>
 void launch_subwave(const Plan& p, const uint8_t* x, uint32_t cols, int64_t rows, int64_t* out,
                     hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(p.grid_blocks));
+    const uint64_t row_bytes = static_cast<uint64_t>(cols) * Fmt::kSize;
+    if (row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+        row_bytes / 16 <= static_cast<uint64_t>(G) * U) {
+        launch_scan(k_subwave<Fmt, OP, G, U, 1>, grid, s, x, cols, rows, out);
+        return;
+    }
     if constexpr (U * Fmt::VW <= 32) {
-        if (span_vectors(x, static_cast<uint64_t>(cols) * Fmt::kSize, rows) <= G * U) {
-            launch_scan(k_subwave<Fmt, OP, G, U, true>, grid, s, x, cols, rows, out);
+        if (span_vectors(x, row_bytes, rows) <= static_cast<uint64_t>(G) * U) {
+            launch_scan(k_subwave<Fmt, OP, G, U, 2>, grid, s, x, cols, rows, out);
             return;
         }
     }
-    launch_scan(k_subwave<Fmt, OP, G, U, false>, grid, s, x, cols, rows, out);
+    launch_scan(k_subwave<Fmt, OP, G, U, 0>, grid, s, x, cols, rows, out);
 }
 
 template <typename Fmt, int OP, int U, int MODE>

@@ -228,14 +228,16 @@ def test_split_rows_not_whole_vectors(oracle_lib, dtype):
 # are not whole vectors: spans that fill the group or step exactly (f32 61: 16 vectors from a
 # 12-byte offset in a group of 16; f16 121 likewise; f32 250: 64 vectors for a wavefront;
 # f32 2049: 513 of 1024), spans one vector past it (the general scan: f32 7, f16 63, f16 3,
-# f16 8191), 8 loads per lane (the general scan: f64 4001), and ordinary fits.
+# f16 8191), 8 loads per lane (the general scan: f64 4001), and ordinary fits; and rows of
+# whole vectors for a wavefront each (fp32 1024, as [65536,1024]): the aligned scan at
+# offset 0, the span or general scan at the others.
 SPAN_PATH_WIDTHS = {
     "f32": [(5, 2, 1), (7, 2, 1), (61, 16, 1), (101, 32, 1), (250, 64, 1), (999, 64, 4),
-            (1500, 256, 2), (2049, 256, 4)],
+            (1500, 256, 2), (2049, 256, 4), (200, 64, 1), (1024, 64, 4)],
     "f16": [(3, 1, 1), (63, 8, 1), (65, 16, 1), (121, 16, 1), (1001, 64, 2), (3001, 256, 2),
-            (8191, 256, 4)],
-    "bf16": [(65, 16, 1), (250, 32, 1), (3001, 256, 2), (4099, 256, 4)],
-    "f64": [(25, 16, 1), (63, 32, 1), (1001, 256, 2), (4001, 256, 8)],
+            (8191, 256, 4), (512, 64, 1), (2048, 64, 4)],
+    "bf16": [(65, 16, 1), (250, 32, 1), (3001, 256, 2), (4099, 256, 4), (1024, 64, 2)],
+    "f64": [(25, 16, 1), (63, 32, 1), (1001, 256, 2), (4001, 256, 8), (256, 64, 2), (512, 64, 4)],
 }
 
 
@@ -244,7 +246,7 @@ def test_group_and_block_rows_not_whole_vectors(oracle_lib, dtype):
     """Lane-group and workgroup-per-row plans on rows that start off a 16-byte boundary or
     end in a partial vector: the span scan (aligned vector loads, the elements outside the
     row masked) when one step of the group or workgroup covers every row's vectors, else the
-    general scan. Banded rows with poison around the tensor, every element offset, one and
+    general scan; rows of 16-byte aligned whole vectors take the aligned scan. Banded rows with poison around the tensor, every element offset, one and
     three rows; then a lane-group width with enough rows that the groups loop over rows."""
     rng = np.random.default_rng(1700 + DTYPES.index(dtype))
     for cols, lanes, unroll in SPAN_PATH_WIDTHS[dtype]:
