@@ -332,9 +332,14 @@ int make_axis_plan(int64_t outer, int64_t len, int64_t inner, int dtype, uintptr
     // no faster (977 and 782 workgroups: +0.6-1.1%).
     int64_t b = 2 * want <= 3 * fill ? want : fill;
     b = b < kMaxBlocksPerRow ? b : kMaxBlocksPerRow;
-    // Two workgroups per tile do not pay for the merge dispatch they need: one per tile,
-    // with twice the steps, measured faster ([256,1024,256] fp32 44.8 -> 41.6 us per call).
-    b = b > 2 ? b : 1;
+    // With 16-byte loads, two workgroups per tile do not pay for the merge dispatch they
+    // need: one per tile, with twice the steps, measured faster ([256,1024,256] fp32 44.8 ->
+    // 41.6 us per call). With element loads (fewer bytes in flight per wave) one per tile
+    // left the device short of loads, and two measured faster: [48,4096,300] fp16 41.4 ->
+    // 29.4 us, [200,2048,63] fp32 30.4 -> 22.9, [64,4096,255] fp32 60.4 -> 47.8,
+    // [64,2048,255] fp64 55.9 -> 47.9, [256,1024,63] fp32 17.7 -> 16.3 (four per tile: 3-16%
+    // slower than two); one short axis slower, [256,512,33] fp32 9.19 -> 9.68.
+    b = b > 2 ? b : ((p->vec || b < 2) ? 1 : b);
     const int forced = g_force_path.load(std::memory_order_relaxed);
     if (forced == ARGREDUCE_PATH_SPLIT) b = b > 2 ? b : 2;
     if (forced == ARGREDUCE_PATH_BLOCK) b = 1;

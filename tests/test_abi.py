@@ -306,6 +306,34 @@ def test_axis_plans(mi355x):
         assert p["lanes_per_row"] == p["blocks_per_row"] * (256 // lanes)  # threads per output
 
 
+def test_axis_two_workgroups_per_tile(mi355x):
+    """Where a quarter of a device wave gives two workgroups per tile (256 tiles), 16-byte
+    loads take one per tile (no merge dispatch) and element loads keep two."""
+    p = B.argreduce_axis_plan(256, 1024, 256, B.F32)
+    assert (p["load_bytes"], p["blocks_per_row"], p["dispatches"]) == (16, 1, 1), p
+    p = B.argreduce_axis_plan(64, 4096, 255, B.F32)
+    assert (p["load_bytes"], p["blocks_per_row"], p["dispatches"]) == (4, 2, 2), p
+
+
+def test_axis_plans_with_more_tiles_than_a_quarter_wave(mi355x):
+    """Element-load plans (x off a 16-byte boundary, as the scratch query also sizes for)
+    whose tiles outnumber a quarter of a device wave of workgroups: one workgroup per tile,
+    a grid of at least one workgroup, and a scratch query that returns (a zero split here
+    once divided the grid size by zero on the host)."""
+    import itertools
+
+    for outer, length, inner in itertools.product([1, 64, 256, 5000, 70000], [1, 16, 1000, 65536],
+                                                  [2, 33, 63, 256, 1001]):
+        if outer * length * inner > (1 << 34):
+            continue
+        for dtype in (B.F32, B.F16, B.BF16, B.F64):
+            need = B.argreduce_axis_scratch_bytes(outer, length, inner, dtype)
+            assert need < (1 << 40), (outer, length, inner, dtype, need)
+            p = B.argreduce_axis_plan(outer, length, inner, dtype)
+            assert p["blocks_per_row"] >= 1 and p["grid_blocks"] >= 1, (outer, length, inner, p)
+    assert B.argreduce_axis_scratch_bytes(256, 16, 256, B.F16) == 0
+
+
 def test_axis_forced_paths(mi355x):
     B.argreduce_debug_force_path(B.PATH_SPLIT)
     assert B.argreduce_axis_plan(64, 100, 256, B.F32)["blocks_per_row"] >= 2

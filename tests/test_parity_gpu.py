@@ -524,10 +524,11 @@ def check_axis(oracle_lib, arr, dtype, op, what, **kw):
 
 # inner spans the 4 / 16 / 64-lane tiles of element loads and the 8 / 32 / 64-lane tiles of
 # 16-byte loads (an inner row of 16, 32, 48 ... bytes), ragged last tiles, and, with a long
-# axis and few outputs, the split over several workgroups with its merge dispatch.
+# axis and few outputs, the split over several workgroups with its merge dispatch; (200,
+# 256, 63): 200 tiles of element loads, two workgroups each.
 AXIS_SHAPES = [(1, 1, 2), (3, 7, 3), (2, 300, 5), (4, 33, 16), (2, 1000, 17), (5, 64, 64),
                (2, 129, 100), (1, 20000, 32), (3, 5000, 4), (1, 70001, 2), (8, 512, 257),
-               (2, 700, 256), (1, 3000, 520), (1, 300000, 8)]
+               (2, 700, 256), (1, 3000, 520), (1, 300000, 8), (200, 256, 63)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
