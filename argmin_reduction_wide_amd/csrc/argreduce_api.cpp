@@ -414,12 +414,17 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
     const auto tiles_of = [&](int64_t u) { return ceil_div(cols, kBlock * u * vec_elems); };
     const int64_t t1 = tiles_of(kScanUnrollTiny), t2 = tiles_of(kScanUnrollShort);
     const bool vecio = aligned && (cols * es) % 16 == 0;
+    const int64_t tile2 = kBlock * kScanUnrollShort * vec_elems, rem2 = cols % tile2;
     if (t2 == 1)
         p->unroll = t1 == 1 ? kScanUnrollTiny : kScanUnrollShort;
-    else if (!vecio && tiles_of(kScanUnrollMid) == 1 && rows >= cap_blocks / 2)
-        // element I/O, many rows: one tile of 4 chunks per lane rather than two or three
-        // chained ones ([2048,2049] fp32 21.3 -> 16.3 us, [1024,4099] fp16 15.2 -> 13.1;
-        // with 16-byte I/O, [4096,4096] fp32, it measured 8% slower)
+    else if ((!vecio || (rem2 != 0 && 2 * rem2 <= tile2)) && tiles_of(kScanUnrollMid) == 1 &&
+             rows >= cap_blocks / 2)
+        // many rows that one tile of 4 chunks per lane holds: that tile rather than two or
+        // three chained ones, for element I/O, and for 16-byte I/O when the last of two
+        // tiles would be at most half full ([2048,2049] fp32, element I/O, 21.3 -> 16.3 us;
+        // [1024,4099] fp16 15.2 -> 13.1; [2048,2560] fp32 19.5 -> 14.5; [2048,1028] fp64
+        // 15.1 -> 11.4; [2048,3000] fp32 21.1 -> 20.0; with a full second tile, [4096,4096]
+        // fp32, 8% slower)
         p->unroll = kScanUnrollMid;
     else if (t1 <= 64 && rows <= 2 * cap_blocks / t1)
         p->unroll = kScanUnrollTiny;

@@ -109,19 +109,21 @@ def test_scan_shapes_all_ops(oracle_lib, dtype):
                 check_scan(oracle_lib, arr, dtype, op, f"shape kind={kind}")
 
 
-# (cols one element past a 2-chunk tile, a whole-vector width read at an element offset)
-ONE_TILE_WIDTHS = {"f32": (2049, 4096), "i32": (2049, 4096), "f16": (4099, 8192), "bf16": (4099, 8192),
-                   "f64": (1025, 2048), "i64": (1025, 2048)}
+# (cols one element past a 2-chunk tile, a whole-vector width read at an element offset,
+# whole vectors one chunk past a 2-chunk tile)
+ONE_TILE_WIDTHS = {"f32": (2049, 4096, 2052), "i32": (2049, 4096, 2052), "f16": (4099, 8192, 4104),
+                   "bf16": (4099, 8192, 4104), "f64": (1025, 2048, 1026), "i64": (1025, 2048, 1026)}
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_scan_many_rows_of_one_element_io_tile(oracle_lib, dtype):
-    """Half a device wave of rows (1024) that are not whole vectors, or not 16-byte aligned,
-    and that one tile of 4 chunks per lane holds: one tile per row with element loads and
-    stores (no look-back), against the oracle at both widths, every op."""
+    """Half a device wave of rows (1024) that one tile of 4 chunks per lane holds, where the
+    plan takes that one tile (no look-back): rows that are not whole vectors or not 16-byte
+    aligned (element loads and stores), and aligned whole-vector rows one chunk past a
+    2-chunk tile (16-byte loads and stores); against the oracle, every op."""
     rng = np.random.default_rng(850 + DTYPES.index(dtype))
-    odd, whole = ONE_TILE_WIDTHS[dtype]
-    for cols, offset in ((odd, 0), (whole, 1)):
+    odd, whole, vec = ONE_TILE_WIDTHS[dtype]
+    for cols, offset in ((odd, 0), (whole, 1), (vec, 0)):
         arr = inputs(rng, 1024, cols, dtype, "ties")
         for op in OPS:
             check_scan(oracle_lib, arr, dtype, op, "one element-I/O tile per row", offset=offset)
