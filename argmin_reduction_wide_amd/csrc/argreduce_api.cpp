@@ -397,8 +397,11 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
     // Tile size (U 16-byte chunks per lane). A row that fits one tile of U <= 2 takes the
     // smallest tile that holds it whole (no look-back: a second tile costs a handoff). A
     // longer row takes U = 1 while it needs at most 64 such tiles and the grid stays within
-    // two device waves of workgroups (more, smaller tiles: more loads in flight, the
-    // look-back still one round), else U = 2 under the same 64-tile bound. Measured against
+    // one device wave of workgroups (more, smaller tiles: more loads in flight, the
+    // look-back still one round), else U = 2 under the same 64-tile bound (a bound of two
+    // device waves measured 14-29% slower between one and two: [512,5000] fp32 11.57 ->
+    // 9.24 us with U = 2, [512,3000] int64 11.07 -> 7.86, [600,7000] bf16 14.0 -> 11.6,
+    // [800,1500] fp64 9.69 -> 7.74). Measured against
     // U = 4 for every short row: [1,65536] int64 5.9 -> 5.35 us, fp32 6.0 -> 4.1, [64,1024]
     // int64 4.0 -> 3.2, [1024,64] int64 4.4 -> 3.0, [4096,1024] fp32 15.5 -> 12.7,
     // [4096,4096] fp32 48.9 -> 45.5 (U = 2, two tiles per row; U = 1 with four: 52.7).
@@ -426,7 +429,7 @@ int make_scan_plan(int64_t rows, int64_t cols, int dtype, bool aligned, ScanPlan
         // 15.1 -> 11.4; [2048,3000] fp32 21.1 -> 20.0; with a full second tile, [4096,4096]
         // fp32, 8% slower)
         p->unroll = kScanUnrollMid;
-    else if (t1 <= 64 && rows <= 2 * cap_blocks / t1)
+    else if (t1 <= 64 && rows <= cap_blocks / t1)
         p->unroll = kScanUnrollTiny;
     else if (t2 <= 64)
         p->unroll = kScanUnrollShort;
