@@ -412,13 +412,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
             // partial step a lane past the end re-reads the last position, and visiting a
             // real element again, with its own position and after every smaller position of
             // the lane, changes no result.
-            // LD = 2: the resource starts at the tile's first output of position 0; a lane's
-            // element at position d is at lane_off + d * rstride (all < 2^32: checked by the
-            // launcher), and the resource ends with the tensor.
-            // (built in every mode; the other modes leave it unused). Its base is computed
-            // from uniform values only and passed through readfirstlane, so that the resource
-            // sits in scalar registers: a resource the compiler takes for per-lane makes every
-            // load a loop over the lanes' distinct resources.
+            // LD = 2 loads through a buffer resource that starts at the tile's first output
+            // at position 0 and ends with the tensor: a lane's element at position d is at
+            // lane_off + d * rstride, below 2^32 (the launcher checks the tile's largest
+            // offset). The resource is built in every mode (the others leave it unused) from
+            // uniform values passed through readfirstlane, so that it sits in scalar
+            // registers: a resource the compiler took for per-lane made every load a loop
+            // over the lanes' distinct resources.
             const uint64_t tfirst = static_cast<uint64_t>(o) * len * static_cast<uint64_t>(inner) +
                                     static_cast<uint64_t>(t - o * tiles_per_o) * TO;
             const uint64_t toff = tfirst * Fmt::kSize;
