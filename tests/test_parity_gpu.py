@@ -228,16 +228,17 @@ def test_split_rows_not_whole_vectors(oracle_lib, dtype):
 # are not whole vectors: spans that fill the group or step exactly (f32 61: 16 vectors from a
 # 12-byte offset in a group of 16; f16 121 likewise; f32 250: 64 vectors for a wavefront;
 # f32 2049: 513 of 1024), spans one vector past it (the general scan: f32 7, f16 63, f16 3,
-# f16 8191), 8 loads per lane (the general scan: f64 4001), and ordinary fits; and rows of
+# f16 8191, and f32 31 and 1023, f16 127, f64 15), 8 loads per lane (the general scan: f64
+# 4001), and ordinary fits; and rows of
 # whole vectors for a wavefront each (fp32 1024, as [65536,1024]): the aligned scan at
 # offset 0, the span or general scan at the others.
 SPAN_PATH_WIDTHS = {
     "f32": [(5, 2, 1), (7, 2, 1), (61, 16, 1), (101, 32, 1), (250, 64, 1), (999, 64, 4),
-            (1500, 256, 2), (2049, 256, 4), (200, 64, 1), (1024, 64, 4)],
+            (1500, 256, 2), (2049, 256, 4), (200, 64, 1), (1024, 64, 4), (1023, 64, 4), (31, 8, 1)],
     "f16": [(3, 1, 1), (63, 8, 1), (65, 16, 1), (121, 16, 1), (1001, 64, 2), (3001, 256, 2),
-            (8191, 256, 4), (512, 64, 1), (2048, 64, 4)],
+            (8191, 256, 4), (512, 64, 1), (2048, 64, 4), (127, 16, 1)],
     "bf16": [(65, 16, 1), (250, 32, 1), (3001, 256, 2), (4099, 256, 4), (1024, 64, 2)],
-    "f64": [(25, 16, 1), (63, 32, 1), (1001, 256, 2), (4001, 256, 8), (256, 64, 2), (512, 64, 4)],
+    "f64": [(25, 16, 1), (63, 32, 1), (1001, 256, 2), (4001, 256, 8), (256, 64, 2), (512, 64, 4), (15, 8, 1)],
 }
 
 
