@@ -601,6 +601,26 @@ def test_axis_torch_wrapper_dims(oracle_lib):
         assert np.array_equal(got.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
 
 
+def test_axis_fuzz(oracle_lib):
+    """Random middle-axis shapes (outer, length and inner log-uniform, at most 4M elements),
+    formats, input kinds and element offsets of the tensor's start, every op: whatever load
+    mode, tile width and split the plan and the launcher choose, the oracle's indices."""
+    rng = np.random.default_rng(4242)
+    dtypes = ("f32", "f16", "bf16", "f64")
+    for trial in range(40):
+        dtype = dtypes[trial % 4]
+        inner = int(np.exp(rng.uniform(np.log(2), np.log(3000))))
+        outer = int(np.exp(rng.uniform(0, np.log(300))))
+        most = max(1, (4 << 20) // (inner * outer))
+        length = int(np.exp(rng.uniform(0, np.log(min(most, 200000)))))
+        kind = ("ties", "special", "bits")[trial % 3]
+        offset = (0, 1, 3)[int(rng.integers(0, 3))]
+        arr = W.random_rows(rng, outer * length, inner, dtype, kind).reshape(outer, length, inner)
+        for op in OPS:
+            check_axis(oracle_lib, arr, dtype, op, f"axis fuzz trial={trial} kind={kind} offset={offset}",
+                       offset=offset, dirty=True)
+
+
 def test_axis_element_loads_past_32bit_offsets():
     """[1, 2^21 + 3, 1025] fp16 (4.3 GB): the element offsets from a tile's first output pass
     2^32 bytes, so the kernel takes 64-bit addresses instead of a buffer resource. Zeros with

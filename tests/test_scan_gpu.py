@@ -129,6 +129,22 @@ def test_scan_many_rows_of_one_element_io_tile(oracle_lib, dtype):
             check_scan(oracle_lib, arr, dtype, op, "one element-I/O tile per row", offset=offset)
 
 
+def test_scan_fuzz(oracle_lib):
+    """Random row counts and lengths (log-uniform, at most 4M elements), every format, input
+    kinds, buffers aligned or one element off: whatever tile size, I/O mode and look-back
+    the plan chooses, the oracle's values and indices."""
+    rng = np.random.default_rng(4343)
+    for trial in range(40):
+        dtype = DTYPES[trial % len(DTYPES)]
+        cols = int(np.exp(rng.uniform(0, np.log(300000))))
+        rows = int(np.exp(rng.uniform(0, np.log(max(1, min(3000, (4 << 20) // cols))))))
+        kind = ("ties", "mixed", "bits")[trial % 3]
+        offset = int(rng.integers(0, 2))
+        arr = inputs(rng, rows, cols, dtype, kind)
+        for op in OPS:
+            check_scan(oracle_lib, arr, dtype, op, f"scan fuzz trial={trial} kind={kind}", offset=offset)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_scan_special_values_and_offsets(oracle_lib, dtype):
     """Special-value alphabet (NaN first or anywhere, +-inf, +-0, subnormals; integer
