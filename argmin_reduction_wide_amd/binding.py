@@ -361,16 +361,22 @@ def _reduce(t, op: int, out=None, scratch=None, dim: int = -1):
     return out
 
 
-def argmax(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False):
+def argmax(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False,
+           keepdim: bool = False):
     """Index of the maximum along `dim` (first occurrence, or the last with
-    select_last_index; NaN is never selected, a leading NaN gives 0)."""
-    return _reduce(t, MAX_LAST if select_last_index else MAX, out, scratch, dim)
+    select_last_index; NaN is never selected, a leading NaN gives 0). With keepdim the
+    result keeps `dim` with size 1 (a view of `out`)."""
+    r = _reduce(t, MAX_LAST if select_last_index else MAX, out, scratch, dim)
+    return r.unsqueeze(dim % t.dim()) if keepdim else r
 
 
-def argmin(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False):
+def argmin(t, dim: int = -1, out=None, scratch=None, select_last_index: bool = False,
+           keepdim: bool = False):
     """Index of the minimum along `dim` (first occurrence, or the last with
-    select_last_index; NaN is never selected, a leading NaN gives 0)."""
-    return _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch, dim)
+    select_last_index; NaN is never selected, a leading NaN gives 0). With keepdim the
+    result keeps `dim` with size 1 (a view of `out`)."""
+    r = _reduce(t, MIN_LAST if select_last_index else MIN, out, scratch, dim)
+    return r.unsqueeze(dim % t.dim()) if keepdim else r
 
 
 def _scan(t, op: int, dim: int, scratch=None):

@@ -599,6 +599,9 @@ def test_axis_torch_wrapper_dims(oracle_lib):
         got = ar.argmin(t, dim=dim, select_last_index=True)
         want = oracle_lib.argreduce_axis(np.ascontiguousarray(arr).reshape(outer, length, inner), "f32", "min_last")
         assert np.array_equal(got.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
+        kept = ar.argmin(t, dim=dim, select_last_index=True, keepdim=True)
+        assert kept.shape == tuple(1 if k == d else s for k, s in enumerate(shp)), (dim, kept.shape)
+        assert np.array_equal(kept.reshape(-1).cpu().numpy(), want.reshape(-1)), dim
 
 
 def test_axis_fuzz(oracle_lib):
