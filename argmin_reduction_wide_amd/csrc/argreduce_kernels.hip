@@ -351,6 +351,10 @@ __device__ inline uint32_t xcd_contiguous_id(uint32_t g) {
     return k * q + (k < r ? k : r) + blockIdx.x / 8;
 }
 
+// Word 3 of a gfx9 buffer resource for raw byte-addressed loads: DATA_FORMAT (bits 15-18) =
+// 4, 32-bit; no swizzle, no index stride, NUM_FORMAT 0.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 template <typename C>
 struct Partial {
     C v;
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_axis(const uint8_t* __restric
             const int nrec = __builtin_amdgcn_readfirstlane(left < 0xffffffffull ? static_cast<int>(left) : -1);
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
                 reinterpret_cast<void*>((static_cast<uintptr_t>(ta_hi) << 32) | ta_lo), 0, nrec,
-                0x00020000);
+                kRawBufferWord3);
             const uint32_t lane_off = static_cast<uint32_t>(rlane * rstride + tl * Fmt::kSize);
             // A full step of element loads: the lane's positions p0 + u * rteam, u < U, in
             // increasing order. The step keeps its best value with the slot u it came from
