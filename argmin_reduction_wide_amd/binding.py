@@ -40,7 +40,7 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 
 # Exported names of include/argreduce.h (checked by the CPU test suite).
 EXPORTS = ("argreduce_scratch_bytes", "argreduce_lastaxis", "argreduce_plan",
-           "argreduce_debug_set_capacity", "argreduce_debug_force_path",
+           "argreduce_debug_set_capacity", "argreduce_debug_force_path", "argreduce_debug_force_split",
            "argreduce_debug_launch_empty", "argreduce_debug_set_kernel_events",
            "argreduce_axis_scratch_bytes", "argreduce_axis", "argreduce_axis_plan",
            "argreduce_scan_scratch_bytes", "argreduce_scan_lastaxis", "argreduce_scan_plan",
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
                 h.argreduce_debug_set_capacity.restype = c_int
                 h.argreduce_debug_force_path.argtypes = [c_int]
                 h.argreduce_debug_force_path.restype = c_int
+                h.argreduce_debug_force_split.argtypes = [i64, c_int]
+                h.argreduce_debug_force_split.restype = c_int
                 h.argreduce_axis_scratch_bytes.argtypes = [i64, i64, i64, c_int]
                 h.argreduce_axis_scratch_bytes.restype = sz
                 h.argreduce_axis.argtypes = [vp, c_int, i64, i64, i64, c_int, vp, vp, sz, vp]
@@ -281,6 +283,11 @@ def argreduce_debug_set_window(elements: int) -> int:
 
 def argreduce_debug_force_path(path: int) -> int:
     return lib().argreduce_debug_force_path(path)
+
+
+def argreduce_debug_force_split(blocks_per_row: int, unroll: int = 1) -> int:
+    """Force the split geometry of last-axis plans (0 restores the automatic plans)."""
+    return lib().argreduce_debug_force_split(blocks_per_row, unroll)
 
 
 def argreduce_debug_launch_empty(stream: int) -> int:

@@ -49,6 +49,9 @@ constexpr int64_t kMaxUnrollBlocks = 8;
 std::atomic<int64_t> g_device_threads[kMaxDevices];
 std::atomic<int64_t> g_capacity_override{0};
 std::atomic<int> g_force_path{ARGREDUCE_PATH_AUTO};
+// Forced split geometry (debug hook): workgroups per row (0 = automatic) and loads per lane.
+std::atomic<int64_t> g_force_split_b{0};
+std::atomic<int> g_force_split_u{0};
 std::atomic<int64_t> g_window{0};
 constexpr int64_t kMaxWindow = int64_t{1} << 30;
 // Workgroups of the streaming-read measurement kernel.
@@ -219,6 +222,11 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     } else if (path == ARGREDUCE_PATH_SPLIT) {
         blocks_per_row = split_b > 2 ? split_b : 2;
     }
+    const int64_t forced_b = g_force_split_b.load(std::memory_order_relaxed);
+    if (forced_b > 0) {
+        path = ARGREDUCE_PATH_SPLIT;
+        blocks_per_row = forced_b;
+    }
 
     *p = Plan{};
     p->path = path;
@@ -255,6 +263,7 @@ int make_plan(int64_t rows, int64_t cols, int dtype, Plan* p) {
     } else {
         int64_t unroll = next_pow2(ceil_div(vec_row, blocks_per_row * kBlock));
         unroll = unroll < kMaxUnrollBlocks ? unroll : kMaxUnrollBlocks;
+        if (forced_b > 0) unroll = g_force_split_u.load(std::memory_order_relaxed);
         int64_t grid_rows = max_grid / blocks_per_row;
         grid_rows = grid_rows > 0 ? grid_rows : 1;
         grid_rows = rows1 < grid_rows ? rows1 : grid_rows;
@@ -549,6 +558,19 @@ ARGREDUCE_EXPORT int argreduce_debug_set_capacity(int64_t threads) {
 ARGREDUCE_EXPORT int argreduce_debug_set_window(int64_t elements) {
     if (elements < 0 || elements > argreduce::kMaxWindow) return ARGREDUCE_ERR_INVALID_ARG;
     argreduce::g_window.store(elements, std::memory_order_relaxed);
+    return ARGREDUCE_OK;
+}
+
+ARGREDUCE_EXPORT int argreduce_debug_force_split(int64_t blocks_per_row, int unroll) {
+    if (blocks_per_row == 0) {
+        argreduce::g_force_split_b.store(0, std::memory_order_relaxed);
+        return ARGREDUCE_OK;
+    }
+    if (blocks_per_row < 2 || blocks_per_row > argreduce::kMaxBlocksPerRow ||
+        (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8))
+        return ARGREDUCE_ERR_INVALID_ARG;
+    argreduce::g_force_split_u.store(unroll, std::memory_order_relaxed);
+    argreduce::g_force_split_b.store(blocks_per_row, std::memory_order_relaxed);
     return ARGREDUCE_OK;
 }
 

@@ -31,7 +31,9 @@ rows split across the host's threads (at most 16), with the host's core count an
 device copy, whose known bytes calibrate FETCH_SIZE / WRITE_SIZE, then 100 calls of each
 configuration and op, and of three more workloads) and prints nothing on stdout;
 `--traffic-summary`, `--counter-summary` and `--trace-summary` turn rocprofv3's CSV output
-of such runs into the committed summaries (no GPU).
+of such runs into the committed summaries (no GPU). `--shape ROWS,COLS,DTYPE[,OP]`
+(repeatable) times the last-axis reduction of any shape against its streaming-read floor
+and prints one JSON line per shape instead of the bench line.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -704,6 +706,46 @@ def cpu_baseline(primary, multi: list, seconds: float) -> dict:
             "host": host, "legs": legs, "_result": res}
 
 
+def shape_lines(specs: list, steps: int, warmup: int) -> int:
+    """--shape: per shape, the per-call time of the timed region (inputs rotated as for the
+    workloads), the trials' median, and the streaming-read floor of the same bytes."""
+    import numpy as np
+    import torch
+
+    import argmin_reduction_wide_amd.binding as B
+    from argmin_reduction_wide_amd import workloads as W
+
+    launch_floor_us(2000)  # brings the host's launch path up to speed first
+    for spec in specs:
+        parts = spec.split(",")
+        if len(parts) not in (3, 4, 6):
+            raise SystemExit(f"--shape {spec}: expected ROWS,COLS,DTYPE[,OP[,B,U]]")
+        rows, cols, dtype = int(parts[0]), int(parts[1]), parts[2]
+        op = parts[3] if len(parts) >= 4 else "max"
+        forced = (int(parts[4]), int(parts[5])) if len(parts) == 6 else (0, 1)
+        if B.argreduce_debug_force_split(*forced) != 0:
+            raise SystemExit(f"--shape {spec}: invalid split B={forced[0]} U={forced[1]}")
+        rng = np.random.default_rng(rows * 1000003 + cols)
+        data = W.to_storage(rng.standard_normal((rows, cols)), dtype)
+        w = W.Workload(name=f"arg{op}_{dtype}_{rows}x{cols}", dtype=dtype, ops=(op,), data=data,
+                       seed=rows * 1000003 + cols, recipe="iid N(0,1)")
+        c = Case(w, op)
+        trials = sorted(c.timed(200, 10, start=1000 * k) for k in range(5))
+        us = c.timed(steps, warmup)
+        floor = c.read_floor(min(steps, 500)) if w.nbytes >= 16 else None
+        print(json.dumps({
+            "shape": [rows, cols], "dtype": dtype, "op": op, "us_per_call": round(us, 3),
+            "trials_median_us": round(trials[2], 3),
+            "gbps": round(algorithmic_bytes(w) / us / 1e3, 1),
+            "read_floor_us": floor["us_per_call"] if floor else None,
+            "pct_of_read_floor": round(100.0 * floor["us_per_call"] / us, 1) if floor else None,
+            "plan": c.plan}), flush=True)
+        del c
+        B.argreduce_debug_force_split(0)
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -723,6 +765,11 @@ def main() -> int:
                          "--pmc-pass (no GPU)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print rocprofv3's kernel statistics under DIR as a table (no GPU)")
+    ap.add_argument("--shape", action="append", metavar="ROWS,COLS,DTYPE[,OP[,B,U]]",
+                    help="time the last-axis reduction (OP: max, min, max_last, min_last; default "
+                         "max) of one seeded N(0,1) [ROWS, COLS] tensor against its streaming-read "
+                         "floor, one JSON line per shape instead of the bench line; B,U force a "
+                         "split of B workgroups per row and U loads per lane; repeatable")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
@@ -749,6 +796,8 @@ def main() -> int:
 
     if args.pmc_pass:
         return pmc_pass()
+    if args.shape:
+        return shape_lines(args.shape, args.steps, args.warmup)
 
     # The launch floors first: they also bring the host's launch path up to speed (the first
     # thousands of launches of a process enqueue measurably slower), so the headline's timed

@@ -210,6 +210,14 @@ int argreduce_debug_set_capacity(int64_t threads);
  * of 10^5 elements). */
 int argreduce_debug_force_path(int path);
 
+/* Force the split path's geometry for every last-axis plan: blocks_per_row workgroups per
+ * row (2 .. the plan's maximum, 1024) and unroll 16-byte loads per lane per step (1, 2, 4 or
+ * 8); rows longer than one step take several. blocks_per_row = 0 restores the automatic
+ * plans. Process-wide; for measuring plan alternatives (a forced grid may exceed what is
+ * resident at once, and then relies on the in-order start of workgroups). Returns
+ * ARGREDUCE_ERR_INVALID_ARG for other values. */
+int argreduce_debug_force_split(int64_t blocks_per_row, int unroll);
+
 /* Window size of the WIDE path in elements, 1 .. 2^30 (0 = automatic). Process-wide. Lets
  * tests run the windowed path on rows small enough for the CPU oracle. */
 int argreduce_debug_set_window(int64_t elements);

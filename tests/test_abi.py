@@ -334,6 +334,25 @@ def test_axis_plans_with_more_tiles_than_a_quarter_wave(mi355x):
     assert B.argreduce_axis_scratch_bytes(256, 16, 256, B.F16) == 0
 
 
+def test_forced_split_geometry(mi355x):
+    """argreduce_debug_force_split: every last-axis plan becomes a split of the given
+    workgroups per row and loads per lane (several steps when one does not cover the row),
+    invalid values are refused, and 0 restores the automatic plans."""
+    auto = B.argreduce_plan(32, 202048, B.F16)
+    try:
+        assert B.argreduce_debug_force_split(8, 4) == 0
+        for rows, cols in ((32, 202048), (1, 1000), (4096, 4096)):
+            p = B.argreduce_plan(rows, cols, B.F16)
+            assert (p["path"], p["blocks_per_row"], p["unroll"]) == (B.PATH_SPLIT, 8, 4), p
+            assert p["grid_blocks"] == rows * 8
+            assert B.argreduce_scratch_bytes(rows, cols, B.F16) >= rows * 8 * 16
+        for b, u in ((1, 4), (2048, 4), (8, 3), (8, 16), (-1, 1)):
+            assert B.argreduce_debug_force_split(b, u) == -1, (b, u)  # ARGREDUCE_ERR_INVALID_ARG
+    finally:
+        assert B.argreduce_debug_force_split(0) == 0
+    assert B.argreduce_plan(32, 202048, B.F16) == auto
+
+
 def test_axis_forced_paths(mi355x):
     B.argreduce_debug_force_path(B.PATH_SPLIT)
     assert B.argreduce_axis_plan(64, 100, 256, B.F32)["blocks_per_row"] >= 2
