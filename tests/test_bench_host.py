@@ -241,3 +241,23 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.gpu
+def test_shape_lines_time_any_shape_and_forced_splits():
+    """bench.py --shape: one JSON line per shape with the per-call time, the trials and the
+    streaming-read floor; a forced split's geometry shows in its plan, and the automatic
+    plan comes back for the next shape."""
+    args = [sys.executable, os.path.join(bench.ROOT, "bench.py"), "--steps", "50", "--warmup", "5",
+            "--shape", "4,20000,f32", "--shape", "4,20000,f32,min_last,3,2",
+            "--shape", "4,20000,f32"]
+    r = subprocess.run(args, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [json.loads(x) for x in r.stdout.splitlines() if x.startswith("{")]
+    assert len(lines) == 3
+    for ln in lines:
+        assert ln["shape"] == [4, 20000] and ln["dtype"] == "f32"
+        assert ln["us_per_call"] > 0 and ln["read_floor_us"] > 0 and 0 < ln["pct_of_read_floor"]
+    assert lines[1]["op"] == "min_last"
+    assert (lines[1]["plan"]["blocks_per_row"], lines[1]["plan"]["unroll"]) == (3, 2)
+    assert lines[2]["plan"] == lines[0]["plan"]
